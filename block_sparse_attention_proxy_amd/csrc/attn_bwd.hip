@@ -1,0 +1,648 @@
+// Fused backward of the sparse GQA attention and the proxy head.
+//
+// The pages fuse the proxy and main-attention backward passes (ai-minor
+// "Dramatically Speeding Up Million-Token Training!", Why Does This Matter?:
+// fused backward; keelcrux "Flash-MSA: Ein Training mit einer Million
+// Tokens", Le fait) and keep every step except the proxy forward sparse.  The
+// proxy gradient is read as a distillation KL over the selected keys: with
+// T = mean over the group's heads of the main attention probabilities (held
+// constant) and Q the proxy softmax, dY = lam (Q - T), dqp = s_p dY kp and
+// dkp = s_p dY^T qp.
+//
+// Kernels, in launch order:
+//   delta_kernel   D = rowsum(dO * O) per (head, token)
+//   dq_kernel      query-major over the same block lists as the forward:
+//                  dQ, and the proxy term sum_u (Q - P/G) kp per head
+//   dqp_reduce     sums the per-head proxy terms when a group spans
+//                  several workgroups (G > 4)
+//   dkdv_kernel    KV-major over the inverted lists: dK, dV and dkp, each
+//                  KV block owned by one workgroup, so no atomics
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+__device__ __forceinline__ int xcd_remap_b(int i, int n) {
+  const int per = n / 8, rem = n % 8;
+  const int x = i % 8, k = i / 8;
+  return x * per + (x < rem ? x : rem) + k;
+}
+
+__device__ __forceinline__ int find_doc(const int32_t* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) { int mid = (lo + hi) >> 1; if (a[mid] <= x) lo = mid; else hi = mid; }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+                                                    float* __restrict__ delta, Geo g) {
+  const int64_t n = (int64_t)g.T * g.Hq;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = e / g.Hq;
+    const int h = (int)(e % g.Hq);
+    const T* a = o + e * D;
+    const T* b = dout + e * D;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < D; ++d) acc += to_f32(a[d]) * to_f32(b[d]);
+    delta[(int64_t)h * g.T + t] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ kernel: a workgroup serves (group, query block, 4 units); a wave owns 32
+// queries of one head.  Stages are 64-key halves of the selected blocks with
+// K (rows and transposed), V rows, kp (rows and transposed) in LDS.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int DP>
+struct DqCfg {
+  static constexpr int KC = 64, PAD = 8, EPC = 16 / (int)sizeof(T);
+  static constexpr int LDK = D + PAD, LDT = KC + PAD, LDP = DP + PAD;
+  static constexpr int KS = KC * LDK, VS = KC * LDK, KT = D * LDT, KPS = KC * LDP, KPT = DP * LDT;
+  static constexpr int STAGE = KS + VS + KT + KPS + KPT;
+  static constexpr int LDS_BYTES = 2 * STAGE * (int)sizeof(T);
+  static constexpr int CPR = D / EPC, CPRP = DP / EPC;
+  static constexpr int NK = KC * CPR / 256, NP = KC * CPRP / 256;
+  static_assert(4 * DP * 32 * 4 <= LDS_BYTES, "reduction scratch");
+};
+
+template <typename T, int D, int DP>
+__global__ __launch_bounds__(256) void dq_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ qp, const T* __restrict__ kp, const float* __restrict__ lse,
+    const float* __restrict__ lse_p, const T* __restrict__ dout, const float* __restrict__ delta,
+    const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_cnt,
+    float* __restrict__ dq, float* __restrict__ dqp, float* __restrict__ cpart, Geo g) {
+  typedef DqCfg<T, D, DP> C;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* smem = reinterpret_cast<T*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hi = lane >> 5;
+  const int NU = g.G * (g.Bq / 32);
+  const int nwg = (NU + 3) >> 2;
+  const int bid = xcd_remap_b(blockIdx.x, gridDim.x);
+  const int64_t item = bid / nwg;
+  const int wgi = bid % nwg;
+  const int grp = (int)(item / g.nqb);
+  const int QB = (int)(item % g.nqb);
+  const int u = wgi * 4 + wave;
+  const bool active = u < NU;
+  const int hl = u % g.G, chunk = u / g.G;
+  const int h = grp * g.G + hl;
+  const int b = find_doc(g.qb0, g.B, QB);
+  const int I = QB - g.qb0[b];
+  const int t0 = g.cu[b];
+  const int L = g.cu[b + 1] - t0;
+  const int kb0 = g.kb0[b];
+  const int diag = (I * g.Bq) >> 7;
+  const int qbase = I * g.Bq + chunk * 32;
+  const int64_t rowi = (int64_t)grp * g.nqb + QB;
+  const int cnt = q2k_cnt[rowi];
+  const int32_t* sel = q2k_idx + rowi * g.stride;
+  const int qpos = qbase + col;
+  const int qrow = qpos < L ? qpos : L - 1;
+  const int64_t tq = t0 + qrow;
+
+  frag_t<T> Qf[D / 16], dOf[D / 16], QPf[DP / 16];
+  float lse2 = 0.f, dl = 0.f, lsep2 = 0.f;
+  if (active) {
+    const T* sq = q + (tq * g.Hq + h) * D + hi * 8;
+    const T* sd = dout + (tq * g.Hq + h) * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) { Qf[ks] = ld8(sq + ks * 16); dOf[ks] = ld8(sd + ks * 16); }
+    const T* sp = qp + (tq * g.Hkv + grp) * DP + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < DP / 16; ++ks) QPf[ks] = ld8(sp + ks * 16);
+    lse2 = lse[(int64_t)h * g.T + tq] * LOG2E;
+    dl = delta[(int64_t)h * g.T + tq];
+    lsep2 = lse_p[(int64_t)grp * g.T + tq] * LOG2E;
+  }
+  const float invG = 1.f / (float)g.G;
+
+  f32x16 dQ[D / 32], Cp[DP / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) dQ[dt] = zero16();
+#pragma unroll
+  for (int dt = 0; dt < DP / 32; ++dt) Cp[dt] = zero16();
+
+  int nst = 2 * cnt;
+  if (cnt > 0 && diag * 128 + 64 > I * g.Bq + g.Bq - 1) nst -= 1;
+
+  uint4 Kr[C::NK], Vr[C::NK], Pr[C::NP];
+  auto load_stage = [&](int s) {
+    const int J = sel[s >> 1] - kb0;
+    const int key0 = J * 128 + (s & 1) * C::KC;
+#pragma unroll
+    for (int i = 0; i < C::NK; ++i) {
+      const int c = tid + 256 * i, r = c % C::KC, cc = c / C::KC, key = key0 + r;
+      const int64_t off = ((int64_t)(t0 + key) * g.Hkv + grp) * D + cc * C::EPC;
+      Kr[i] = key < L ? *reinterpret_cast<const uint4*>(k + off) : make_uint4(0, 0, 0, 0);
+      Vr[i] = key < L ? *reinterpret_cast<const uint4*>(v + off) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < C::NP; ++i) {
+      const int c = tid + 256 * i, r = c % C::KC, cc = c / C::KC, key = key0 + r;
+      Pr[i] = key < L ? *reinterpret_cast<const uint4*>(kp + ((int64_t)(t0 + key) * g.Hkv + grp) * DP + cc * C::EPC)
+                      : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_stage = [&](int buf) {
+    T* Ks = smem + buf * C::STAGE;
+    T* Vs = Ks + C::KS;
+    T* Kt = Vs + C::VS;
+    T* KPs = Kt + C::KT;
+    T* KPt = KPs + C::KPS;
+#pragma unroll
+    for (int i = 0; i < C::NK; ++i) {
+      const int c = tid + 256 * i, r = c % C::KC, cc = c / C::KC;
+      *reinterpret_cast<uint4*>(Ks + r * C::LDK + cc * C::EPC) = Kr[i];
+      *reinterpret_cast<uint4*>(Vs + r * C::LDK + cc * C::EPC) = Vr[i];
+      const T* e = reinterpret_cast<const T*>(&Kr[i]);
+#pragma unroll
+      for (int j = 0; j < C::EPC; ++j) Kt[(cc * C::EPC + j) * C::LDT + r] = e[j];
+    }
+#pragma unroll
+    for (int i = 0; i < C::NP; ++i) {
+      const int c = tid + 256 * i, r = c % C::KC, cc = c / C::KC;
+      *reinterpret_cast<uint4*>(KPs + r * C::LDP + cc * C::EPC) = Pr[i];
+      const T* e = reinterpret_cast<const T*>(&Pr[i]);
+#pragma unroll
+      for (int j = 0; j < C::EPC; ++j) KPt[(cc * C::EPC + j) * C::LDT + r] = e[j];
+    }
+  };
+
+  if (nst > 0) { load_stage(0); store_stage(0); }
+  __syncthreads();
+
+  for (int s = 0; s < nst; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nst) load_stage(s + 1);
+    const int J = sel[s >> 1] - kb0;
+    const int kpos0 = J * 128 + (s & 1) * C::KC;
+    if (active && kpos0 <= qbase + 31) {
+      const T* Ks = smem + buf * C::STAGE;
+      const T* Vs = Ks + C::KS;
+      const T* Kt = Vs + C::VS;
+      const T* KPs = Kt + C::KT;
+      const T* KPt = KPs + C::KPS;
+      const bool need_mask = (J == diag);
+      f32x16 S[2], dP[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        S[kt] = zero16();
+        dP[kt] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const frag_t<T> a = ld8(Ks + (kt * 32 + col) * C::LDK + ks * 16 + hi * 8);
+          mma(S[kt], a, Qf[ks]);
+          const frag_t<T> bv = ld8(Vs + (kt * 32 + col) * C::LDK + ks * 16 + hi * 8);
+          mma(dP[kt], bv, dOf[ks]);
+        }
+      }
+      // P (into S) and dS (into dP)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = __builtin_amdgcn_exp2f(S[kt][i] * g.scale_log2 - lse2);
+          if (need_mask && kpos0 + kt * 32 + acc_row(i, lane) > qpos) p = 0.f;
+          S[kt][i] = p;
+          dP[kt][i] = p * (dP[kt][i] - dl);
+        }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const frag_t<T> bs = acc_frag<T>(dP[kk >> 1], kk & 1);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const T* kr = Kt + (dt * 32 + col) * C::LDT + kk * 16 + hi * 4;
+          mma(dQ[dt], ld4x2(kr, kr + 8), bs);
+        }
+      }
+      // proxy: E = [assigned] Q - P / G ;  C^T += kp^T E^T
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bool assigned = ((s * 2 + kt) % g.G) == hl;
+        if (assigned) {
+          f32x16 Y = zero16();
+#pragma unroll
+          for (int ks = 0; ks < DP / 16; ++ks)
+            mma(Y, ld8(KPs + (kt * 32 + col) * C::LDP + ks * 16 + hi * 8), QPf[ks]);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float qv = __builtin_amdgcn_exp2f(Y[i] * g.pscale_log2 - lsep2);
+            if (need_mask && kpos0 + kt * 32 + acc_row(i, lane) > qpos) qv = 0.f;
+            S[kt][i] = qv - S[kt][i] * invG;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) S[kt][i] = -S[kt][i] * invG;
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const frag_t<T> be = acc_frag<T>(S[kk >> 1], kk & 1);
+#pragma unroll
+        for (int dt = 0; dt < DP / 32; ++dt) {
+          const T* pr = KPt + (dt * 32 + col) * C::LDT + kk * 16 + hi * 4;
+          mma(Cp[dt], ld4x2(pr, pr + 8), be);
+        }
+      }
+    }
+    if (s + 1 < nst) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dQ out (fp32)
+  if (active && qpos < L) {
+    float* dst = dq + ((int64_t)(t0 + qpos) * g.Hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = dQ[dt][i4 * 4 + j] * g.scale;
+        *reinterpret_cast<f32x4*>(dst + dt * 32 + acc_row(i4 * 4, lane)) = r;
+      }
+  }
+  // proxy term: sum over the heads of this workgroup that share a chunk
+  float* red = reinterpret_cast<float*>(smem_raw);          // [4][DP][32]
+  if (active) {
+#pragma unroll
+    for (int dt = 0; dt < DP / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red[(wave * DP + dt * 32 + acc_row(i, lane)) * 32 + col] = Cp[dt][i];
+  }
+  __syncthreads();
+  const int u_lo = wgi * 4;
+  const int u_hi = (u_lo + 4 < NU ? u_lo + 4 : NU) - 1;
+  const int c_lo = u_lo / g.G, c_hi = u_hi / g.G;
+  const int nhg = g.G > 4 ? g.G / 4 : 1;
+  const int hg = g.G > 4 ? (wgi % nhg) : 0;
+  const int nel = (c_hi - c_lo + 1) * 32 * DP;
+  for (int e = tid; e < nel; e += 256) {
+    const int cidx = e / (32 * DP);
+    const int rem = e % (32 * DP);
+    const int qq = rem / DP, dpi = rem % DP;
+    const int c = c_lo + cidx;
+    float acc = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const int uw = u_lo + w;
+      if (uw < NU && uw / g.G == c) acc += red[(w * DP + dpi) * 32 + qq];
+    }
+    const int pos = I * g.Bq + c * 32 + qq;
+    if (pos < L) {
+      const int64_t t = t0 + pos;
+      if (nhg == 1) dqp[(t * g.Hkv + grp) * DP + dpi] = acc * g.pscale * g.lam;
+      else cpart[(((int64_t)grp * nhg + hg) * g.T + t) * DP + dpi] = acc;
+    }
+  }
+}
+
+template <int DP>
+__global__ void dqp_reduce_kernel(const float* __restrict__ cpart, float* __restrict__ dqp, Geo g) {
+  const int nhg = g.G / 4;
+  const int64_t n = (int64_t)g.T * g.Hkv * DP;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = e / (g.Hkv * DP);
+    const int grp = (int)((e / DP) % g.Hkv);
+    const int dpi = (int)(e % DP);
+    float acc = 0.f;
+    for (int hg = 0; hg < nhg; ++hg) acc += cpart[(((int64_t)grp * nhg + hg) * g.T + t) * DP + dpi];
+    dqp[e] = acc * g.pscale * g.lam;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV kernel: a workgroup owns one KV block of one group; wave w owns keys
+// [32w, 32w + 32) and keeps K, V, kp of them as B fragments.  Stages walk the
+// inverted list: (query block, 32-query chunk, head), with Q and dO staged in
+// LDS both row-major and transposed.  T (the group-mean probability) is
+// accumulated over the heads of a chunk, and the proxy term is applied at the
+// chunk's last head, whose stage also carries qp.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int DP>
+struct KvCfg {
+  static constexpr int QC = 32, PAD = 8, EPC = 16 / (int)sizeof(T);
+  static constexpr int LDQ = D + PAD, LDT = QC + PAD, LDP = DP + PAD;
+  static constexpr int QS = QC * LDQ, QTT = D * LDT, PS = QC * LDP, PT = DP * LDT;
+  static constexpr int STAGE_T = 2 * QS + 2 * QTT + PS + PT;       // elements of T
+  static constexpr int STAGE_BYTES = ((STAGE_T * (int)sizeof(T) + 15) / 16) * 16 + 3 * QC * 4;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int CPR = D / EPC, CPRP = DP / EPC;
+  static constexpr int NQ = QC * CPR / 256, NP = (QC * CPRP + 255) / 256;
+  static constexpr int NPE = QC * CPRP;                             // proxy chunks per stage
+  static_assert(NQ >= 1 && NP >= 1, "tile split");
+};
+
+template <typename T, int D, int DP>
+__global__ __launch_bounds__(256) void dkdv_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ qp, const T* __restrict__ kp, const float* __restrict__ lse,
+    const float* __restrict__ lse_p, const T* __restrict__ dout, const float* __restrict__ delta,
+    const int32_t* __restrict__ k2q_ptr, const int32_t* __restrict__ k2q_idx,
+    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dkp, Geo g) {
+  typedef KvCfg<T, D, DP> C;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hi = lane >> 5;
+  const int bid = xcd_remap_b(blockIdx.x, gridDim.x);
+  const int grp = bid / g.nkb;
+  const int KB = bid % g.nkb;
+  const int b = find_doc(g.kb0, g.B, KB);
+  const int J = KB - g.kb0[b];
+  const int t0 = g.cu[b];
+  const int L = g.cu[b + 1] - t0;
+  const int qb0 = g.qb0[b];
+  const int kpos = J * 128 + wave * 32 + col;               // this lane's key (B-fragment column)
+  const int krow = kpos < L ? kpos : L - 1;
+  const int64_t tk = t0 + krow;
+  const int32_t* lst = k2q_idx + (int64_t)grp * g.cap + k2q_ptr[(int64_t)grp * (g.nkb + 1) + KB];
+  const int len = k2q_ptr[(int64_t)grp * (g.nkb + 1) + KB + 1] - k2q_ptr[(int64_t)grp * (g.nkb + 1) + KB];
+  const int nch = g.Bq / 32;
+  const int G = g.G;
+  const float invG = 1.f / (float)G;
+
+  frag_t<T> Kf[D / 16], Vf[D / 16], KPf[DP / 16];
+  {
+    const T* sk = k + (tk * g.Hkv + grp) * D + hi * 8;
+    const T* sv = v + (tk * g.Hkv + grp) * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) { Kf[ks] = ld8(sk + ks * 16); Vf[ks] = ld8(sv + ks * 16); }
+    const T* sp = kp + (tk * g.Hkv + grp) * DP + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < DP / 16; ++ks) KPf[ks] = ld8(sp + ks * 16);
+  }
+  f32x16 dK[D / 32], dV[D / 32], dKp[DP / 32], Tacc = zero16();
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) { dK[dt] = zero16(); dV[dt] = zero16(); }
+#pragma unroll
+  for (int dt = 0; dt < DP / 32; ++dt) dKp[dt] = zero16();
+
+  const int nst = len * nch * G;
+  uint4 Qr[C::NQ], Dr[C::NQ], Pr[C::NP];
+  float lr = 0.f, dlr = 0.f, lpr = 0.f;
+  auto stage_of = [&](int s, int& I, int& c, int& hl) {
+    hl = s % G;
+    c = (s / G) % nch;
+    I = lst[s / (G * nch)] - qb0;
+  };
+  auto load_stage = [&](int s) {
+    int I, c, hl;
+    stage_of(s, I, c, hl);
+    const int h = grp * G + hl;
+    const int row0 = I * g.Bq + c * 32;
+#pragma unroll
+    for (int i = 0; i < C::NQ; ++i) {
+      const int e = tid + 256 * i, r = e % C::QC, cc = e / C::QC, pos = row0 + r;
+      const int64_t off = ((int64_t)(t0 + pos) * g.Hq + h) * D + cc * C::EPC;
+      Qr[i] = pos < L ? *reinterpret_cast<const uint4*>(q + off) : make_uint4(0, 0, 0, 0);
+      Dr[i] = pos < L ? *reinterpret_cast<const uint4*>(dout + off) : make_uint4(0, 0, 0, 0);
+    }
+    const bool last = hl == G - 1;
+    if (last) {
+#pragma unroll
+      for (int i = 0; i < C::NP; ++i) {
+        const int e = tid + 256 * i, r = e % C::QC, cc = e / C::QC, pos = row0 + r;
+        if (e >= C::NPE) break;
+        Pr[i] = pos < L ? *reinterpret_cast<const uint4*>(qp + ((int64_t)(t0 + pos) * g.Hkv + grp) * DP + cc * C::EPC)
+                        : make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (tid < C::QC) {
+      const int pos = row0 + tid;
+      const bool ok = pos < L;
+      const int64_t t = t0 + pos;
+      lr = ok ? lse[(int64_t)h * g.T + t] * LOG2E : INFINITY;   // invalid rows get P = 0
+      dlr = ok ? delta[(int64_t)h * g.T + t] : 0.f;
+      lpr = (ok && last) ? lse_p[(int64_t)grp * g.T + t] * LOG2E : INFINITY;
+    }
+  };
+  auto store_stage = [&](int buf, int s) {
+    unsigned char* base = smem_raw + buf * C::STAGE_BYTES;
+    T* Qs = reinterpret_cast<T*>(base);
+    T* dOs = Qs + C::QS;
+    T* Qt = dOs + C::QS;
+    T* dOt = Qt + C::QTT;
+    T* Ps = dOt + C::QTT;
+    T* Pt = Ps + C::PS;
+    float* fl = reinterpret_cast<float*>(base + ((C::STAGE_T * (int)sizeof(T) + 15) / 16) * 16);
+#pragma unroll
+    for (int i = 0; i < C::NQ; ++i) {
+      const int e = tid + 256 * i, r = e % C::QC, cc = e / C::QC;
+      *reinterpret_cast<uint4*>(Qs + r * C::LDQ + cc * C::EPC) = Qr[i];
+      *reinterpret_cast<uint4*>(dOs + r * C::LDQ + cc * C::EPC) = Dr[i];
+      const T* eq = reinterpret_cast<const T*>(&Qr[i]);
+      const T* ed = reinterpret_cast<const T*>(&Dr[i]);
+#pragma unroll
+      for (int j = 0; j < C::EPC; ++j) {
+        Qt[(cc * C::EPC + j) * C::LDT + r] = eq[j];
+        dOt[(cc * C::EPC + j) * C::LDT + r] = ed[j];
+      }
+    }
+    if ((s % G) == G - 1) {
+#pragma unroll
+      for (int i = 0; i < C::NP; ++i) {
+        const int e = tid + 256 * i, r = e % C::QC, cc = e / C::QC;
+        if (e >= C::NPE) break;
+        *reinterpret_cast<uint4*>(Ps + r * C::LDP + cc * C::EPC) = Pr[i];
+        const T* ep = reinterpret_cast<const T*>(&Pr[i]);
+#pragma unroll
+        for (int j = 0; j < C::EPC; ++j) Pt[(cc * C::EPC + j) * C::LDT + r] = ep[j];
+      }
+    }
+    if (tid < C::QC) { fl[tid] = lr; fl[C::QC + tid] = dlr; fl[2 * C::QC + tid] = lpr; }
+  };
+
+  if (nst > 0) { load_stage(0); store_stage(0, 0); }
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nst) load_stage(s + 1);
+    int I, c, hl;
+    stage_of(s, I, c, hl);
+    const int diag = (I * g.Bq) >> 7;
+    const int qpos0 = I * g.Bq + c * 32;
+    const bool need_mask = (J == diag);
+    // skip when every key of this wave lies after every query of the chunk
+    const bool skip = need_mask && (J * 128 + wave * 32 > qpos0 + 31);
+    const unsigned char* base = smem_raw + buf * C::STAGE_BYTES;
+    const T* Qs = reinterpret_cast<const T*>(base);
+    const T* dOs = Qs + C::QS;
+    const T* Qt = dOs + C::QS;
+    const T* dOt = Qt + C::QTT;
+    const T* Ps = dOt + C::QTT;
+    const T* Pt = Ps + C::PS;
+    const float* fl = reinterpret_cast<const float*>(base + ((C::STAGE_T * (int)sizeof(T) + 15) / 16) * 16);
+    if (!skip) {
+      f32x16 S = zero16(), dP = zero16();
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        mma(S, ld8(Qs + col * C::LDQ + ks * 16 + hi * 8), Kf[ks]);
+        mma(dP, ld8(dOs + col * C::LDQ + ks * 16 + hi * 8), Vf[ks]);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = acc_row(i, lane);
+        float p = __builtin_amdgcn_exp2f(S[i] * g.scale_log2 - fl[r]);
+        if (need_mask && kpos > qpos0 + r) p = 0.f;
+        S[i] = p;
+        dP[i] = p * (dP[i] - fl[C::QC + r]);
+        Tacc[i] += p;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const frag_t<T> ap = acc_frag<T>(S, kk);
+        const frag_t<T> as = acc_frag<T>(dP, kk);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const T* dr = dOt + (dt * 32 + col) * C::LDT + kk * 16 + hi * 4;
+          mma(dV[dt], ap, ld4x2(dr, dr + 8));
+          const T* qr = Qt + (dt * 32 + col) * C::LDT + kk * 16 + hi * 4;
+          mma(dK[dt], as, ld4x2(qr, qr + 8));
+        }
+      }
+    }
+    if (hl == G - 1) {
+      if (!skip) {
+        f32x16 Y = zero16();
+#pragma unroll
+        for (int ks = 0; ks < DP / 16; ++ks) mma(Y, ld8(Ps + col * C::LDP + ks * 16 + hi * 8), KPf[ks]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = acc_row(i, lane);
+          float qv = __builtin_amdgcn_exp2f(Y[i] * g.pscale_log2 - fl[2 * C::QC + r]);
+          if (need_mask && kpos > qpos0 + r) qv = 0.f;
+          Y[i] = g.lam * (qv - Tacc[i] * invG);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const frag_t<T> ay = acc_frag<T>(Y, kk);
+#pragma unroll
+          for (int dt = 0; dt < DP / 32; ++dt) {
+            const T* pr = Pt + (dt * 32 + col) * C::LDT + kk * 16 + hi * 4;
+            mma(dKp[dt], ay, ld4x2(pr, pr + 8));
+          }
+        }
+      }
+      Tacc = zero16();
+    }
+    if (s + 1 < nst) store_stage(buf ^ 1, s + 1);
+    __syncthreads();
+  }
+
+  // outputs: lane holds column d = dt*32 + col for 16 key rows
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int key = J * 128 + wave * 32 + acc_row(i, lane);
+    if (key < L) {
+      const int64_t t = t0 + key;
+      float* pk = dk + (t * g.Hkv + grp) * D;
+      float* pv = dv + (t * g.Hkv + grp) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        pk[dt * 32 + col] = dK[dt][i] * g.scale;
+        pv[dt * 32 + col] = dV[dt][i];
+      }
+      float* pp = dkp + (t * g.Hkv + grp) * DP;
+#pragma unroll
+      for (int dt = 0; dt < DP / 32; ++dt) pp[dt * 32 + col] = dKp[dt][i] * g.pscale;
+    }
+  }
+}
+
+static int grid_for_b(int64_t n, int threads) {
+  int64_t b = (n + threads - 1) / threads;
+  if (b < 1) b = 1;
+  if (b > 65536) b = 65536;
+  return (int)b;
+}
+
+template <typename T, int D, int DP>
+static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const void* v,
+                               const void* qp, const void* kp, const void* o, const float* lse,
+                               const float* lse_p, const void* dout, const int32_t* q2k_idx,
+                               const int32_t* q2k_cnt, const int32_t* k2q_ptr,
+                               const int32_t* k2q_idx, float* dq, float* dk, float* dv, float* dqp,
+                               float* dkp, const Work& w, hipStream_t s) {
+  typedef DqCfg<T, D, DP> CQ;
+  typedef KvCfg<T, D, DP> CK;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)dq_kernel<T, D, DP>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, CQ::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)dkdv_kernel<T, D, DP>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, CK::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipError_t e;
+  const int64_t nd = (int64_t)g.T * g.Hq;
+  if (nd > 0) {
+    hipLaunchKernelGGL((delta_kernel<T, D>), dim3(grid_for_b(nd, 256)), dim3(256), 0, s,
+                       (const T*)o, (const T*)dout, w.delta, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int NU = g.G * (g.Bq / 32);
+  const int64_t nq = (int64_t)g.Hkv * g.nqb * ((NU + 3) / 4);
+  if (nq > 0) {
+    hipLaunchKernelGGL((dq_kernel<T, D, DP>), dim3((unsigned)nq), dim3(256), CQ::LDS_BYTES, s,
+                       (const T*)q, (const T*)k, (const T*)v, (const T*)qp, (const T*)kp, lse, lse_p,
+                       (const T*)dout, w.delta, q2k_idx, q2k_cnt, dq, dqp, w.cpart, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (g.G > 4 && g.T > 0) {
+    hipLaunchKernelGGL((dqp_reduce_kernel<DP>), dim3(grid_for_b((int64_t)g.T * g.Hkv * DP, 256)),
+                       dim3(256), 0, s, w.cpart, dqp, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t nk = (int64_t)g.Hkv * g.nkb;
+  if (nk > 0) {
+    hipLaunchKernelGGL((dkdv_kernel<T, D, DP>), dim3((unsigned)nk), dim3(256), CK::LDS_BYTES, s,
+                       (const T*)q, (const T*)k, (const T*)v, (const T*)qp, (const T*)kp, lse, lse_p,
+                       (const T*)dout, w.delta, k2q_ptr, k2q_idx, dk, dv, dkp, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_bwd(const Geo& g, int is_bf16, const void* q, const void* k, const void* v,
+                      const void* qp, const void* kp, const void* o, const float* lse,
+                      const float* lse_p, const void* dout, const int32_t* q2k_idx,
+                      const int32_t* q2k_cnt, const int32_t* k2q_ptr, const int32_t* k2q_idx,
+                      float* dq, float* dk, float* dv, float* dqp, float* dkp, const Work& w,
+                      hipStream_t s) {
+  if (is_bf16) {
+    if (g.D == 128)
+      return bwd_dispatch<bf16, 128, 64>(g, q, k, v, qp, kp, o, lse, lse_p, dout, q2k_idx, q2k_cnt,
+                                         k2q_ptr, k2q_idx, dq, dk, dv, dqp, dkp, w, s);
+    return bwd_dispatch<bf16, 64, 32>(g, q, k, v, qp, kp, o, lse, lse_p, dout, q2k_idx, q2k_cnt,
+                                      k2q_ptr, k2q_idx, dq, dk, dv, dqp, dkp, w, s);
+  }
+  return bwd_dispatch<float, 64, 32>(g, q, k, v, qp, kp, o, lse, lse_p, dout, q2k_idx, q2k_cnt,
+                                     k2q_ptr, k2q_idx, dq, dk, dv, dqp, dkp, w, s);
+}
+
+}  // namespace msa
+
+namespace msa {
+int bwd_kernels(KernelEntry* out, int max) {
+  const KernelEntry all[] = {
+      {"bwd_dq<bf16,d128,dp64>", (const void*)dq_kernel<bf16, 128, 64>, 256, DqCfg<bf16, 128, 64>::LDS_BYTES},
+      {"bwd_dkdv<bf16,d128,dp64>", (const void*)dkdv_kernel<bf16, 128, 64>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
+      {"bwd_dq<bf16,d64,dp32>", (const void*)dq_kernel<bf16, 64, 32>, 256, DqCfg<bf16, 64, 32>::LDS_BYTES},
+      {"bwd_dkdv<bf16,d64,dp32>", (const void*)dkdv_kernel<bf16, 64, 32>, 256, KvCfg<bf16, 64, 32>::LDS_BYTES},
+      {"bwd_dq<f32,d64,dp32>", (const void*)dq_kernel<float, 64, 32>, 256, DqCfg<float, 64, 32>::LDS_BYTES},
+      {"bwd_dkdv<f32,d64,dp32>", (const void*)dkdv_kernel<float, 64, 32>, 256, KvCfg<float, 64, 32>::LDS_BYTES},
+  };
+  int n = (int)(sizeof(all) / sizeof(all[0]));
+  for (int i = 0; i < n && i < max; ++i) out[i] = all[i];
+  return n;
+}
+}  // namespace msa

@@ -1,0 +1,322 @@
+// C ABI of the MSA hot path: argument checks, buffer layout, workspace
+// carving and launches.  Every check runs on the host before anything is
+// enqueued; errors are returned as msa_status with a thread-local message.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/msa.h"
+#include "msa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+msa_status fail(msa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+msa_status hip_fail(hipError_t e, const char* where) {
+  return fail(MSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kAlign = 256;
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Host view of one call: sizes plus workspace region offsets.
+struct Plan {
+  msa::Geo g{};
+  msa_layout lay{};
+  int64_t off_qb0, off_kb0, off_s0, off_order, off_unit0, off_counts, off_cursor, off_delta,
+      off_cpart;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
+  g_last_error.clear();
+  if (!cfg || !vl) return fail(MSA_ERR_INVALID_ARG, "cfg and vl must be non-null");
+  const msa_config& c = *cfg;
+  if (c.heads_kv <= 0 || c.heads_q <= 0)
+    return fail(MSA_ERR_INVALID_ARG, "heads_q (%d) and heads_kv (%d) must be positive", c.heads_q, c.heads_kv);
+  if (c.heads_q % c.heads_kv != 0)
+    return fail(MSA_ERR_INVALID_ARG, "heads_q (%d) must be a multiple of heads_kv (%d)", c.heads_q, c.heads_kv);
+  const int G = c.heads_q / c.heads_kv;
+  if (G > 4 && G % 4 != 0)
+    return fail(MSA_ERR_UNSUPPORTED, "group size %d: groups above 4 must be a multiple of 4", G);
+  if (c.dtype != MSA_BF16 && c.dtype != MSA_F32) return fail(MSA_ERR_INVALID_ARG, "unknown dtype %d", c.dtype);
+  const bool dims_ok = (c.head_dim == 128 && c.proxy_dim == 64 && c.dtype == MSA_BF16) ||
+                       (c.head_dim == 64 && c.proxy_dim == 32);
+  if (!dims_ok)
+    return fail(MSA_ERR_UNSUPPORTED, "(head_dim, proxy_dim, dtype) = (%d, %d, %s) not built; built: (128, 64, bf16), (64, 32, bf16|f32)",
+                c.head_dim, c.proxy_dim, c.dtype == MSA_BF16 ? "bf16" : "f32");
+  if (c.kv_block != 128) return fail(MSA_ERR_UNSUPPORTED, "kv_block must be 128 (got %d)", c.kv_block);
+  if (c.q_block != 64 && c.q_block != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "q_block must be 64 or 128 (got %d)", c.q_block);
+  if (c.topk < 1) return fail(MSA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", c.topk);
+  if (c.local_window < 0) return fail(MSA_ERR_INVALID_ARG, "local_window must be >= 0 (got %d)", c.local_window);
+  if ((int64_t)c.topk + c.local_window > (1 << 20))
+    return fail(MSA_ERR_INVALID_ARG, "topk + local_window too large");
+  if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale) || !(c.proxy_scale >= 0.f) ||
+      !std::isfinite(c.proxy_scale) || !std::isfinite(c.proxy_loss_weight))
+    return fail(MSA_ERR_INVALID_ARG, "scales must be finite and >= 0, the loss weight finite");
+  if (vl->batch < 1) return fail(MSA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", vl->batch);
+  if (vl->total_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "total_tokens must be >= 0");
+  if (!vl->cu_seqlens_host) return fail(MSA_ERR_INVALID_ARG, "cu_seqlens_host must be non-null");
+  const int32_t* cu = vl->cu_seqlens_host;
+  if (cu[0] != 0) return fail(MSA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+  int64_t nqb = 0, nkb = 0, se = 0, pairs = 0, max_nq = 0, units = 0;
+  for (int b = 0; b < vl->batch; ++b) {
+    const int64_t L = (int64_t)cu[b + 1] - cu[b];
+    if (L < 0) return fail(MSA_ERR_INVALID_ARG, "cu_seqlens decreases at index %d", b + 1);
+    const int64_t nq = (L + c.q_block - 1) / c.q_block, nk = (L + 127) / 128;
+    nqb += nq;
+    nkb += nk;
+    se += nq * nk;
+    if (nq > max_nq) max_nq = nq;
+    units += ((L + 127) / 128 + 1) / 2;
+    for (int64_t I = 0; I < nq; ++I) {
+      const int64_t diag = I * c.q_block / 128;
+      if (diag + 1 <= (int64_t)c.topk + c.local_window) continue;
+      const int64_t rows = std::min<int64_t>(c.q_block, L - I * c.q_block);
+      pairs += rows * (diag - c.local_window) * 128;
+    }
+  }
+  if (cu[vl->batch] != vl->total_tokens)
+    return fail(MSA_ERR_INVALID_ARG, "cu_seqlens[batch] (%d) != total_tokens (%d)", cu[vl->batch], vl->total_tokens);
+  if (max_nq > 16384)
+    return fail(MSA_ERR_UNSUPPORTED, "a document of %lld query blocks exceeds the 16384 supported",
+                (long long)max_nq);
+  if (nqb * ((int64_t)c.topk + c.local_window) > INT32_MAX || se * (int64_t)c.heads_kv > ((int64_t)1 << 40))
+    return fail(MSA_ERR_UNSUPPORTED, "problem too large for 32-bit block indexing");
+
+  msa::Geo& g = P->g;
+  g.Hq = c.heads_q; g.Hkv = c.heads_kv; g.G = G; g.D = c.head_dim; g.DP = c.proxy_dim;
+  g.Bq = c.q_block; g.topk = c.topk; g.lw = c.local_window; g.stride = c.topk + c.local_window;
+  g.B = vl->batch; g.T = vl->total_tokens; g.nqb = (int32_t)nqb; g.nkb = (int32_t)nkb;
+  g.max_nq = (int32_t)max_nq; g.cap = nqb * g.stride; g.score_elems = se; g.n_units = (int32_t)units;
+  g.scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.f / std::sqrt((float)c.head_dim);
+  g.pscale = c.proxy_scale > 0.f ? c.proxy_scale : 1.f / std::sqrt((float)c.proxy_dim);
+  g.lam = c.proxy_loss_weight;
+  g.scale_log2 = g.scale * 1.4426950408889634f;
+  g.pscale_log2 = g.pscale * 1.4426950408889634f;
+  g.cu = vl->cu_seqlens;
+
+  const int64_t B = vl->batch;
+  int64_t off = 0;
+  P->off_qb0 = off;    off = align_up(off + 4 * (B + 1));
+  P->off_kb0 = off;    off = align_up(off + 4 * (B + 1));
+  P->off_s0 = off;     off = align_up(off + 8 * (B + 1));
+  P->off_order = off;  off = align_up(off + 4 * B);
+  P->off_unit0 = off;  off = align_up(off + 4 * (B + 1));
+  P->off_counts = off; off = align_up(off + 4 * (int64_t)c.heads_kv * nkb);
+  P->off_cursor = off; off = align_up(off + 4 * (int64_t)c.heads_kv * nkb);
+  P->off_delta = off;  off = align_up(off + 4 * (int64_t)c.heads_q * vl->total_tokens);
+  P->off_cpart = off;
+  if (G > 4) off = align_up(off + 4 * (int64_t)c.heads_kv * (G / 4) * vl->total_tokens * c.proxy_dim);
+
+  msa_layout& l = P->lay;
+  l.total_qblocks = nqb;
+  l.total_kvblocks = nkb;
+  l.score_elems = se;
+  l.sel_stride = g.stride;
+  l.k2q_capacity = g.cap;
+  l.scored_pairs = pairs;
+  l.max_qblocks_doc = max_nq;
+  l.workspace_bytes = off;
+  return MSA_OK;
+}
+
+msa_status bind_workspace(Plan* P, void* ws, size_t ws_bytes, msa::Work* w) {
+  if (!ws) return fail(MSA_ERR_INVALID_ARG, "workspace must be non-null");
+  if (!aligned16(ws)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if ((int64_t)ws_bytes < P->lay.workspace_bytes)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes; %lld needed", ws_bytes,
+                (long long)P->lay.workspace_bytes);
+  if (!P->g.cu) return fail(MSA_ERR_INVALID_ARG, "cu_seqlens (device) must be non-null");
+  char* base = static_cast<char*>(ws);
+  P->g.qb0 = reinterpret_cast<int32_t*>(base + P->off_qb0);
+  P->g.kb0 = reinterpret_cast<int32_t*>(base + P->off_kb0);
+  P->g.s0 = reinterpret_cast<int64_t*>(base + P->off_s0);
+  P->g.order = reinterpret_cast<int32_t*>(base + P->off_order);
+  P->g.unit0 = reinterpret_cast<int32_t*>(base + P->off_unit0);
+  if (w) {
+    w->counts = reinterpret_cast<int32_t*>(base + P->off_counts);
+    w->cursor = reinterpret_cast<int32_t*>(base + P->off_cursor);
+    w->delta = reinterpret_cast<float*>(base + P->off_delta);
+    w->cpart = reinterpret_cast<float*>(base + P->off_cpart);
+  }
+  return MSA_OK;
+}
+
+msa_status check_ptrs(std::initializer_list<std::pair<const void*, const char*>> ps) {
+  for (auto& p : ps) {
+    if (!p.first) return fail(MSA_ERR_INVALID_ARG, "%s must be non-null", p.second);
+    if (!aligned16(p.first)) return fail(MSA_ERR_INVALID_ARG, "%s must be 16-byte aligned", p.second);
+  }
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+const char* msa_status_string(msa_status s) {
+  switch (s) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_INVALID_ARG: return "invalid argument";
+    case MSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MSA_ERR_HIP: return "HIP error";
+    case MSA_ERR_WORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+msa_status msa_get_layout(const msa_config* cfg, const msa_varlen* vl, msa_layout* out) {
+  if (!out) return fail(MSA_ERR_INVALID_ARG, "out must be non-null");
+  Plan P;
+  msa_status s = plan(cfg, vl, &P);
+  if (s != MSA_OK) return s;
+  *out = P.lay;
+  return MSA_OK;
+}
+
+msa_status msa_proxy_scores(const msa_config* cfg, const msa_varlen* vl, const void* qp,
+                            const void* kp, float* block_scores, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  Plan P;
+  msa_status s = plan(cfg, vl, &P);
+  if (s != MSA_OK) return s;
+  if (P.g.T == 0) return MSA_OK;
+  if ((s = check_ptrs({{qp, "qp"}, {kp, "kp"}, {block_scores, "block_scores"}})) != MSA_OK) return s;
+  if ((s = bind_workspace(&P, workspace, workspace_bytes, nullptr)) != MSA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = msa::launch_meta(P.g, st);
+  if (e != hipSuccess) return hip_fail(e, "metadata");
+  e = msa::launch_proxy_scores(P.g, cfg->dtype == MSA_BF16, qp, kp, block_scores, st);
+  if (e != hipSuccess) return hip_fail(e, "proxy_scores");
+  return MSA_OK;
+}
+
+msa_status msa_select_blocks(const msa_config* cfg, const msa_varlen* vl, const float* block_scores,
+                             int32_t* q2k_idx, int32_t* q2k_cnt, int32_t* k2q_ptr,
+                             int32_t* k2q_idx, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  Plan P;
+  msa_status s = plan(cfg, vl, &P);
+  if (s != MSA_OK) return s;
+  if (P.g.T == 0) return MSA_OK;
+  if ((s = check_ptrs({{block_scores, "block_scores"}, {q2k_idx, "q2k_idx"}, {q2k_cnt, "q2k_cnt"},
+                       {k2q_ptr, "k2q_ptr"}, {k2q_idx, "k2q_idx"}})) != MSA_OK)
+    return s;
+  msa::Work w;
+  if ((s = bind_workspace(&P, workspace, workspace_bytes, &w)) != MSA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = msa::launch_meta(P.g, st);
+  if (e != hipSuccess) return hip_fail(e, "metadata");
+  e = msa::launch_select(P.g, block_scores, q2k_idx, q2k_cnt, k2q_ptr, k2q_idx, w, st);
+  if (e != hipSuccess) return hip_fail(e, "select_blocks");
+  return MSA_OK;
+}
+
+msa_status msa_fwd(const msa_config* cfg, const msa_varlen* vl, const void* q, const void* k,
+                   const void* v, const void* qp, const void* kp, const int32_t* q2k_idx,
+                   const int32_t* q2k_cnt, void* o, float* lse, float* lse_p, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  Plan P;
+  msa_status s = plan(cfg, vl, &P);
+  if (s != MSA_OK) return s;
+  if (P.g.T == 0) return MSA_OK;
+  if ((s = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {qp, "qp"}, {kp, "kp"}, {q2k_idx, "q2k_idx"},
+                       {q2k_cnt, "q2k_cnt"}, {o, "o"}, {lse, "lse"}, {lse_p, "lse_p"}})) != MSA_OK)
+    return s;
+  if ((s = bind_workspace(&P, workspace, workspace_bytes, nullptr)) != MSA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = msa::launch_meta(P.g, st);
+  if (e != hipSuccess) return hip_fail(e, "metadata");
+  e = msa::launch_fwd(P.g, cfg->dtype == MSA_BF16, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, st);
+  if (e != hipSuccess) return hip_fail(e, "fwd");
+  return MSA_OK;
+}
+
+msa_status msa_bwd(const msa_config* cfg, const msa_varlen* vl, const void* q, const void* k,
+                   const void* v, const void* qp, const void* kp, const void* o, const float* lse,
+                   const float* lse_p, const void* dout, const int32_t* q2k_idx,
+                   const int32_t* q2k_cnt, const int32_t* k2q_ptr, const int32_t* k2q_idx,
+                   float* dq, float* dk, float* dv, float* dqp, float* dkp, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  Plan P;
+  msa_status s = plan(cfg, vl, &P);
+  if (s != MSA_OK) return s;
+  if (P.g.T == 0) return MSA_OK;
+  if ((s = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {qp, "qp"}, {kp, "kp"}, {o, "o"}, {lse, "lse"},
+                       {lse_p, "lse_p"}, {dout, "dout"}, {q2k_idx, "q2k_idx"}, {q2k_cnt, "q2k_cnt"},
+                       {k2q_ptr, "k2q_ptr"}, {k2q_idx, "k2q_idx"}, {dq, "dq"}, {dk, "dk"}, {dv, "dv"},
+                       {dqp, "dqp"}, {dkp, "dkp"}})) != MSA_OK)
+    return s;
+  msa::Work w;
+  if ((s = bind_workspace(&P, workspace, workspace_bytes, &w)) != MSA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = msa::launch_meta(P.g, st);
+  if (e != hipSuccess) return hip_fail(e, "metadata");
+  e = msa::launch_bwd(P.g, cfg->dtype == MSA_BF16, q, k, v, qp, kp, o, lse, lse_p, dout, q2k_idx,
+                      q2k_cnt, k2q_ptr, k2q_idx, dq, dk, dv, dqp, dkp, w, st);
+  if (e != hipSuccess) return hip_fail(e, "bwd");
+  return MSA_OK;
+}
+
+static std::vector<msa::KernelEntry> all_kernels() {
+  std::vector<msa::KernelEntry> v(64);
+  int n = 0;
+  n += msa::select_kernels(v.data() + n, 64 - n);
+  n += msa::fwd_kernels(v.data() + n, 64 - n);
+  n += msa::bwd_kernels(v.data() + n, 64 - n);
+  v.resize(n);
+  return v;
+}
+
+int32_t msa_kernel_count(void) { return (int32_t)all_kernels().size(); }
+
+msa_status msa_kernel_info(int32_t index, char* name, size_t name_len, int32_t* regs,
+                           int32_t* lds_bytes, int32_t* scratch_bytes, int32_t* wg_per_cu) {
+  g_last_error.clear();
+  auto ks = all_kernels();
+  if (index < 0 || index >= (int32_t)ks.size()) return fail(MSA_ERR_INVALID_ARG, "kernel index %d out of range", index);
+  const msa::KernelEntry& k = ks[index];
+  if (name && name_len > 0) {
+    std::strncpy(name, k.name, name_len - 1);
+    name[name_len - 1] = '\0';
+  }
+  hipFuncAttributes a;
+  hipError_t e = hipFuncGetAttributes(&a, k.fn);
+  if (e != hipSuccess) return hip_fail(e, "hipFuncGetAttributes");
+  if (k.dyn_lds > 65536) {
+    e = hipFuncSetAttribute(k.fn, hipFuncAttributeMaxDynamicSharedMemorySize, k.dyn_lds);
+    if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+  }
+  int nb = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k.fn, k.block, k.dyn_lds);
+  if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  if (regs) *regs = a.numRegs;
+  if (lds_bytes) *lds_bytes = (int32_t)a.sharedSizeBytes + k.dyn_lds;
+  if (scratch_bytes) *scratch_bytes = (int32_t)a.localSizeBytes;
+  if (wg_per_cu) *wg_per_cu = nb;
+  return MSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// Device-side building blocks shared by the MSA kernels (gfx950 / CDNA4).
+//
+// Matrix work uses the 32x32 MFMA family.  A "k-slice" is 16 contraction
+// slots; in every operand fragment lane l holds 8 of them (element j), with
+// the same (l >> 5, j) -> slot map for the A and the B operand, so any
+// consistent slot permutation computes the same contraction.
+//
+//   A fragment (M x 16): lane l -> row  m = l & 31, 8 slots
+//   B fragment (16 x N): lane l -> col  n = l & 31, 8 slots
+//   accumulator (32x32 fp32, 16 per lane): lane l -> col n = l & 31,
+//       element i -> row ((i >> 2) << 3) + ((l >> 5) << 2) + (i & 3)
+//
+// "Natural" slots: element j of lane l is slot ((l >> 5) << 3) + j, i.e. 8
+// contiguous elements of a row of the operand in memory.
+// "Accumulator" slots: element j of lane l in k-slice s of a 32-row
+// accumulator tile is row  s*16 + ((j >> 2) << 3) + ((l >> 5) << 2) + (j & 3),
+// so the accumulator's elements [8s, 8s+8) are directly a fragment whose
+// slots are the accumulator's rows.  The operand paired with it is read from a
+// transposed tile as two runs of 4 contiguous elements.
+//
+// bf16 tiles use v_mfma_f32_32x32x16_bf16.  fp32 tiles use eight
+// v_mfma_f32_32x32x2f32 steps per k-slice (step j contracts slot pair j).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float NEG_BIG = -1.0e30f;   // finite "minus infinity" for running maxima
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 type; typedef bf16x4 half; };
+template <> struct Frag<float> { typedef f32x8 type; typedef f32x4 half; };
+template <typename T> using frag_t = typename Frag<T>::type;
+template <typename T> using half_t = typename Frag<T>::half;
+
+__device__ __forceinline__ void mma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// 8 contiguous elements (16-byte aligned for bf16, 16-byte aligned for fp32).
+__device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f32x8 ld8(const float* p) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  f32x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { r[j] = a[j]; r[j + 4] = b[j]; }
+  return r;
+}
+// Two runs of 4 contiguous elements -> one fragment (accumulator-slot reads).
+__device__ __forceinline__ bf16x8 ld4x2(const bf16* p0, const bf16* p1) {
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { r[j] = a[j]; r[j + 4] = b[j]; }
+  return r;
+}
+__device__ __forceinline__ f32x8 ld4x2(const float* p0, const float* p1) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p0);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p1);
+  f32x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { r[j] = a[j]; r[j + 4] = b[j]; }
+  return r;
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// Elements [8s, 8s+8) of an accumulator as an operand fragment (accumulator slots).
+template <typename T>
+__device__ __forceinline__ frag_t<T> acc_frag(const f32x16& acc, int s) {
+  frag_t<T> r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = from_f32<T>(acc[s * 8 + j]);
+  return r;
+}
+
+// Row of accumulator element i for lane l (see the layout note above).
+__device__ __forceinline__ int acc_row(int i, int lane) {
+  return ((i >> 2) << 3) + ((lane >> 5) << 2) + (i & 3);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+// Fill kernel (used instead of memset so every clear is an ordinary launch).
+__global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n);
+
+}  // namespace msa

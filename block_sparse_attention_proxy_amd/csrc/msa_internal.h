@@ -1,0 +1,64 @@
+// Internal interface between the C-ABI layer (msa_api.cpp) and the kernel
+// launchers (*.hip).  Not installed; not part of the public header.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+// Geometry of one call, resolved on the host and passed to every kernel by value.
+struct Geo {
+  int32_t Hq, Hkv, G, D, DP;
+  int32_t Bq, topk, lw, stride;      // stride = topk + local_window
+  int32_t B, T, nqb, nkb;            // documents, tokens, total query / KV blocks
+  int32_t max_nq;                    // largest per-document query-block count
+  int64_t cap;                       // k2q capacity per group = nqb * stride
+  int64_t score_elems;               // per group
+  int32_t n_units;                   // proxy-scoring units (pairs of 128-row tiles)
+  float scale, pscale, lam;          // softmax scale, proxy scale, proxy loss weight
+  float scale_log2, pscale_log2;     // scale * log2(e), pscale * log2(e)
+  const int32_t* cu;                 // device cu_seqlens [B + 1]
+  // per-document tables written by the metadata kernel into the workspace
+  int32_t* qb0;                      // [B + 1] first global query block
+  int32_t* kb0;                      // [B + 1] first global KV block
+  int64_t* s0;                       // [B + 1] score-rectangle offset
+  int32_t* order;                    // [B]     documents by length, longest first
+  int32_t* unit0;                    // [B + 1] first scoring unit, in that order
+};
+
+// Workspace regions (byte offsets are computed by the host layout routine).
+struct Work {
+  int32_t* counts;                   // [Hkv * nkb]
+  int32_t* cursor;                   // [Hkv * nkb]
+  float* delta;                      // [Hq * T]       rowsum(dO * O)
+  float* cpart;                      // [Hkv * nhg * T * DP] proxy-gradient partials (G > 4)
+};
+
+hipError_t launch_meta(const Geo& g, hipStream_t s);
+hipError_t launch_proxy_scores(const Geo& g, int is_bf16, const void* qp, const void* kp,
+                               float* scores, hipStream_t s);
+hipError_t launch_select(const Geo& g, const float* scores, int32_t* q2k_idx, int32_t* q2k_cnt,
+                         int32_t* k2q_ptr, int32_t* k2q_idx, const Work& w, hipStream_t s);
+hipError_t launch_fwd(const Geo& g, int is_bf16, const void* q, const void* k, const void* v,
+                      const void* qp, const void* kp, const int32_t* q2k_idx,
+                      const int32_t* q2k_cnt, void* o, float* lse, float* lse_p, hipStream_t s);
+hipError_t launch_bwd(const Geo& g, int is_bf16, const void* q, const void* k, const void* v,
+                      const void* qp, const void* kp, const void* o, const float* lse,
+                      const float* lse_p, const void* dout, const int32_t* q2k_idx,
+                      const int32_t* q2k_cnt, const int32_t* k2q_ptr, const int32_t* k2q_idx,
+                      float* dq, float* dk, float* dv, float* dqp, float* dkp, const Work& w,
+                      hipStream_t s);
+
+// Kernel registry for the resource report: each translation unit lists the
+// kernels it instantiates, with the block size and dynamic LDS of its launch.
+struct KernelEntry {
+  const char* name;
+  const void* fn;
+  int block;
+  int dyn_lds;
+};
+int select_kernels(KernelEntry* out, int max);
+int fwd_kernels(KernelEntry* out, int max);
+int bwd_kernels(KernelEntry* out, int max);
+
+}  // namespace msa

@@ -1,0 +1,515 @@
+// Proxy block scoring, top-k block selection and the KV-major inverted index.
+//
+// Method (pages: ai-minor "Dramatically Speeding Up Million-Token Training!",
+// News Overview and Terminology; socker-news Flash-MSA summary 要約):
+// a proxy head scores query-key pairs, the scores are max-pooled over
+// 128-token KV blocks, and each query block keeps its best KV blocks.
+// Readings used here: the pooled tile is (query block x KV block), the raw
+// dot product <qp, kp> is pooled (a positive scale cannot change a ranking),
+// candidates are the blocks strictly before the forced diagonal + window, and
+// an exact score tie goes to the lower block index.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+__global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += step) p[i] = v;
+}
+
+static hipError_t fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+// Index b in [0, n) with a[b] <= x < a[b + 1] (a has n + 1 non-decreasing entries).
+template <typename I>
+__device__ __forceinline__ int find_segment(const I* a, int n, I x) {
+  int lo = 0, hi = n;  // invariant: a[lo] <= x, answer < hi
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+// metadata: per-document block offsets and a longest-first document order
+// ---------------------------------------------------------------------------
+
+// Block-wide exclusive scan of int64 values (256 threads); returns the
+// exclusive prefix of this thread's value and adds the chunk total to *carry.
+__device__ int64_t block_exscan256(int64_t v, int64_t* sh, int64_t& carry) {
+  const int t = threadIdx.x;
+  sh[t] = v;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    int64_t add = (t >= o) ? sh[t - o] : 0;
+    __syncthreads();
+    sh[t] += add;
+    __syncthreads();
+  }
+  int64_t incl = sh[t];
+  int64_t total = sh[255];
+  __syncthreads();
+  int64_t r = carry + incl - v;
+  carry += total;
+  return r;
+}
+
+__global__ __launch_bounds__(256) void meta_kernel(Geo g) {
+  __shared__ int64_t sh[256];
+  const int B = g.B;
+  int64_t cq = 0, ck = 0, cs = 0, cu_ = 0;
+  for (int base = 0; base < B + 1; base += 256) {
+    int b = base + threadIdx.x;
+    int64_t nq = 0, nk = 0;
+    if (b < B) {
+      int64_t L = g.cu[b + 1] - g.cu[b];
+      nq = (L + g.Bq - 1) / g.Bq;
+      nk = (L + 127) / 128;
+    }
+    int64_t eq = block_exscan256(nq, sh, cq);
+    int64_t ek = block_exscan256(nk, sh, ck);
+    int64_t es = block_exscan256(nq * nk, sh, cs);
+    if (b <= B) {
+      g.qb0[b] = (int32_t)eq;
+      g.kb0[b] = (int32_t)ek;
+      g.s0[b] = es;
+    }
+  }
+  // rank documents by length (longest first, index breaks ties)
+  for (int b = threadIdx.x; b < B; b += 256) {
+    int Lb = g.cu[b + 1] - g.cu[b];
+    int r = 0;
+    for (int c = 0; c < B; ++c) {
+      int Lc = g.cu[c + 1] - g.cu[c];
+      r += (Lc > Lb) || (Lc == Lb && c < b);
+    }
+    g.order[r] = b;
+  }
+  __syncthreads();
+  for (int base = 0; base < B + 1; base += 256) {
+    int r = base + threadIdx.x;
+    int64_t n = 0;
+    if (r < B) {
+      int b = g.order[r];
+      int64_t L = g.cu[b + 1] - g.cu[b];
+      int64_t tiles = (L + 127) / 128;
+      n = (tiles + 1) / 2;
+    }
+    int64_t e = block_exscan256(n, sh, cu_);
+    if (r <= B) g.unit0[r] = (int32_t)e;
+  }
+}
+
+hipError_t launch_meta(const Geo& g, hipStream_t s) {
+  hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// proxy scores: S[g, I, J] = max over the tile of <qp, kp>
+// ---------------------------------------------------------------------------
+//
+// One wave owns a unit = a pair of 128-row query tiles (p, nt - 1 - p) of one
+// document, so every unit of a document costs about the same.  Per tile it
+// keeps its 128 qp rows as A fragments and streams the candidate KV blocks of
+// kp as B fragments straight from global memory (the waves of a workgroup
+// walk the same KV blocks together and share them through the caches).
+// Each KV block gives four 32x32 row tiles x four 32-key tiles; the maxima are
+// folded per lane, reduced over the wave, and written 64 blocks at a time.
+
+template <typename T, int DP, int BQ>
+__global__ __launch_bounds__(256) void proxy_scores_kernel(const T* __restrict__ qp,
+                                                           const T* __restrict__ kp,
+                                                           float* __restrict__ scores, Geo g) {
+  constexpr int KSL = DP / 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int grp = blockIdx.x % g.Hkv;
+  const int unit = (blockIdx.x / g.Hkv) * 4 + wave;
+  if (unit >= g.n_units) return;   // no barriers below
+  const int r = find_segment<int32_t>(g.unit0, g.B, unit);
+  const int b = g.order[r];
+  const int p = unit - g.unit0[r];
+  const int t0 = g.cu[b];
+  const int L = g.cu[b + 1] - t0;
+  const int nt = (L + 127) >> 7;
+  const int nk = nt;
+  const int nq = (L + BQ - 1) / BQ;
+  const int64_t s0 = g.s0[b];
+  const int Hp = g.Hkv;
+  const int col = lane & 31;
+  const int hi8 = (lane >> 5) * 8;
+
+  for (int pass = 0; pass < 2; ++pass) {
+    const int tile = pass == 0 ? p : nt - 1 - p;
+    if (pass == 1 && tile == p) break;
+    if (tile + 1 <= g.topk + g.lw) continue;      // every block is selected; nothing to score
+    const int ncand = tile - g.lw;
+
+    frag_t<T> A[4][KSL];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      int row = tile * 128 + rt * 32 + col;
+      row = row < L ? row : L - 1;                // duplicate rows leave the max unchanged
+      const T* src = qp + ((int64_t)(t0 + row) * Hp + grp) * DP + hi8;
+#pragma unroll
+      for (int ks = 0; ks < KSL; ++ks) A[rt][ks] = ld8(src + ks * 16);
+    }
+    const int I0 = (BQ == 128) ? tile : 2 * tile;
+    const bool has1 = (BQ == 64) && (2 * tile + 1 < nq);
+    float* out0 = scores + (int64_t)grp * g.score_elems + s0 + (int64_t)I0 * nk;
+    float* out1 = out0 + nk;
+    float stash0 = 0.f, stash1 = 0.f;
+
+    frag_t<T> Bc[4][KSL];
+    auto load_b = [&](int J, frag_t<T> (&Bf)[4][KSL]) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const T* src = kp + ((int64_t)(t0 + J * 128 + kt * 32 + col) * Hp + grp) * DP + hi8;
+#pragma unroll
+        for (int ks = 0; ks < KSL; ++ks) Bf[kt][ks] = ld8(src + ks * 16);
+      }
+    };
+    load_b(0, Bc);
+    for (int J = 0; J < ncand; ++J) {
+      frag_t<T> Bn[4][KSL];
+      if (J + 1 < ncand) load_b(J + 1, Bn);
+      float m0 = NEG_BIG, m1 = NEG_BIG;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          f32x16 acc = zero16();
+#pragma unroll
+          for (int ks = 0; ks < KSL; ++ks) mma(acc, A[rt][ks], Bc[kt][ks]);
+          float mm = acc[0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) mm = fmaxf(mm, acc[i]);
+          if (BQ == 64 && rt >= 2) m1 = fmaxf(m1, mm); else m0 = fmaxf(m0, mm);
+        }
+      }
+      m0 = wave_max(m0);
+      if (BQ == 64) m1 = wave_max(m1);
+      if (lane == (J & 63)) { stash0 = m0; stash1 = m1; }
+      if ((J & 63) == 63 || J == ncand - 1) {
+        const int base = J & ~63;
+        if (lane <= (J & 63)) {
+          out0[base + lane] = stash0;
+          if (has1) out1[base + lane] = stash1;
+        }
+      }
+      if (J + 1 < ncand) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int ks = 0; ks < KSL; ++ks) Bc[kt][ks] = Bn[kt][ks];
+      }
+    }
+  }
+}
+
+template <typename T, int DP>
+static hipError_t scores_dispatch_bq(const Geo& g, const void* qp, const void* kp, float* scores,
+                                     hipStream_t s) {
+  int nblk = (g.n_units + 3) / 4 * g.Hkv;
+  if (nblk == 0) return hipSuccess;
+  if (g.Bq == 128)
+    hipLaunchKernelGGL((proxy_scores_kernel<T, DP, 128>), dim3(nblk), dim3(256), 0, s,
+                       (const T*)qp, (const T*)kp, scores, g);
+  else
+    hipLaunchKernelGGL((proxy_scores_kernel<T, DP, 64>), dim3(nblk), dim3(256), 0, s,
+                       (const T*)qp, (const T*)kp, scores, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_proxy_scores(const Geo& g, int is_bf16, const void* qp, const void* kp,
+                               float* scores, hipStream_t s) {
+  if (is_bf16) {
+    if (g.DP == 64) return scores_dispatch_bq<bf16, 64>(g, qp, kp, scores, s);
+    return scores_dispatch_bq<bf16, 32>(g, qp, kp, scores, s);
+  }
+  return scores_dispatch_bq<float, 32>(g, qp, kp, scores, s);
+}
+
+// ---------------------------------------------------------------------------
+// selection: one wave per (group, query block)
+// ---------------------------------------------------------------------------
+//
+// The k - 1 best candidates are found by a 4-pass, 8-bit radix select of the
+// (k-1)-th largest order-preserving key; keys above it are taken, and of the
+// keys equal to it the lowest block indices, up to k - 1 in total.  The pick
+// is emitted in ascending block order with a ballot prefix count, followed by
+// the forced window and diagonal blocks, then -1 padding.
+
+__device__ __forceinline__ uint32_t order_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;                   // -0 ties with +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ scores,
+                                                     int32_t* __restrict__ q2k_idx,
+                                                     int32_t* __restrict__ q2k_cnt, Geo g) {
+  __shared__ uint32_t hist[4][256];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const bool active = row < (int64_t)g.Hkv * g.nqb;
+  int grp = 0, QB = 0, b = 0, I = 0, diag = 0, nk = 0, kb0 = 0, ncand = 0, rem = 0, full = 1;
+  const float* srow = nullptr;
+  if (active) {
+    grp = (int)(row / g.nqb);
+    QB = (int)(row % g.nqb);
+    b = find_segment<int32_t>(g.qb0, g.B, QB);
+    I = QB - g.qb0[b];
+    const int L = g.cu[b + 1] - g.cu[b];
+    nk = (L + 127) >> 7;
+    kb0 = g.kb0[b];
+    diag = (I * g.Bq) >> 7;
+    full = (diag + 1) <= g.topk + g.lw;
+    if (!full) {
+      ncand = diag - g.lw;
+      rem = g.topk - 1;
+      srow = scores + (int64_t)grp * g.score_elems + g.s0[b] + (int64_t)I * nk;
+    }
+  }
+  uint32_t prefix = 0, pmask = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = lane; i < 256; i += 64) hist[wave][i] = 0;
+    __syncthreads();
+    if (rem > 0) {
+      for (int j = lane; j < ncand; j += 64) {
+        uint32_t key = order_key(srow[j]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    if (rem > 0) {
+      uint32_t h0 = hist[wave][4 * lane + 0], h1 = hist[wave][4 * lane + 1];
+      uint32_t h2 = hist[wave][4 * lane + 2], h3 = hist[wave][4 * lane + 3];
+      int c = (int)(h0 + h1 + h2 + h3);
+      int incl = c;  // inclusive suffix sum over lanes >= lane
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_down(incl, o, 64);
+        if (lane + o < 64) incl += t;
+      }
+      int above = incl - c;     // count in bins of higher lanes
+      int found = -1, newrem = 0;
+      uint32_t hb[4] = {h0, h1, h2, h3};
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        if (found < 0 && above < rem && rem <= above + (int)hb[q]) { found = q; newrem = rem - above; }
+        above += (int)hb[q];
+      }
+      uint64_t m = __ballot(found >= 0);
+      int src = __ffsll((unsigned long long)m) - 1;
+      int digit = __shfl(4 * lane + found, src, 64);
+      rem = __shfl(newrem, src, 64);
+      prefix |= (uint32_t)digit << shift;
+      pmask |= 255u << shift;
+    }
+  }
+  if (!active) return;
+  int32_t* out = q2k_idx + ((int64_t)grp * g.nqb + QB) * g.stride;
+  int pos = 0;
+  if (full) {
+    for (int j = lane; j <= diag; j += 64) out[j] = kb0 + j;
+    pos = diag + 1;
+  } else {
+    const uint32_t theta = prefix;
+    int eq_taken = 0;
+    for (int base = 0; base < ncand; base += 64) {
+      const int j = base + lane;
+      uint32_t key = 0;
+      if (j < ncand) key = order_key(srow[j]);
+      const bool valid = j < ncand && (g.topk > 1);
+      const bool gt = valid && key > theta;
+      const bool eq = valid && key == theta;
+      const uint64_t eqm = __ballot(eq);
+      const int eq_rank = eq_taken + __popcll(eqm & lanes_below(lane));
+      const bool take = gt || (eq && eq_rank < rem);
+      const uint64_t tm = __ballot(take);
+      if (take) out[pos + __popcll(tm & lanes_below(lane))] = kb0 + j;
+      pos += __popcll(tm);
+      eq_taken += __popcll(eqm);
+    }
+    for (int j = lane; j <= g.lw; j += 64) out[pos + j] = kb0 + diag - g.lw + j;
+    pos += g.lw + 1;
+  }
+  for (int j = pos + lane; j < g.stride; j += 64) out[j] = -1;
+  if (lane == 0) q2k_cnt[(int64_t)grp * g.nqb + QB] = pos;
+}
+
+// ---------------------------------------------------------------------------
+// inverted index: count -> exclusive scan -> scatter -> per-list sort
+// ---------------------------------------------------------------------------
+
+__global__ void k2q_count_kernel(const int32_t* __restrict__ q2k_idx,
+                                 const int32_t* __restrict__ q2k_cnt, int32_t* counts, Geo g) {
+  const int64_t n = (int64_t)g.Hkv * g.nqb * g.stride;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t rowi = e / g.stride;
+    const int slot = (int)(e % g.stride);
+    if (slot < q2k_cnt[rowi]) {
+      const int grp = (int)(rowi / g.nqb);
+      atomicAdd(&counts[(int64_t)grp * g.nkb + q2k_idx[e]], 1);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k2q_scan_kernel(const int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ k2q_ptr, Geo g) {
+  __shared__ int64_t sh[256];
+  const int grp = blockIdx.x;
+  int64_t carry = 0;
+  for (int base = 0; base < g.nkb + 1; base += 256) {
+    const int i = base + threadIdx.x;
+    const int64_t v = i < g.nkb ? counts[(int64_t)grp * g.nkb + i] : 0;
+    const int64_t e = block_exscan256(v, sh, carry);
+    if (i <= g.nkb) k2q_ptr[(int64_t)grp * (g.nkb + 1) + i] = (int32_t)e;
+  }
+}
+
+__global__ void k2q_scatter_kernel(const int32_t* __restrict__ q2k_idx,
+                                   const int32_t* __restrict__ q2k_cnt,
+                                   const int32_t* __restrict__ k2q_ptr, int32_t* cursor,
+                                   int32_t* __restrict__ k2q_idx, Geo g) {
+  const int64_t n = (int64_t)g.Hkv * g.nqb * g.stride;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t rowi = e / g.stride;
+    const int slot = (int)(e % g.stride);
+    if (slot < q2k_cnt[rowi]) {
+      const int grp = (int)(rowi / g.nqb);
+      const int QB = (int)(rowi % g.nqb);
+      const int KB = q2k_idx[e];
+      const int at = atomicAdd(&cursor[(int64_t)grp * g.nkb + KB], 1);
+      k2q_idx[(int64_t)grp * g.cap + k2q_ptr[(int64_t)grp * (g.nkb + 1) + KB] + at] = QB;
+    }
+  }
+}
+
+__global__ void k2q_tail_kernel(const int32_t* __restrict__ k2q_ptr, int32_t* __restrict__ k2q_idx,
+                                Geo g) {
+  const int64_t n = (int64_t)g.Hkv * g.cap;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int grp = (int)(e / g.cap);
+    const int64_t i = e % g.cap;
+    if (i >= k2q_ptr[(int64_t)grp * (g.nkb + 1) + g.nkb]) k2q_idx[e] = -1;
+  }
+}
+
+// Sort one inverted list ascending (bitonic, in LDS).  Lists hold distinct
+// query-block ids, so the sorted list is unique whatever order the scatter's
+// atomics produced.
+__global__ __launch_bounds__(256) void k2q_sort_kernel(const int32_t* __restrict__ k2q_ptr,
+                                                       int32_t* __restrict__ k2q_idx, Geo g) {
+  extern __shared__ int32_t sh[];
+  const int grp = blockIdx.x / g.nkb;
+  const int KB = blockIdx.x % g.nkb;
+  const int32_t* ptr = k2q_ptr + (int64_t)grp * (g.nkb + 1);
+  const int beg = ptr[KB];
+  const int len = ptr[KB + 1] - beg;
+  if (len <= 1) return;
+  int P = 1;
+  while (P < len) P <<= 1;
+  int32_t* seg = k2q_idx + (int64_t)grp * g.cap + beg;
+  for (int i = threadIdx.x; i < P; i += blockDim.x) sh[i] = i < len ? seg[i] : 0x7fffffff;
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const bool up = (i & k) == 0;
+          const int32_t a = sh[i], c = sh[ixj];
+          if ((a > c) == up) { sh[i] = c; sh[ixj] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < len; i += blockDim.x) seg[i] = sh[i];
+}
+
+static int grid_for(int64_t n, int threads) {
+  int64_t b = (n + threads - 1) / threads;
+  if (b < 1) b = 1;
+  if (b > 65536) b = 65536;
+  return (int)b;
+}
+
+hipError_t launch_select(const Geo& g, const float* scores, int32_t* q2k_idx, int32_t* q2k_cnt,
+                         int32_t* k2q_ptr, int32_t* k2q_idx, const Work& w, hipStream_t s) {
+  hipError_t e;
+  const int64_t rows = (int64_t)g.Hkv * g.nqb;
+  if (rows > 0) {
+    hipLaunchKernelGGL(select_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, scores,
+                       q2k_idx, q2k_cnt, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t nc = (int64_t)g.Hkv * g.nkb;
+  if ((e = fill_i32(w.counts, 0, nc, s)) != hipSuccess) return e;
+  if ((e = fill_i32(w.cursor, 0, nc, s)) != hipSuccess) return e;
+  const int64_t ne = rows * g.stride;
+  if (ne > 0) {
+    hipLaunchKernelGGL(k2q_count_kernel, dim3(grid_for(ne, 256)), dim3(256), 0, s, q2k_idx,
+                       q2k_cnt, w.counts, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k2q_scan_kernel, dim3(g.Hkv), dim3(256), 0, s, w.counts, k2q_ptr, g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ne > 0) {
+    hipLaunchKernelGGL(k2q_scatter_kernel, dim3(grid_for(ne, 256)), dim3(256), 0, s, q2k_idx,
+                       q2k_cnt, k2q_ptr, w.cursor, k2q_idx, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t ncap = (int64_t)g.Hkv * g.cap;
+  if (ncap > 0) {
+    hipLaunchKernelGGL(k2q_tail_kernel, dim3(grid_for(ncap, 256)), dim3(256), 0, s, k2q_ptr,
+                       k2q_idx, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (nc > 0) {
+    int P = 1;
+    while (P < g.max_nq) P <<= 1;
+    hipLaunchKernelGGL(k2q_sort_kernel, dim3((unsigned)nc), dim3(256), (size_t)P * 4, s, k2q_ptr,
+                       k2q_idx, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace msa
+
+namespace msa {
+int select_kernels(KernelEntry* out, int max) {
+  const KernelEntry all[] = {
+      {"proxy_scores<bf16,dp64,bq128>", (const void*)proxy_scores_kernel<bf16, 64, 128>, 256, 0},
+      {"proxy_scores<bf16,dp64,bq64>", (const void*)proxy_scores_kernel<bf16, 64, 64>, 256, 0},
+      {"proxy_scores<bf16,dp32,bq64>", (const void*)proxy_scores_kernel<bf16, 32, 64>, 256, 0},
+      {"proxy_scores<f32,dp32,bq64>", (const void*)proxy_scores_kernel<float, 32, 64>, 256, 0},
+      {"select", (const void*)select_kernel, 256, 0},
+      {"k2q_sort", (const void*)k2q_sort_kernel, 256, 4096 * 4},
+  };
+  int n = (int)(sizeof(all) / sizeof(all[0]));
+  for (int i = 0; i < n && i < max; ++i) out[i] = all[i];
+  return n;
+}
+}  // namespace msa

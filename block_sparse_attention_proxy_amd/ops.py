@@ -1,0 +1,213 @@
+"""Python face of the C ABI: the same entry points, taking torch tensors.
+
+Each function checks devices, dtypes, shapes and contiguity, then passes raw
+pointers and the current HIP stream to libmsa.so.  No computation happens
+here.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import MsaConfig, MsaLayout, MsaVarlen, check, load
+
+
+@dataclass(frozen=True)
+class Config:
+    """Mirror of ``msa_config``.  Scales of 0 mean 1/sqrt(d) and 1/sqrt(dp)."""
+    heads_q: int
+    heads_kv: int
+    head_dim: int
+    proxy_dim: int
+    q_block: int
+    topk: int
+    local_window: int = 0
+    kv_block: int = 128
+    softmax_scale: float = 0.0
+    proxy_scale: float = 0.0
+    proxy_loss_weight: float = 1.0
+    dtype: str = "bf16"
+
+    def to_c(self) -> MsaConfig:
+        return MsaConfig(self.heads_q, self.heads_kv, self.head_dim, self.proxy_dim, self.kv_block,
+                         self.q_block, self.topk, self.local_window, self.softmax_scale,
+                         self.proxy_scale, self.proxy_loss_weight,
+                         _lib.MSA_BF16 if self.dtype == "bf16" else _lib.MSA_F32)
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+class Varlen:
+    """cu_seqlens on the device plus the host copy the library reads for sizes."""
+
+    def __init__(self, cu_seqlens: torch.Tensor, cu_seqlens_host: Optional[Sequence[int]] = None):
+        if cu_seqlens.dtype != torch.int32:
+            raise ValueError("cu_seqlens must be int32")
+        self.cu = cu_seqlens.contiguous()
+        host = cu_seqlens.cpu().numpy() if cu_seqlens_host is None else cu_seqlens_host
+        self.host = np.ascontiguousarray(np.asarray(host, dtype=np.int32))
+        self.batch = len(self.host) - 1
+        self.total = int(self.host[-1]) if len(self.host) else 0
+
+    def to_c(self) -> MsaVarlen:
+        ptr = self.host.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        dev = self.cu.data_ptr() if self.cu.is_cuda else None
+        return MsaVarlen(dev, ptr, self.batch, self.total)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def msa_get_layout(cfg: Config, vl: Varlen) -> dict:
+    lib = load()
+    out = MsaLayout()
+    c, v = cfg.to_c(), vl.to_c()
+    check(lib.msa_get_layout(ctypes.byref(c), ctypes.byref(v), ctypes.byref(out)))
+    return out.as_dict()
+
+
+def msa_proxy_scores(cfg: Config, vl: Varlen, qp, kp, block_scores, workspace, stream=None):
+    lib = load()
+    lay = msa_get_layout(cfg, vl)
+    T, Hp, dp = vl.total, cfg.heads_kv, cfg.proxy_dim
+    dt = cfg.torch_dtype
+    a = [_ptr(qp, "qp", dt, (T, Hp, dp)), _ptr(kp, "kp", dt, (T, Hp, dp)),
+         _ptr(block_scores, "block_scores", torch.float32, (Hp, lay["score_elems"])),
+         _ptr(workspace, "workspace", torch.uint8)]
+    c, v = cfg.to_c(), vl.to_c()
+    check(lib.msa_proxy_scores(ctypes.byref(c), ctypes.byref(v), a[0], a[1], a[2], a[3],
+                               workspace.numel(), _stream(stream)))
+
+
+def msa_select_blocks(cfg: Config, vl: Varlen, block_scores, q2k_idx, q2k_cnt, k2q_ptr, k2q_idx,
+                      workspace, stream=None):
+    lib = load()
+    lay = msa_get_layout(cfg, vl)
+    Hp = cfg.heads_kv
+    i32 = torch.int32
+    a = [_ptr(block_scores, "block_scores", torch.float32, (Hp, lay["score_elems"])),
+         _ptr(q2k_idx, "q2k_idx", i32, (Hp, lay["total_qblocks"], lay["sel_stride"])),
+         _ptr(q2k_cnt, "q2k_cnt", i32, (Hp, lay["total_qblocks"])),
+         _ptr(k2q_ptr, "k2q_ptr", i32, (Hp, lay["total_kvblocks"] + 1)),
+         _ptr(k2q_idx, "k2q_idx", i32, (Hp, lay["k2q_capacity"])),
+         _ptr(workspace, "workspace", torch.uint8)]
+    c, v = cfg.to_c(), vl.to_c()
+    check(lib.msa_select_blocks(ctypes.byref(c), ctypes.byref(v), *a, workspace.numel(),
+                                _stream(stream)))
+
+
+def msa_fwd(cfg: Config, vl: Varlen, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, workspace,
+            stream=None):
+    lib = load()
+    lay = msa_get_layout(cfg, vl)
+    T, Hq, Hkv, d, dp = vl.total, cfg.heads_q, cfg.heads_kv, cfg.head_dim, cfg.proxy_dim
+    dt, i32, f32 = cfg.torch_dtype, torch.int32, torch.float32
+    a = [_ptr(q, "q", dt, (T, Hq, d)), _ptr(k, "k", dt, (T, Hkv, d)), _ptr(v, "v", dt, (T, Hkv, d)),
+         _ptr(qp, "qp", dt, (T, Hkv, dp)), _ptr(kp, "kp", dt, (T, Hkv, dp)),
+         _ptr(q2k_idx, "q2k_idx", i32, (Hkv, lay["total_qblocks"], lay["sel_stride"])),
+         _ptr(q2k_cnt, "q2k_cnt", i32, (Hkv, lay["total_qblocks"])),
+         _ptr(o, "o", dt, (T, Hq, d)), _ptr(lse, "lse", f32, (Hq, T)),
+         _ptr(lse_p, "lse_p", f32, (Hkv, T)), _ptr(workspace, "workspace", torch.uint8)]
+    c, vv = cfg.to_c(), vl.to_c()
+    check(lib.msa_fwd(ctypes.byref(c), ctypes.byref(vv), *a, workspace.numel(), _stream(stream)))
+
+
+def msa_bwd(cfg: Config, vl: Varlen, q, k, v, qp, kp, o, lse, lse_p, dout, q2k_idx, q2k_cnt,
+            k2q_ptr, k2q_idx, dq, dk, dv, dqp, dkp, workspace, stream=None):
+    lib = load()
+    lay = msa_get_layout(cfg, vl)
+    T, Hq, Hkv, d, dp = vl.total, cfg.heads_q, cfg.heads_kv, cfg.head_dim, cfg.proxy_dim
+    dt, i32, f32 = cfg.torch_dtype, torch.int32, torch.float32
+    a = [_ptr(q, "q", dt, (T, Hq, d)), _ptr(k, "k", dt, (T, Hkv, d)), _ptr(v, "v", dt, (T, Hkv, d)),
+         _ptr(qp, "qp", dt, (T, Hkv, dp)), _ptr(kp, "kp", dt, (T, Hkv, dp)),
+         _ptr(o, "o", dt, (T, Hq, d)), _ptr(lse, "lse", f32, (Hq, T)),
+         _ptr(lse_p, "lse_p", f32, (Hkv, T)), _ptr(dout, "dout", dt, (T, Hq, d)),
+         _ptr(q2k_idx, "q2k_idx", i32, (Hkv, lay["total_qblocks"], lay["sel_stride"])),
+         _ptr(q2k_cnt, "q2k_cnt", i32, (Hkv, lay["total_qblocks"])),
+         _ptr(k2q_ptr, "k2q_ptr", i32, (Hkv, lay["total_kvblocks"] + 1)),
+         _ptr(k2q_idx, "k2q_idx", i32, (Hkv, lay["k2q_capacity"])),
+         _ptr(dq, "dq", f32, (T, Hq, d)), _ptr(dk, "dk", f32, (T, Hkv, d)),
+         _ptr(dv, "dv", f32, (T, Hkv, d)), _ptr(dqp, "dqp", f32, (T, Hkv, dp)),
+         _ptr(dkp, "dkp", f32, (T, Hkv, dp)), _ptr(workspace, "workspace", torch.uint8)]
+    c, vv = cfg.to_c(), vl.to_c()
+    check(lib.msa_bwd(ctypes.byref(c), ctypes.byref(vv), *a, workspace.numel(), _stream(stream)))
+
+
+def kernel_resources() -> list:
+    """Per-kernel VGPRs, LDS bytes, scratch bytes and resident workgroups per CU (needs a GPU)."""
+    lib = load()
+    out = []
+    for i in range(lib.msa_kernel_count()):
+        name = ctypes.create_string_buffer(96)
+        regs, lds, scr, occ = (ctypes.c_int32() for _ in range(4))
+        check(lib.msa_kernel_info(i, name, 96, ctypes.byref(regs), ctypes.byref(lds),
+                                  ctypes.byref(scr), ctypes.byref(occ)))
+        out.append(dict(name=name.value.decode(), vgprs=regs.value, lds_bytes=lds.value,
+                        scratch_bytes=scr.value, workgroups_per_cu=occ.value))
+    return out
+
+
+class Buffers:
+    """Every device buffer of one layer call, allocated once with torch."""
+
+    def __init__(self, cfg: Config, vl: Varlen, device="cuda", need_bwd: bool = True):
+        lay = msa_get_layout(cfg, vl)
+        self.layout = lay
+        T, Hq, Hkv, d, dp = vl.total, cfg.heads_q, cfg.heads_kv, cfg.head_dim, cfg.proxy_dim
+        i32, f32 = torch.int32, torch.float32
+        z = dict(device=device)
+        self.workspace = torch.empty(max(lay["workspace_bytes"], 16), dtype=torch.uint8, **z)
+        self.scores = torch.empty((Hkv, max(lay["score_elems"], 1)), dtype=f32, **z)[:, :lay["score_elems"]]
+        if lay["score_elems"] == 0:
+            self.scores = torch.empty((Hkv, 0), dtype=f32, **z)
+        self.q2k_idx = torch.empty((Hkv, lay["total_qblocks"], lay["sel_stride"]), dtype=i32, **z)
+        self.q2k_cnt = torch.empty((Hkv, lay["total_qblocks"]), dtype=i32, **z)
+        self.k2q_ptr = torch.empty((Hkv, lay["total_kvblocks"] + 1), dtype=i32, **z)
+        self.k2q_idx = torch.empty((Hkv, lay["k2q_capacity"]), dtype=i32, **z)
+        self.o = torch.empty((T, Hq, d), dtype=cfg.torch_dtype, **z)
+        self.lse = torch.empty((Hq, T), dtype=f32, **z)
+        self.lse_p = torch.empty((Hkv, T), dtype=f32, **z)
+        if need_bwd:
+            self.dq = torch.empty((T, Hq, d), dtype=f32, **z)
+            self.dk = torch.empty((T, Hkv, d), dtype=f32, **z)
+            self.dv = torch.empty((T, Hkv, d), dtype=f32, **z)
+            self.dqp = torch.empty((T, Hkv, dp), dtype=f32, **z)
+            self.dkp = torch.empty((T, Hkv, dp), dtype=f32, **z)
+
+
+def run_forward(cfg: Config, vl: Varlen, q, k, v, qp, kp, buf: Buffers, stream=None):
+    """proxy scores -> selection (+ inverted index) -> sparse forward."""
+    msa_proxy_scores(cfg, vl, qp, kp, buf.scores, buf.workspace, stream)
+    msa_select_blocks(cfg, vl, buf.scores, buf.q2k_idx, buf.q2k_cnt, buf.k2q_ptr, buf.k2q_idx,
+                      buf.workspace, stream)
+    msa_fwd(cfg, vl, q, k, v, qp, kp, buf.q2k_idx, buf.q2k_cnt, buf.o, buf.lse, buf.lse_p,
+            buf.workspace, stream)
+
+
+def run_backward(cfg: Config, vl: Varlen, q, k, v, qp, kp, dout, buf: Buffers, stream=None):
+    msa_bwd(cfg, vl, q, k, v, qp, kp, buf.o, buf.lse, buf.lse_p, dout, buf.q2k_idx, buf.q2k_cnt,
+            buf.k2q_ptr, buf.k2q_idx, buf.dq, buf.dk, buf.dv, buf.dqp, buf.dkp, buf.workspace, stream)
