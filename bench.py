@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA training hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+proxy block scores -> block selection (+ inverted index) -> sparse GQA
+forward (+ proxy LSE) -> fused main + proxy backward, all through the C ABI.
+Inputs are drawn on the device before timing (resident in HBM).
+
+Default workload: ``varlen-1m-packed`` (1,048,576 tokens packed from seeded
+log-uniform document lengths, 32 query / 8 KV heads, d 128, dp 64, query
+block 128, top-k 64), bf16 inputs with fp32 accumulation.
+
+Prints one JSON line.  ``value`` is the step's TFLOP/s: the proxy-scoring
+FLOPs plus the forward and backward FLOPs over the selected (query, key)
+pairs (FlashAttention convention: 4 d per pair forward, 10 d backward; proxy
+2 dp forward, 6 dp backward), divided by the measured step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X published dense bf16/fp16
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+METRIC = "MSA fwd+bwd ms/step and TFLOP/s (selected FLOPs) at 128k–1M tok; % MFMA peak"
+ROOFLINE_KERNELS = ("proxy_scores", "fwd", "bwd_dq", "bwd_dkdv")
+
+
+def selected_pairs(seqlens, q_block, topk, window):
+    """Exactly-valid (query, key) pairs attended per KV group (every group has
+    the same count: the number of selected blocks depends only on the
+    diagonal).  Non-diagonal selected blocks lie wholly before the query
+    block; the diagonal block contributes the causal triangle."""
+    total = 0
+    for L in seqlens:
+        nq = -(-L // q_block)
+        for I in range(nq):
+            lo = I * q_block
+            rows = min(q_block, L - lo)
+            diag = lo // 128
+            cnt = min(topk + window, diag + 1)
+            first = lo - diag * 128 + 1           # keys of the diagonal block for query lo
+            total += rows * 128 * (cnt - 1) + rows * first + rows * (rows - 1) // 2
+    return total
+
+
+def flop_model(w, seqlens, scored_pairs):
+    d, dp, Hq, Hp = w.head_dim, w.proxy_dim, w.heads_q, w.heads_kv
+    n = selected_pairs(seqlens, w.q_block, w.topk, w.local_window)
+    f = {
+        "pairs_per_group": n,
+        "scoring": 2 * dp * Hp * scored_pairs,
+        "fwd_counted": 4 * d * Hq * n + 2 * dp * Hp * n,
+        "bwd_counted": 10 * d * Hq * n + 6 * dp * Hp * n,
+        # per-kernel algorithmic work
+        "k:proxy_scores": 2 * dp * Hp * scored_pairs,
+        "k:fwd": 4 * d * Hq * n,
+        "k:proxy_lse": 2 * dp * Hp * n,
+        "k:bwd_dq": 6 * d * Hq * n + 4 * dp * Hp * n,
+        "k:bwd_dkdv": 8 * d * Hq * n + 4 * dp * Hp * n,
+    }
+    return f
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "proxy_scores": ["block_sparse_attention_proxy_amd/csrc/select.hip"],
+    "select": ["block_sparse_attention_proxy_amd/csrc/select.hip"],
+    "fwd": ["block_sparse_attention_proxy_amd/csrc/attn_fwd.hip"],
+    "bwd_dq": ["block_sparse_attention_proxy_amd/csrc/attn_bwd.hip"],
+    "bwd_dkdv": ["block_sparse_attention_proxy_amd/csrc/attn_bwd.hip"],
+}
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tab = json.load(f)
+    ent = tab.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seqlens, x, budget_s, seed):
+    """The oracle, untuned, on a bounded sample of the same workload: scoring,
+    selection, forward and backward of sampled query blocks of the longest
+    document, in the oracle's fp64 numpy.  Returns TFLOP/s under the same
+    FLOP convention."""
+    import numpy as np
+    import torch
+    from oracle import msa_oracle as om
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    ocfg = om.Config(w.heads_q, w.heads_kv, w.head_dim, w.proxy_dim, w.q_block, w.topk, w.local_window)
+    b = max(range(len(seqlens)), key=lambda i: seqlens[i])
+    s0 = int(sum(seqlens[:b]))
+    L = seqlens[b]
+    doc = om.Doc(0, L, -(-L // w.q_block), -(-L // 128), 0, 0, 0)
+    g = 0
+    sl = slice(s0, s0 + L)
+
+    def host(name, heads):
+        return x[name][sl, heads].float().cpu().numpy().astype(np.float64)
+
+    G = w.group
+    arrs = dict(q=host("q", slice(g * G, (g + 1) * G)), k=host("k", slice(g, g + 1)),
+                v=host("v", slice(g, g + 1)), qp=host("qp", slice(g, g + 1)),
+                kp=host("kp", slice(g, g + 1)), dO=host("dO", slice(g * G, (g + 1) * G)))
+    c1 = om.Config(G, 1, w.head_dim, w.proxy_dim, w.q_block, w.topk, w.local_window)
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(doc.nq)
+    flops, done, t0 = 0, 0, time.perf_counter()
+    for I in order:
+        I = int(I)
+        S = om.proxy_row_scores(arrs["qp"], arrs["kp"], doc, 0, I, c1)
+        sel = om.select_row(S, I, c1)
+        fw = om.qblock_forward(arrs["q"], arrs["k"], arrs["v"], arrs["qp"], arrs["kp"], doc, 0, I, sel, c1)
+        om.qblock_backward(fw, arrs["q"], arrs["k"], arrs["v"], arrs["qp"], arrs["kp"], arrs["dO"], 0, c1)
+        rows = len(fw["rows"])
+        n = int(fw["mask"].sum())
+        flops += 2 * w.proxy_dim * rows * len(S) * 128
+        flops += (4 + 10) * w.head_dim * G * n + (2 + 6) * w.proxy_dim * n
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} query blocks (group 0, all {G} heads) of the longest document "
+                      f"({L} tokens): scoring, selection, forward and backward in fp64 numpy, "
+                      f"{dt:.1f} s wall", "seconds": dt}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="varlen-1m-packed")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0 = skip)")
+    ap.add_argument("--report", default=None, help="also write the JSON (plus details) here")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (this path has no "
+              "multi-GPU mode: each GPU would run the same op on its own documents).", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        return 1
+    import block_sparse_attention_proxy_amd as msa
+    from msa_inputs import WORKLOADS, make_case_torch, seqlens_of
+
+    w = WORKLOADS[a.workload]
+    seqlens = seqlens_of(w, a.seed)
+    t_gen = time.perf_counter()
+    x = make_case_torch(w, a.seed, device="cuda", seqlens=seqlens)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    cfg = msa.Config(w.heads_q, w.heads_kv, w.head_dim, w.proxy_dim, w.q_block, w.topk, w.local_window,
+                     128, 0.0, 0.0, w.proxy_loss_weight, w.dtype)
+    vl = msa.Varlen(x["cu_seqlens"], x["cu_seqlens"].cpu().numpy())
+    buf = msa.Buffers(cfg, vl, device="cuda", need_bwd=True)
+    lay = buf.layout
+
+    def step():
+        msa.run_forward(cfg, vl, x["q"], x["k"], x["v"], x["qp"], x["kp"], buf)
+        msa.run_backward(cfg, vl, x["q"], x["k"], x["v"], x["qp"], x["kp"], x["dO"], buf)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    msa.profile_enable(True)
+    msa.profile_collect()                       # drop anything recorded before the timed region
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(a.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = ev0.elapsed_time(ev1) / a.steps
+    kern = msa.profile_collect()
+    msa.profile_enable(False)
+
+    f = flop_model(w, seqlens, lay["scored_pairs"])
+    per_kernel = {k: {"avg_ms": ms / n, "launches_per_step": n / a.steps} for k, (ms, n) in kern.items()}
+    stage_of = {"proxy_scores": "scores", "select": "select", "k2q_count": "select", "k2q_scan": "select",
+                "k2q_scatter": "select", "k2q_tail": "select", "k2q_sort": "select", "fill": "select",
+                "fwd": "fwd", "proxy_lse": "fwd", "bwd_delta": "bwd", "bwd_dq": "bwd",
+                "bwd_dqp_reduce": "bwd", "bwd_dkdv": "bwd", "meta": "meta"}
+    stages = {}
+    for k, (ms, n) in kern.items():
+        stages[stage_of.get(k, k)] = stages.get(stage_of.get(k, k), 0.0) + ms / a.steps
+    for k, v in per_kernel.items():
+        if "k:" + k in f:
+            v["tflops"] = f["k:" + k] / (v["avg_ms"] * 1e-3) / 1e12
+    total_flops = f["scoring"] + f["fwd_counted"] + f["bwd_counted"]
+    value = total_flops / (step_ms * 1e-3) / 1e12
+    attn_ms = stages.get("fwd", 0.0) + stages.get("bwd", 0.0)
+    attn_tflops = (f["fwd_counted"] + f["bwd_counted"]) / (attn_ms * 1e-3) / 1e12 if attn_ms else None
+
+    dom = max(ROOFLINE_KERNELS, key=lambda k: per_kernel.get(k, {}).get("avg_ms", 0.0) *
+              per_kernel.get(k, {}).get("launches_per_step", 0.0))
+    achieved = per_kernel[dom]["tflops"]
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_for(dom, a.workload), "kernel": dom,
+                "avg_launch_ms": round(per_kernel[dom]["avg_ms"], 4),
+                "flops_per_launch": f["k:" + dom]}
+    # selection kernel against HBM: candidate scores read + block lists written
+    n_cand_entries = 0
+    for L in seqlens:
+        nq = -(-L // w.q_block)
+        for I in range(nq):
+            diag = I * w.q_block // 128
+            if diag + 1 > w.topk + w.local_window:
+                n_cand_entries += diag - w.local_window
+    sel_bytes = w.heads_kv * (4 * n_cand_entries + 4 * lay["total_qblocks"] * (lay["sel_stride"] + 1))
+    selection = None
+    if "select" in per_kernel:
+        gbps = sel_bytes / (per_kernel["select"]["avg_ms"] * 1e-3) / 1e9
+        selection = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": sel_bytes}
+
+    cpu = None
+    if a.cpu_budget > 0:
+        cpu = cpu_baseline(w, seqlens, x, a.cpu_budget, a.seed)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "total_tokens": int(sum(seqlens)), "docs": len(seqlens),
+                   "heads_q": w.heads_q, "heads_kv": w.heads_kv, "head_dim": w.head_dim,
+                   "proxy_dim": w.proxy_dim, "kv_block": 128, "q_block": w.q_block, "topk": w.topk,
+                   "local_window": w.local_window, "seed": a.seed, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
+        "stages_ms": {k: round(v, 3) for k, v in sorted(stages.items())},
+        "attn_fwd_bwd_tflops": None if attn_tflops is None else round(attn_tflops, 2),
+        "attn_mfma_frac": None if attn_tflops is None else round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "selection_roofline": selection,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in sorted(per_kernel.items())},
+        "flops": {k: v for k, v in f.items() if not k.startswith("k:")},
+        "wall_s_timed": round(wall, 3),
+        "input_gen_s": round(t_gen, 2),
+    }
+    line = json.dumps(out)
+    print(line, flush=True)
+    if a.report:
+        with open(a.report, "w") as fh:
+            fh.write(line + "\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

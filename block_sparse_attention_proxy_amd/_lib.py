@@ -19,7 +19,7 @@ MSA_BF16, MSA_F32 = 0, 1
 # Every symbol include/msa.h declares.
 EXPORTS = ("msa_abi_version", "msa_status_string", "msa_last_error", "msa_get_layout",
            "msa_proxy_scores", "msa_select_blocks", "msa_fwd", "msa_bwd", "msa_kernel_count",
-           "msa_kernel_info")
+           "msa_kernel_info", "msa_profile_enable", "msa_profile_collect", "msa_profile_entry")
 
 
 class MsaConfig(ctypes.Structure):
@@ -80,7 +80,12 @@ def load():
     lib.msa_kernel_count.restype = c_int32
     lib.msa_kernel_info.restype = c_int32
     lib.msa_kernel_info.argtypes = [c_int32, c_char_p, c_size_t, pi, pi, pi, pi]
-    _ = pi
+    lib.msa_profile_enable.restype = c_int32
+    lib.msa_profile_enable.argtypes = [c_int32]
+    lib.msa_profile_collect.restype = c_int32
+    lib.msa_profile_entry.restype = c_int32
+    lib.msa_profile_entry.argtypes = [c_int32, c_char_p, c_size_t, POINTER(ctypes.c_double),
+                                      POINTER(c_int64)]
     _lib = lib
     return lib
 

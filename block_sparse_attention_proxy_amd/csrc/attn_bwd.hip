@@ -19,6 +19,7 @@
 //                  KV block owned by one workgroup, so no atomics
 #include "msa_device.h"
 #include "msa_internal.h"
+#include "msa_profile.h"
 
 namespace msa {
 
@@ -585,28 +586,32 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
   hipError_t e;
   const int64_t nd = (int64_t)g.T * g.Hq;
   if (nd > 0) {
+    { ProfScope _ps("bwd_delta", s);
     hipLaunchKernelGGL((delta_kernel<T, D>), dim3(grid_for_b(nd, 256)), dim3(256), 0, s,
-                       (const T*)o, (const T*)dout, w.delta, g);
+                       (const T*)o, (const T*)dout, w.delta, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int NU = g.G * (g.Bq / 32);
   const int64_t nq = (int64_t)g.Hkv * g.nqb * ((NU + 3) / 4);
   if (nq > 0) {
+    { ProfScope _ps("bwd_dq", s);
     hipLaunchKernelGGL((dq_kernel<T, D, DP>), dim3((unsigned)nq), dim3(256), CQ::LDS_BYTES, s,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)qp, (const T*)kp, lse, lse_p,
-                       (const T*)dout, w.delta, q2k_idx, q2k_cnt, dq, dqp, w.cpart, g);
+                       (const T*)dout, w.delta, q2k_idx, q2k_cnt, dq, dqp, w.cpart, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (g.G > 4 && g.T > 0) {
+    { ProfScope _ps("bwd_dqp_reduce", s);
     hipLaunchKernelGGL((dqp_reduce_kernel<DP>), dim3(grid_for_b((int64_t)g.T * g.Hkv * DP, 256)),
-                       dim3(256), 0, s, w.cpart, dqp, g);
+                       dim3(256), 0, s, w.cpart, dqp, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t nk = (int64_t)g.Hkv * g.nkb;
   if (nk > 0) {
+    { ProfScope _ps("bwd_dkdv", s);
     hipLaunchKernelGGL((dkdv_kernel<T, D, DP>), dim3((unsigned)nk), dim3(256), CK::LDS_BYTES, s,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)qp, (const T*)kp, lse, lse_p,
-                       (const T*)dout, w.delta, k2q_ptr, k2q_idx, dk, dv, dkp, g);
+                       (const T*)dout, w.delta, k2q_ptr, k2q_idx, dk, dv, dkp, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

@@ -18,6 +18,7 @@
 // contractions), which keeps the main kernel's registers for attention.
 #include "msa_device.h"
 #include "msa_internal.h"
+#include "msa_profile.h"
 
 namespace msa {
 
@@ -358,14 +359,16 @@ static hipError_t fwd_dispatch(const Geo& g, const void* q, const void* k, const
   const int NU = g.G * (g.Bq / (32 * QT));
   const int64_t nblk = (int64_t)g.Hkv * g.nqb * ((NU + 3) / 4);
   if (nblk == 0) return hipSuccess;
+  { ProfScope _ps("fwd", s);
   hipLaunchKernelGGL(fn, dim3((unsigned)nblk), dim3(256), C::LDS_BYTES, s, (const T*)q, (const T*)k,
-                     (const T*)v, (const T*)qp, (const T*)kp, q2k_idx, q2k_cnt, (T*)o, lse, lse_p, g);
+                     (const T*)v, (const T*)qp, (const T*)kp, q2k_idx, q2k_cnt, (T*)o, lse, lse_p, g); }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int per_wg = 4 / (g.Bq / 32);
   const int64_t nrow = (int64_t)g.Hkv * g.nqb;
+  { ProfScope _ps("proxy_lse", s);
   hipLaunchKernelGGL((proxy_lse_kernel<T, DP>), dim3((unsigned)((nrow + per_wg - 1) / per_wg)), dim3(256),
-                     0, s, (const T*)qp, (const T*)kp, q2k_idx, q2k_cnt, lse_p, g);
+                     0, s, (const T*)qp, (const T*)kp, q2k_idx, q2k_cnt, lse_p, g); }
   return hipGetLastError();
 }
 

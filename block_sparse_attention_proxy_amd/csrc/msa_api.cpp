@@ -12,6 +12,7 @@
 
 #include "../../include/msa.h"
 #include "msa_internal.h"
+#include "msa_profile.h"
 
 namespace {
 
@@ -168,9 +169,91 @@ msa_status check_ptrs(std::initializer_list<std::pair<const void*, const char*>>
   return MSA_OK;
 }
 
+// ---- per-kernel timing -----------------------------------------------------
+struct ProfRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+struct ProfAgg {
+  std::string name;
+  double ms;
+  int64_t launches;
+};
+thread_local bool t_prof_on = false;
+thread_local std::vector<hipEvent_t> t_pool;
+thread_local std::vector<ProfRecord> t_records;
+thread_local std::vector<ProfAgg> t_agg;
+thread_local const char* t_open_name = nullptr;
+thread_local hipEvent_t t_open_start = nullptr;
+
+hipEvent_t pool_get() {
+  if (!t_pool.empty()) {
+    hipEvent_t e = t_pool.back();
+    t_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
 }  // namespace
 
+namespace msa {
+bool prof_enabled() { return t_prof_on; }
+void prof_begin(const char* name, hipStream_t s) {
+  t_open_name = name;
+  t_open_start = pool_get();
+  if (t_open_start) (void)hipEventRecord(t_open_start, s);
+}
+void prof_end(hipStream_t s) {
+  hipEvent_t stop = pool_get();
+  if (!t_open_start || !stop) return;
+  (void)hipEventRecord(stop, s);
+  t_records.push_back({t_open_name, t_open_start, stop});
+  t_open_start = nullptr;
+}
+}  // namespace msa
+
 extern "C" {
+
+msa_status msa_profile_enable(int32_t on) {
+  g_last_error.clear();
+  t_prof_on = on != 0;
+  return MSA_OK;
+}
+
+int32_t msa_profile_collect(void) {
+  t_agg.clear();
+  for (const ProfRecord& r : t_records) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) == hipSuccess && hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+      bool found = false;
+      for (ProfAgg& a : t_agg)
+        if (a.name == r.name) { a.ms += ms; a.launches += 1; found = true; break; }
+      if (!found) t_agg.push_back({r.name, (double)ms, 1});
+    }
+    t_pool.push_back(r.start);
+    t_pool.push_back(r.stop);
+  }
+  t_records.clear();
+  return (int32_t)t_agg.size();
+}
+
+msa_status msa_profile_entry(int32_t index, char* name, size_t name_len, double* total_ms,
+                             int64_t* launches) {
+  g_last_error.clear();
+  if (index < 0 || index >= (int32_t)t_agg.size())
+    return fail(MSA_ERR_INVALID_ARG, "profile entry %d out of range", index);
+  if (name && name_len > 0) {
+    std::strncpy(name, t_agg[index].name.c_str(), name_len - 1);
+    name[name_len - 1] = '\0';
+  }
+  if (total_ms) *total_ms = t_agg[index].ms;
+  if (launches) *launches = t_agg[index].launches;
+  return MSA_OK;
+}
+
 
 int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
 

@@ -10,6 +10,7 @@
 // an exact score tie goes to the lower block index.
 #include "msa_device.h"
 #include "msa_internal.h"
+#include "msa_profile.h"
 
 namespace msa {
 
@@ -23,8 +24,9 @@ static hipError_t fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
+  { ProfScope _ps("fill", s);
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, v, n);
-  return hipGetLastError();
+  return hipGetLastError(); }
 }
 
 // Index b in [0, n) with a[b] <= x < a[b + 1] (a has n + 1 non-decreasing entries).
@@ -109,8 +111,9 @@ __global__ __launch_bounds__(256) void meta_kernel(Geo g) {
 }
 
 hipError_t launch_meta(const Geo& g, hipStream_t s) {
+  { ProfScope _ps("meta", s);
   hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(256), 0, s, g);
-  return hipGetLastError();
+  return hipGetLastError(); }
 }
 
 // ---------------------------------------------------------------------------
@@ -222,11 +225,13 @@ static hipError_t scores_dispatch_bq(const Geo& g, const void* qp, const void* k
   int nblk = (g.n_units + 3) / 4 * g.Hkv;
   if (nblk == 0) return hipSuccess;
   if (g.Bq == 128)
+    { ProfScope _ps("proxy_scores", s);
     hipLaunchKernelGGL((proxy_scores_kernel<T, DP, 128>), dim3(nblk), dim3(256), 0, s,
-                       (const T*)qp, (const T*)kp, scores, g);
+                       (const T*)qp, (const T*)kp, scores, g); }
   else
+    { ProfScope _ps("proxy_scores", s);
     hipLaunchKernelGGL((proxy_scores_kernel<T, DP, 64>), dim3(nblk), dim3(256), 0, s,
-                       (const T*)qp, (const T*)kp, scores, g);
+                       (const T*)qp, (const T*)kp, scores, g); }
   return hipGetLastError();
 }
 
@@ -460,8 +465,9 @@ hipError_t launch_select(const Geo& g, const float* scores, int32_t* q2k_idx, in
   hipError_t e;
   const int64_t rows = (int64_t)g.Hkv * g.nqb;
   if (rows > 0) {
+    { ProfScope _ps("select", s);
     hipLaunchKernelGGL(select_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, scores,
-                       q2k_idx, q2k_cnt, g);
+                       q2k_idx, q2k_cnt, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t nc = (int64_t)g.Hkv * g.nkb;
@@ -469,28 +475,33 @@ hipError_t launch_select(const Geo& g, const float* scores, int32_t* q2k_idx, in
   if ((e = fill_i32(w.cursor, 0, nc, s)) != hipSuccess) return e;
   const int64_t ne = rows * g.stride;
   if (ne > 0) {
+    { ProfScope _ps("k2q_count", s);
     hipLaunchKernelGGL(k2q_count_kernel, dim3(grid_for(ne, 256)), dim3(256), 0, s, q2k_idx,
-                       q2k_cnt, w.counts, g);
+                       q2k_cnt, w.counts, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k2q_scan_kernel, dim3(g.Hkv), dim3(256), 0, s, w.counts, k2q_ptr, g);
+  { ProfScope _ps("k2q_scan", s);
+  hipLaunchKernelGGL(k2q_scan_kernel, dim3(g.Hkv), dim3(256), 0, s, w.counts, k2q_ptr, g); }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ne > 0) {
+    { ProfScope _ps("k2q_scatter", s);
     hipLaunchKernelGGL(k2q_scatter_kernel, dim3(grid_for(ne, 256)), dim3(256), 0, s, q2k_idx,
-                       q2k_cnt, k2q_ptr, w.cursor, k2q_idx, g);
+                       q2k_cnt, k2q_ptr, w.cursor, k2q_idx, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t ncap = (int64_t)g.Hkv * g.cap;
   if (ncap > 0) {
+    { ProfScope _ps("k2q_tail", s);
     hipLaunchKernelGGL(k2q_tail_kernel, dim3(grid_for(ncap, 256)), dim3(256), 0, s, k2q_ptr,
-                       k2q_idx, g);
+                       k2q_idx, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (nc > 0) {
     int P = 1;
     while (P < g.max_nq) P <<= 1;
+    { ProfScope _ps("k2q_sort", s);
     hipLaunchKernelGGL(k2q_sort_kernel, dim3((unsigned)nc), dim3(256), (size_t)P * 4, s, k2q_ptr,
-                       k2q_idx, g);
+                       k2q_idx, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

@@ -171,6 +171,24 @@ def kernel_resources() -> list:
     return out
 
 
+def profile_enable(on: bool = True) -> None:
+    """Start (or stop) per-kernel HIP-event timing on this thread."""
+    check(load().msa_profile_enable(1 if on else 0))
+
+
+def profile_collect() -> dict:
+    """Wait for the recorded events; {kernel name: (total ms, launches)}; clears the record."""
+    lib = load()
+    n = lib.msa_profile_collect()
+    out = {}
+    for i in range(n):
+        name = ctypes.create_string_buffer(64)
+        ms, cnt = ctypes.c_double(), ctypes.c_int64()
+        check(lib.msa_profile_entry(i, name, 64, ctypes.byref(ms), ctypes.byref(cnt)))
+        out[name.value.decode()] = (ms.value, cnt.value)
+    return out
+
+
 class Buffers:
     """Every device buffer of one layer call, allocated once with torch."""
 

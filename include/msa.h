@@ -170,6 +170,21 @@ int32_t msa_kernel_count(void);
 msa_status msa_kernel_info(int32_t index, char* name, size_t name_len, int32_t* regs,
                            int32_t* lds_bytes, int32_t* scratch_bytes, int32_t* wg_per_cu);
 
+/*
+ * Per-kernel timing, for roofline figures.  While enabled (per calling
+ * thread), every kernel launch the library makes is bracketed by two
+ * hipEvents recorded on the launch stream; the events come from a pool the
+ * library creates on first use and keeps until the process ends.
+ * msa_profile_collect waits for the recorded events, sums the elapsed time
+ * per kernel name, clears the record and returns the number of names;
+ * msa_profile_entry(i, ...) reads name i, its total milliseconds and its
+ * launch count.  Needs a GPU.
+ */
+msa_status msa_profile_enable(int32_t on);
+int32_t msa_profile_collect(void);
+msa_status msa_profile_entry(int32_t index, char* name, size_t name_len, double* total_ms,
+                             int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif
