@@ -21,6 +21,8 @@
 #include "msa_internal.h"
 #include "msa_profile.h"
 
+#include <type_traits>
+
 namespace msa {
 
 __device__ __forceinline__ int xcd_remap_b(int i, int n) {
@@ -56,17 +58,19 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, con
 // ---------------------------------------------------------------------------
 // dQ kernel: a workgroup serves (group, query block, 4 units); a wave owns 32
 // queries of one head.  Stages are 64-key halves of the selected blocks with
-// K (rows and transposed), V rows, kp (rows and transposed) in LDS.
+// K, V and kp rows in LDS; K^T and kp^T fragments come from the same tiles
+// through LDS transpose reads.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int DP>
 struct DqCfg {
   static constexpr int KC = 64, PAD = 8, EPC = 16 / (int)sizeof(T);
-  static constexpr int LDK = D + PAD, LDT = KC + PAD, LDP = DP + PAD;
-  static constexpr int KS = KC * LDK, VS = KC * LDK, KT = D * LDT, KPS = KC * LDP, KPT = DP * LDT;
-  static constexpr int STAGE = KS + VS + KT + KPS + KPT;
+  static constexpr int LDK = D + PAD, LDP = DP + PAD;
+  static constexpr int KS = KC * LDK, KPS = KC * LDP;
+  static constexpr int STAGE = 2 * KS + KPS;
   static constexpr int LDS_BYTES = 2 * STAGE * (int)sizeof(T);
   static constexpr int CPR = D / EPC, CPRP = DP / EPC;
   static constexpr int NK = KC * CPR / 256, NP = KC * CPRP / 256;
+  static_assert(NK >= 1 && NP >= 1, "tile split");
   static_assert(4 * DP * 32 * 4 <= LDS_BYTES, "reduction scratch");
 };
 
@@ -138,14 +142,14 @@ __global__ __launch_bounds__(256) void dq_kernel(
     const int key0 = J * 128 + (s & 1) * C::KC;
 #pragma unroll
     for (int i = 0; i < C::NK; ++i) {
-      const int c = tid + 256 * i, r = c % C::KC, cc = c / C::KC, key = key0 + r;
+      const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR, key = key0 + r;
       const int64_t off = ((int64_t)(t0 + key) * g.Hkv + grp) * D + cc * C::EPC;
       Kr[i] = key < L ? *reinterpret_cast<const uint4*>(k + off) : make_uint4(0, 0, 0, 0);
       Vr[i] = key < L ? *reinterpret_cast<const uint4*>(v + off) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::NP; ++i) {
-      const int c = tid + 256 * i, r = c % C::KC, cc = c / C::KC, key = key0 + r;
+      const int c = tid + 256 * i, r = c / C::CPRP, cc = c % C::CPRP, key = key0 + r;
       Pr[i] = key < L ? *reinterpret_cast<const uint4*>(kp + ((int64_t)(t0 + key) * g.Hkv + grp) * DP + cc * C::EPC)
                       : make_uint4(0, 0, 0, 0);
     }
@@ -153,25 +157,66 @@ __global__ __launch_bounds__(256) void dq_kernel(
   auto store_stage = [&](int buf) {
     T* Ks = smem + buf * C::STAGE;
     T* Vs = Ks + C::KS;
-    T* Kt = Vs + C::VS;
-    T* KPs = Kt + C::KT;
-    T* KPt = KPs + C::KPS;
+    T* KPs = Vs + C::KS;
 #pragma unroll
     for (int i = 0; i < C::NK; ++i) {
-      const int c = tid + 256 * i, r = c % C::KC, cc = c / C::KC;
+      const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR;
       *reinterpret_cast<uint4*>(Ks + r * C::LDK + cc * C::EPC) = Kr[i];
       *reinterpret_cast<uint4*>(Vs + r * C::LDK + cc * C::EPC) = Vr[i];
-      const T* e = reinterpret_cast<const T*>(&Kr[i]);
-#pragma unroll
-      for (int j = 0; j < C::EPC; ++j) Kt[(cc * C::EPC + j) * C::LDT + r] = e[j];
     }
 #pragma unroll
     for (int i = 0; i < C::NP; ++i) {
-      const int c = tid + 256 * i, r = c % C::KC, cc = c / C::KC;
+      const int c = tid + 256 * i, r = c / C::CPRP, cc = c % C::CPRP;
       *reinterpret_cast<uint4*>(KPs + r * C::LDP + cc * C::EPC) = Pr[i];
-      const T* e = reinterpret_cast<const T*>(&Pr[i]);
+    }
+  };
+
+  // one 32-key tile of a stage
+  auto tile = [&](const T* Ks, const T* Vs, const T* KPs, int kt, int kpos, bool assigned, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
+    f32x16 S = zero16(), dP = zero16();
 #pragma unroll
-      for (int j = 0; j < C::EPC; ++j) KPt[(cc * C::EPC + j) * C::LDT + r] = e[j];
+    for (int ks = 0; ks < D / 16; ++ks) {
+      mma(S, ld8(Ks + (kt * 32 + col) * C::LDK + ks * 16 + hi * 8), Qf[ks]);
+      mma(dP, ld8(Vs + (kt * 32 + col) * C::LDK + ks * 16 + hi * 8), dOf[ks]);
+    }
+    const int lim = qpos - kpos;                         // key row r is visible iff r <= lim
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = __builtin_amdgcn_exp2f(fmaf(S[i], g.scale_log2, -lse2));
+      if (MASK && acc_row(i, lane) > lim) p = 0.f;
+      S[i] = p;
+      dP[i] = p * (dP[i] - dl);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const frag_t<T> bs = acc_frag<T>(dP, kk);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        mma(dQ[dt], lds_col_frag<T>(Ks, C::LDK, kt * 32 + kk * 16, dt * 32, lane), bs);
+    }
+    // proxy: E = [assigned] Q - P / G ;  C^T += kp^T E^T
+    if (assigned) {
+      f32x16 Y = zero16();
+#pragma unroll
+      for (int ks = 0; ks < DP / 16; ++ks)
+        mma(Y, ld8(KPs + (kt * 32 + col) * C::LDP + ks * 16 + hi * 8), QPf[ks]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], g.pscale_log2, -lsep2));
+        if (MASK && acc_row(i, lane) > lim) qv = 0.f;
+        S[i] = qv - S[i] * invG;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[i] = -S[i] * invG;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const frag_t<T> be = acc_frag<T>(S, kk);
+#pragma unroll
+      for (int dt = 0; dt < DP / 32; ++dt)
+        mma(Cp[dt], lds_col_frag<T>(KPs, C::LDP, kt * 32 + kk * 16, dt * 32, lane), be);
     }
   };
 
@@ -186,71 +231,16 @@ __global__ __launch_bounds__(256) void dq_kernel(
     if (active && kpos0 <= qbase + 31) {
       const T* Ks = smem + buf * C::STAGE;
       const T* Vs = Ks + C::KS;
-      const T* Kt = Vs + C::VS;
-      const T* KPs = Kt + C::KT;
-      const T* KPt = KPs + C::KPS;
-      const bool need_mask = (J == diag);
-      f32x16 S[2], dP[2];
+      const T* KPs = Vs + C::KS;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        S[kt] = zero16();
-        dP[kt] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const frag_t<T> a = ld8(Ks + (kt * 32 + col) * C::LDK + ks * 16 + hi * 8);
-          mma(S[kt], a, Qf[ks]);
-          const frag_t<T> bv = ld8(Vs + (kt * 32 + col) * C::LDK + ks * 16 + hi * 8);
-          mma(dP[kt], bv, dOf[ks]);
-        }
-      }
-      // P (into S) and dS (into dP)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = __builtin_amdgcn_exp2f(S[kt][i] * g.scale_log2 - lse2);
-          if (need_mask && kpos0 + kt * 32 + acc_row(i, lane) > qpos) p = 0.f;
-          S[kt][i] = p;
-          dP[kt][i] = p * (dP[kt][i] - dl);
-        }
-      // dQ^T += K^T dS^T
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const frag_t<T> bs = acc_frag<T>(dP[kk >> 1], kk & 1);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const T* kr = Kt + (dt * 32 + col) * C::LDT + kk * 16 + hi * 4;
-          mma(dQ[dt], ld4x2(kr, kr + 8), bs);
-        }
-      }
-      // proxy: E = [assigned] Q - P / G ;  C^T += kp^T E^T
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+        const int kpos = kpos0 + kt * 32;
         const bool assigned = ((s * 2 + kt) % g.G) == hl;
-        if (assigned) {
-          f32x16 Y = zero16();
-#pragma unroll
-          for (int ks = 0; ks < DP / 16; ++ks)
-            mma(Y, ld8(KPs + (kt * 32 + col) * C::LDP + ks * 16 + hi * 8), QPf[ks]);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float qv = __builtin_amdgcn_exp2f(Y[i] * g.pscale_log2 - lsep2);
-            if (need_mask && kpos0 + kt * 32 + acc_row(i, lane) > qpos) qv = 0.f;
-            S[kt][i] = qv - S[kt][i] * invG;
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) S[kt][i] = -S[kt][i] * invG;
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const frag_t<T> be = acc_frag<T>(S[kk >> 1], kk & 1);
-#pragma unroll
-        for (int dt = 0; dt < DP / 32; ++dt) {
-          const T* pr = KPt + (dt * 32 + col) * C::LDT + kk * 16 + hi * 4;
-          mma(Cp[dt], ld4x2(pr, pr + 8), be);
-        }
+        if (kpos > qbase + 31) break;                     // every key of the tile follows every query
+        if (J == diag && kpos + 31 > qbase)
+          tile(Ks, Vs, KPs, kt, kpos, assigned, std::true_type());
+        else
+          tile(Ks, Vs, KPs, kt, kpos, assigned, std::false_type());
       }
     }
     if (s + 1 < nst) store_stage(buf ^ 1);
@@ -322,18 +312,19 @@ __global__ void dqp_reduce_kernel(const float* __restrict__ cpart, float* __rest
 // ---------------------------------------------------------------------------
 // dK/dV kernel: a workgroup owns one KV block of one group; wave w owns keys
 // [32w, 32w + 32) and keeps K, V, kp of them as B fragments.  Stages walk the
-// inverted list: (query block, 32-query chunk, head), with Q and dO staged in
-// LDS both row-major and transposed.  T (the group-mean probability) is
-// accumulated over the heads of a chunk, and the proxy term is applied at the
-// chunk's last head, whose stage also carries qp.
+// inverted list: (query block, 32-query chunk, head), with Q and dO rows in
+// LDS (their transposed fragments come through LDS transpose reads).  T (the
+// group-mean probability) is accumulated over the heads of a chunk, and the
+// proxy term is applied at the chunk's last head, whose stage also carries qp.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int DP>
 struct KvCfg {
   static constexpr int QC = 32, PAD = 8, EPC = 16 / (int)sizeof(T);
-  static constexpr int LDQ = D + PAD, LDT = QC + PAD, LDP = DP + PAD;
-  static constexpr int QS = QC * LDQ, QTT = D * LDT, PS = QC * LDP, PT = DP * LDT;
-  static constexpr int STAGE_T = 2 * QS + 2 * QTT + PS + PT;       // elements of T
-  static constexpr int STAGE_BYTES = ((STAGE_T * (int)sizeof(T) + 15) / 16) * 16 + 3 * QC * 4;
+  static constexpr int LDQ = D + PAD, LDP = DP + PAD;
+  static constexpr int QS = QC * LDQ, PS = QC * LDP;
+  static constexpr int STAGE_T = 2 * QS + PS;                        // elements of T
+  static constexpr int FL_OFF = ((STAGE_T * (int)sizeof(T) + 15) / 16) * 16;
+  static constexpr int STAGE_BYTES = FL_OFF + 3 * QC * 4;
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
   static constexpr int CPR = D / EPC, CPRP = DP / EPC;
   static constexpr int NQ = QC * CPR / 256, NP = (QC * CPRP + 255) / 256;
@@ -341,7 +332,7 @@ struct KvCfg {
   static_assert(NQ >= 1 && NP >= 1, "tile split");
 };
 
-template <typename T, int D, int DP>
+template <typename T, int D, int DP, int G>
 __global__ __launch_bounds__(256) void dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ qp, const T* __restrict__ kp, const float* __restrict__ lse,
@@ -363,11 +354,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
   const int kpos = J * 128 + wave * 32 + col;               // this lane's key (B-fragment column)
   const int krow = kpos < L ? kpos : L - 1;
   const int64_t tk = t0 + krow;
-  const int32_t* lst = k2q_idx + (int64_t)grp * g.cap + k2q_ptr[(int64_t)grp * (g.nkb + 1) + KB];
-  const int len = k2q_ptr[(int64_t)grp * (g.nkb + 1) + KB + 1] - k2q_ptr[(int64_t)grp * (g.nkb + 1) + KB];
+  const int32_t* ptr = k2q_ptr + (int64_t)grp * (g.nkb + 1);
+  const int32_t* lst = k2q_idx + (int64_t)grp * g.cap + ptr[KB];
+  const int len = ptr[KB + 1] - ptr[KB];
   const int nch = g.Bq / 32;
-  const int G = g.G;
   const float invG = 1.f / (float)G;
+  const float lam_ps = g.lam * g.pscale;
 
   frag_t<T> Kf[D / 16], Vf[D / 16], KPf[DP / 16];
   {
@@ -385,156 +377,154 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
 #pragma unroll
   for (int dt = 0; dt < DP / 32; ++dt) dKp[dt] = zero16();
 
-  const int nst = len * nch * G;
   uint4 Qr[C::NQ], Dr[C::NQ], Pr[C::NP];
   float lr = 0.f, dlr = 0.f, lpr = 0.f;
-  auto stage_of = [&](int s, int& I, int& c, int& hl) {
-    hl = s % G;
-    c = (s / G) % nch;
-    I = lst[s / (G * nch)] - qb0;
-  };
-  auto load_stage = [&](int s) {
-    int I, c, hl;
-    stage_of(s, I, c, hl);
+  // Stage = (list entry li, query chunk c, head hl); with_qp for the chunk's last head.
+  auto load_stage = [&](int li, int c, int hl, bool with_qp) {
+    const int I = lst[li] - qb0;
     const int h = grp * G + hl;
     const int row0 = I * g.Bq + c * 32;
 #pragma unroll
     for (int i = 0; i < C::NQ; ++i) {
-      const int e = tid + 256 * i, r = e % C::QC, cc = e / C::QC, pos = row0 + r;
+      const int e = tid + 256 * i, r = e / C::CPR, cc = e % C::CPR, pos = row0 + r;
       const int64_t off = ((int64_t)(t0 + pos) * g.Hq + h) * D + cc * C::EPC;
       Qr[i] = pos < L ? *reinterpret_cast<const uint4*>(q + off) : make_uint4(0, 0, 0, 0);
       Dr[i] = pos < L ? *reinterpret_cast<const uint4*>(dout + off) : make_uint4(0, 0, 0, 0);
     }
-    const bool last = hl == G - 1;
-    if (last) {
+    if (with_qp) {
 #pragma unroll
       for (int i = 0; i < C::NP; ++i) {
-        const int e = tid + 256 * i, r = e % C::QC, cc = e / C::QC, pos = row0 + r;
-        if (e >= C::NPE) break;
-        Pr[i] = pos < L ? *reinterpret_cast<const uint4*>(qp + ((int64_t)(t0 + pos) * g.Hkv + grp) * DP + cc * C::EPC)
-                        : make_uint4(0, 0, 0, 0);
+        const int e = tid + 256 * i, r = e / C::CPRP, cc = e % C::CPRP, pos = row0 + r;
+        if (e < C::NPE)
+          Pr[i] = pos < L ? *reinterpret_cast<const uint4*>(qp + ((int64_t)(t0 + pos) * g.Hkv + grp) * DP + cc * C::EPC)
+                          : make_uint4(0, 0, 0, 0);
       }
     }
     if (tid < C::QC) {
       const int pos = row0 + tid;
       const bool ok = pos < L;
-      const int64_t t = t0 + pos;
-      lr = ok ? lse[(int64_t)h * g.T + t] * LOG2E : INFINITY;   // invalid rows get P = 0
+      const int64_t t = t0 + (ok ? pos : 0);
+      lr = ok ? lse[(int64_t)h * g.T + t] * LOG2E : INFINITY;   // rows past the end get P = 0
       dlr = ok ? delta[(int64_t)h * g.T + t] : 0.f;
-      lpr = (ok && last) ? lse_p[(int64_t)grp * g.T + t] * LOG2E : INFINITY;
+      lpr = (ok && with_qp) ? lse_p[(int64_t)grp * g.T + t] * LOG2E : INFINITY;
     }
   };
-  auto store_stage = [&](int buf, int s) {
+  auto store_stage = [&](int buf, bool with_qp) {
     unsigned char* base = smem_raw + buf * C::STAGE_BYTES;
     T* Qs = reinterpret_cast<T*>(base);
     T* dOs = Qs + C::QS;
-    T* Qt = dOs + C::QS;
-    T* dOt = Qt + C::QTT;
-    T* Ps = dOt + C::QTT;
-    T* Pt = Ps + C::PS;
-    float* fl = reinterpret_cast<float*>(base + ((C::STAGE_T * (int)sizeof(T) + 15) / 16) * 16);
+    T* Ps = dOs + C::QS;
+    float* fl = reinterpret_cast<float*>(base + C::FL_OFF);
 #pragma unroll
     for (int i = 0; i < C::NQ; ++i) {
-      const int e = tid + 256 * i, r = e % C::QC, cc = e / C::QC;
+      const int e = tid + 256 * i, r = e / C::CPR, cc = e % C::CPR;
       *reinterpret_cast<uint4*>(Qs + r * C::LDQ + cc * C::EPC) = Qr[i];
       *reinterpret_cast<uint4*>(dOs + r * C::LDQ + cc * C::EPC) = Dr[i];
-      const T* eq = reinterpret_cast<const T*>(&Qr[i]);
-      const T* ed = reinterpret_cast<const T*>(&Dr[i]);
-#pragma unroll
-      for (int j = 0; j < C::EPC; ++j) {
-        Qt[(cc * C::EPC + j) * C::LDT + r] = eq[j];
-        dOt[(cc * C::EPC + j) * C::LDT + r] = ed[j];
-      }
     }
-    if ((s % G) == G - 1) {
+    if (with_qp) {
 #pragma unroll
       for (int i = 0; i < C::NP; ++i) {
-        const int e = tid + 256 * i, r = e % C::QC, cc = e / C::QC;
-        if (e >= C::NPE) break;
-        *reinterpret_cast<uint4*>(Ps + r * C::LDP + cc * C::EPC) = Pr[i];
-        const T* ep = reinterpret_cast<const T*>(&Pr[i]);
-#pragma unroll
-        for (int j = 0; j < C::EPC; ++j) Pt[(cc * C::EPC + j) * C::LDT + r] = ep[j];
+        const int e = tid + 256 * i, r = e / C::CPRP, cc = e % C::CPRP;
+        if (e < C::NPE) *reinterpret_cast<uint4*>(Ps + r * C::LDP + cc * C::EPC) = Pr[i];
       }
     }
     if (tid < C::QC) { fl[tid] = lr; fl[C::QC + tid] = dlr; fl[2 * C::QC + tid] = lpr; }
   };
-
-  if (nst > 0) { load_stage(0); store_stage(0, 0); }
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nst) load_stage(s + 1);
-    int I, c, hl;
-    stage_of(s, I, c, hl);
-    const int diag = (I * g.Bq) >> 7;
-    const int qpos0 = I * g.Bq + c * 32;
-    const bool need_mask = (J == diag);
-    // skip when every key of this wave lies after every query of the chunk
-    const bool skip = need_mask && (J * 128 + wave * 32 > qpos0 + 31);
-    const unsigned char* base = smem_raw + buf * C::STAGE_BYTES;
+  // per-lane values of the 16 query rows held by accumulator elements
+  auto rows16 = [&](const float* f, float (&out)[16]) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(f + acc_row(i4 * 4, lane));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[i4 * 4 + j] = x[j];
+    }
+  };
+  // rows below lim_base are queries that precede this lane's key (masked)
+  auto main_part = [&](const unsigned char* base, int lim_base) {
     const T* Qs = reinterpret_cast<const T*>(base);
     const T* dOs = Qs + C::QS;
-    const T* Qt = dOs + C::QS;
-    const T* dOt = Qt + C::QTT;
-    const T* Ps = dOt + C::QTT;
-    const T* Pt = Ps + C::PS;
-    const float* fl = reinterpret_cast<const float*>(base + ((C::STAGE_T * (int)sizeof(T) + 15) / 16) * 16);
-    if (!skip) {
-      f32x16 S = zero16(), dP = zero16();
+    const float* fl = reinterpret_cast<const float*>(base + C::FL_OFF);
+    f32x16 S = zero16(), dP = zero16();
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        mma(S, ld8(Qs + col * C::LDQ + ks * 16 + hi * 8), Kf[ks]);
-        mma(dP, ld8(dOs + col * C::LDQ + ks * 16 + hi * 8), Vf[ks]);
-      }
+    for (int ks = 0; ks < D / 16; ++ks) {
+      mma(S, ld8(Qs + col * C::LDQ + ks * 16 + hi * 8), Kf[ks]);
+      mma(dP, ld8(dOs + col * C::LDQ + ks * 16 + hi * 8), Vf[ks]);
+    }
+    float lr16[16], dl16[16];
+    rows16(fl, lr16);
+    rows16(fl + C::QC, dl16);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = acc_row(i, lane);
-        float p = __builtin_amdgcn_exp2f(S[i] * g.scale_log2 - fl[r]);
-        if (need_mask && kpos > qpos0 + r) p = 0.f;
-        S[i] = p;
-        dP[i] = p * (dP[i] - fl[C::QC + r]);
-        Tacc[i] += p;
-      }
+    for (int i = 0; i < 16; ++i) {
+      float p = __builtin_amdgcn_exp2f(fmaf(S[i], g.scale_log2, -lr16[i]));
+      p = acc_row(i, lane) >= lim_base ? p : 0.f;
+      S[i] = p;
+      dP[i] = p * (dP[i] - dl16[i]) * g.scale;             // dS with the softmax scale of dK folded in
+      Tacc[i] += p;
+    }
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const frag_t<T> ap = acc_frag<T>(S, kk);
-        const frag_t<T> as = acc_frag<T>(dP, kk);
+    for (int kk = 0; kk < 2; ++kk) {
+      const frag_t<T> ap = acc_frag<T>(S, kk);
+      const frag_t<T> as = acc_frag<T>(dP, kk);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const T* dr = dOt + (dt * 32 + col) * C::LDT + kk * 16 + hi * 4;
-          mma(dV[dt], ap, ld4x2(dr, dr + 8));
-          const T* qr = Qt + (dt * 32 + col) * C::LDT + kk * 16 + hi * 4;
-          mma(dK[dt], as, ld4x2(qr, qr + 8));
-        }
+      for (int dt = 0; dt < D / 32; ++dt) {
+        mma(dV[dt], ap, lds_col_frag<T>(dOs, C::LDQ, kk * 16, dt * 32, lane));
+        mma(dK[dt], as, lds_col_frag<T>(Qs, C::LDQ, kk * 16, dt * 32, lane));
       }
     }
-    if (hl == G - 1) {
-      if (!skip) {
-        f32x16 Y = zero16();
+  };
+  auto proxy_part = [&](const unsigned char* base, int lim_base) {
+    const T* Ps = reinterpret_cast<const T*>(base) + 2 * C::QS;
+    const float* fl = reinterpret_cast<const float*>(base + C::FL_OFF);
+    f32x16 Y = zero16();
 #pragma unroll
-        for (int ks = 0; ks < DP / 16; ++ks) mma(Y, ld8(Ps + col * C::LDP + ks * 16 + hi * 8), KPf[ks]);
+    for (int ks = 0; ks < DP / 16; ++ks) mma(Y, ld8(Ps + col * C::LDP + ks * 16 + hi * 8), KPf[ks]);
+    float lp16[16];
+    rows16(fl + 2 * C::QC, lp16);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = acc_row(i, lane);
-          float qv = __builtin_amdgcn_exp2f(Y[i] * g.pscale_log2 - fl[2 * C::QC + r]);
-          if (need_mask && kpos > qpos0 + r) qv = 0.f;
-          Y[i] = g.lam * (qv - Tacc[i] * invG);
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const frag_t<T> ay = acc_frag<T>(Y, kk);
-#pragma unroll
-          for (int dt = 0; dt < DP / 32; ++dt) {
-            const T* pr = Pt + (dt * 32 + col) * C::LDT + kk * 16 + hi * 4;
-            mma(dKp[dt], ay, ld4x2(pr, pr + 8));
-          }
-        }
-      }
-      Tacc = zero16();
+    for (int i = 0; i < 16; ++i) {
+      float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], g.pscale_log2, -lp16[i]));
+      qv = acc_row(i, lane) >= lim_base ? qv : 0.f;
+      Y[i] = lam_ps * (qv - Tacc[i] * invG);                 // lam * s_p * dY
     }
-    if (s + 1 < nst) store_stage(buf ^ 1, s + 1);
-    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const frag_t<T> ay = acc_frag<T>(Y, kk);
+#pragma unroll
+      for (int dt = 0; dt < DP / 32; ++dt) mma(dKp[dt], ay, lds_col_frag<T>(Ps, C::LDP, kk * 16, dt * 32, lane));
+    }
+  };
+
+  // Outer loop over (list entry, query chunk); the G heads of a chunk are
+  // unrolled so the loop body is straight-line.  The stage after the last one
+  // re-reads the last chunk (always valid memory) into the unused buffer.
+  const int nchunk = len * nch;
+  if (nchunk > 0) {
+    load_stage(0, 0, 0, G == 1);
+    store_stage(0, G == 1);
+  }
+  __syncthreads();
+  int li = 0, c = 0;
+  for (int ci = 0; ci < nchunk; ++ci) {
+    const int I = lst[li] - qb0;
+    const int qpos0 = I * g.Bq + c * 32;
+    const int lim_base = (J == ((I * g.Bq) >> 7)) ? kpos - qpos0 : -1024;
+    int nli = li, nc = c + 1;
+    if (nc == nch) { nc = 0; ++nli; }
+    if (nli == len) { nli = li; nc = c; }
+#pragma unroll
+    for (int hl = 0; hl < G; ++hl) {
+      const int buf = (G % 2 == 0) ? (hl & 1) : ((ci * G + hl) & 1);
+      const unsigned char* base = smem_raw + buf * C::STAGE_BYTES;
+      if (hl + 1 < G) load_stage(li, c, hl + 1, hl + 1 == G - 1);
+      else load_stage(nli, nc, 0, G == 1);
+      main_part(base, lim_base);
+      if (hl == G - 1) proxy_part(base, lim_base);
+      store_stage(buf ^ 1, (hl + 1 < G) ? (hl + 1 == G - 1) : (G == 1));
+      __syncthreads();
+    }
+    Tacc = zero16();
+    li = nli;
+    c = nc;
   }
 
   // outputs: lane holds column d = dt*32 + col for 16 key rows
@@ -547,12 +537,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
       float* pv = dv + (t * g.Hkv + grp) * D;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        pk[dt * 32 + col] = dK[dt][i] * g.scale;
+        pk[dt * 32 + col] = dK[dt][i];
         pv[dt * 32 + col] = dV[dt][i];
       }
       float* pp = dkp + (t * g.Hkv + grp) * DP;
 #pragma unroll
-      for (int dt = 0; dt < DP / 32; ++dt) pp[dt * 32 + col] = dKp[dt][i] * g.pscale;
+      for (int dt = 0; dt < DP / 32; ++dt) pp[dt * 32 + col] = dKp[dt][i];
     }
   }
 }
@@ -578,9 +568,12 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
     hipError_t e = hipFuncSetAttribute((const void*)dq_kernel<T, D, DP>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, CQ::LDS_BYTES);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)dkdv_kernel<T, D, DP>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, CK::LDS_BYTES);
-    if (e != hipSuccess) return e;
+    const void* fns[] = {(const void*)dkdv_kernel<T, D, DP, 1>, (const void*)dkdv_kernel<T, D, DP, 2>,
+                         (const void*)dkdv_kernel<T, D, DP, 4>, (const void*)dkdv_kernel<T, D, DP, 8>};
+    for (const void* f : fns) {
+      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, CK::LDS_BYTES);
+      if (e != hipSuccess) return e;
+    }
     attr = true;
   }
   hipError_t e;
@@ -609,9 +602,18 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
   const int64_t nk = (int64_t)g.Hkv * g.nkb;
   if (nk > 0) {
     { ProfScope _ps("bwd_dkdv", s);
-    hipLaunchKernelGGL((dkdv_kernel<T, D, DP>), dim3((unsigned)nk), dim3(256), CK::LDS_BYTES, s,
-                       (const T*)q, (const T*)k, (const T*)v, (const T*)qp, (const T*)kp, lse, lse_p,
-                       (const T*)dout, w.delta, k2q_ptr, k2q_idx, dk, dv, dkp, g); }
+#define MSA_LAUNCH_DKDV(GG)                                                                          \
+    hipLaunchKernelGGL((dkdv_kernel<T, D, DP, GG>), dim3((unsigned)nk), dim3(256), CK::LDS_BYTES, s, \
+                       (const T*)q, (const T*)k, (const T*)v, (const T*)qp, (const T*)kp, lse, lse_p,  \
+                       (const T*)dout, w.delta, k2q_ptr, k2q_idx, dk, dv, dkp, g)
+    switch (g.G) {
+      case 1: MSA_LAUNCH_DKDV(1); break;
+      case 2: MSA_LAUNCH_DKDV(2); break;
+      case 4: MSA_LAUNCH_DKDV(4); break;
+      default: MSA_LAUNCH_DKDV(8); break;
+    }
+#undef MSA_LAUNCH_DKDV
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -640,11 +642,12 @@ namespace msa {
 int bwd_kernels(KernelEntry* out, int max) {
   const KernelEntry all[] = {
       {"bwd_dq<bf16,d128,dp64>", (const void*)dq_kernel<bf16, 128, 64>, 256, DqCfg<bf16, 128, 64>::LDS_BYTES},
-      {"bwd_dkdv<bf16,d128,dp64>", (const void*)dkdv_kernel<bf16, 128, 64>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
+      {"bwd_dkdv<bf16,d128,dp64,g4>", (const void*)dkdv_kernel<bf16, 128, 64, 4>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
+      {"bwd_dkdv<bf16,d128,dp64,g8>", (const void*)dkdv_kernel<bf16, 128, 64, 8>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
       {"bwd_dq<bf16,d64,dp32>", (const void*)dq_kernel<bf16, 64, 32>, 256, DqCfg<bf16, 64, 32>::LDS_BYTES},
-      {"bwd_dkdv<bf16,d64,dp32>", (const void*)dkdv_kernel<bf16, 64, 32>, 256, KvCfg<bf16, 64, 32>::LDS_BYTES},
+      {"bwd_dkdv<bf16,d64,dp32,g4>", (const void*)dkdv_kernel<bf16, 64, 32, 4>, 256, KvCfg<bf16, 64, 32>::LDS_BYTES},
       {"bwd_dq<f32,d64,dp32>", (const void*)dq_kernel<float, 64, 32>, 256, DqCfg<float, 64, 32>::LDS_BYTES},
-      {"bwd_dkdv<f32,d64,dp32>", (const void*)dkdv_kernel<float, 64, 32>, 256, KvCfg<float, 64, 32>::LDS_BYTES},
+      {"bwd_dkdv<f32,d64,dp32,g4>", (const void*)dkdv_kernel<float, 64, 32, 4>, 256, KvCfg<float, 64, 32>::LDS_BYTES},
   };
   int n = (int)(sizeof(all) / sizeof(all[0]));
   for (int i = 0; i < n && i < max; ++i) out[i] = all[i];

@@ -9,8 +9,9 @@
 // taken over the same set and only its log-sum-exp is kept.
 //
 // Work split: a workgroup (4 waves) serves one (KV group, query block) and
-// stages each selected KV block through LDS in two 64-key halves (K rows and
-// V transposed), double-buffered with a register prefetch of the next half.
+// stages each selected KV block through LDS in two 64-key halves (K and V
+// rows), double-buffered with a register prefetch of the next half; V^T
+// fragments come from the row-major V tile through LDS transpose reads.
 // A wave owns QT x 32 queries of one head and computes S^T = K Q^T on bf16
 // MFMA so that each lane holds one query column; the probabilities then feed
 // O^T += V^T P^T without leaving registers.  The proxy log-sum-exp over the
@@ -19,6 +20,8 @@
 #include "msa_device.h"
 #include "msa_internal.h"
 #include "msa_profile.h"
+
+#include <type_traits>
 
 namespace msa {
 
@@ -50,21 +53,19 @@ struct FwdCfg {
   static constexpr int KC = 64;                         // keys per stage
   static constexpr int EPC = 16 / (int)sizeof(T);        // elements per 16-byte chunk
   static constexpr int PAD = 8;
-  static constexpr int LDK = D + PAD;                    // K rows  [KC][LDK]
-  static constexpr int LDV = KC + PAD;                   // V^T     [D][LDV]
-  static constexpr int KS = KC * LDK, VT = D * LDV;
-  static constexpr int STAGE = KS + VT;
+  static constexpr int LDK = D + PAD;                    // K and V rows [KC][LDK]
+  static constexpr int KS = KC * LDK;
+  static constexpr int STAGE = 2 * KS;
   static constexpr int LDS_BYTES = 2 * STAGE * (int)sizeof(T);
   static constexpr int CPR = D / EPC;                    // chunks per row
-  static constexpr int NK = KC * CPR / 256, NV = NK;
+  static constexpr int NK = KC * CPR / 256;              // chunks per thread per tensor
 };
 
 template <typename T, int D, int DP, int QT>
 __global__ __launch_bounds__(256) void fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ qp, const T* __restrict__ kp, const int32_t* __restrict__ q2k_idx,
-    const int32_t* __restrict__ q2k_cnt, T* __restrict__ o, float* __restrict__ lse,
-    float* __restrict__ lse_p, Geo g) {
+    const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_cnt,
+    T* __restrict__ o, float* __restrict__ lse, Geo g) {
   typedef FwdCfg<T, D, DP, QT> C;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* smem = reinterpret_cast<T*>(smem_raw);
@@ -84,11 +85,12 @@ __global__ __launch_bounds__(256) void fwd_kernel(
   const int hl = u % g.G, chunk = u / g.G;
   const int h = grp * g.G + hl;
 
-  const int b = [&] {
+  int b;
+  {
     int lo = 0, hi_ = g.B;
     while (hi_ - lo > 1) { int mid = (lo + hi_) >> 1; if (g.qb0[mid] <= QB) lo = mid; else hi_ = mid; }
-    return lo;
-  }();
+    b = lo;
+  }
   const int I = QB - g.qb0[b];
   const int t0 = g.cu[b];
   const int L = g.cu[b + 1] - t0;
@@ -125,121 +127,124 @@ __global__ __launch_bounds__(256) void fwd_kernel(
   int nst = 2 * cnt;
   if (cnt > 0 && diag * 128 + 64 > I * g.Bq + g.Bq - 1) nst -= 1;
 
-  uint4 Kr[C::NK], Vr[C::NV];
+  uint4 Kr[C::NK], Vr[C::NK];
   auto load_stage = [&](int s) {
     const int J = sel[s >> 1] - kb0;
     const int key0 = J * 128 + (s & 1) * C::KC;
 #pragma unroll
     for (int i = 0; i < C::NK; ++i) {
       const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR, key = key0 + r;
-      Kr[i] = key < L ? *reinterpret_cast<const uint4*>(k + ((int64_t)(t0 + key) * g.Hkv + grp) * D + cc * C::EPC)
-                      : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < C::NV; ++i) {
-      const int c = tid + 256 * i, r = c % C::KC, cc = c / C::KC, key = key0 + r;
-      Vr[i] = key < L ? *reinterpret_cast<const uint4*>(v + ((int64_t)(t0 + key) * g.Hkv + grp) * D + cc * C::EPC)
-                      : make_uint4(0, 0, 0, 0);
+      const int64_t off = ((int64_t)(t0 + key) * g.Hkv + grp) * D + cc * C::EPC;
+      Kr[i] = key < L ? *reinterpret_cast<const uint4*>(k + off) : make_uint4(0, 0, 0, 0);
+      Vr[i] = key < L ? *reinterpret_cast<const uint4*>(v + off) : make_uint4(0, 0, 0, 0);
     }
   };
   auto store_stage = [&](int buf) {
     T* Ks = smem + buf * C::STAGE;
-    T* Vt = Ks + C::KS;
+    T* Vs = Ks + C::KS;
 #pragma unroll
     for (int i = 0; i < C::NK; ++i) {
       const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR;
       *reinterpret_cast<uint4*>(Ks + r * C::LDK + cc * C::EPC) = Kr[i];
+      *reinterpret_cast<uint4*>(Vs + r * C::LDK + cc * C::EPC) = Vr[i];
+    }
+  };
+
+  // One 32-key step: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  // lim: key row r of the tile is visible to query column qt iff r <= lim[qt]
+  // (a large value when nothing is masked).  The running maximum m used for
+  // the exponentials is only raised when a row's true maximum exceeds it by
+  // more than RESCALE_GAP (base 2): P then stays below 2^RESCALE_GAP, the
+  // result is the same after the final division by l, and the accumulator
+  // rescale (VALU work on O) is rare.
+  constexpr float RESCALE_GAP = 8.f;
+  auto step = [&](const T* Ks, const T* Vs, int kt, const int (&lim)[QT]) {
+    f32x16 S[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) S[qt] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const frag_t<T> a = ld8(Ks + (kt * 32 + col) * C::LDK + ks * 16 + hi * 8);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) mma(S[qt], a, Qf[qt][ks]);
+    }
+    bool grow = false;
+    float mnew[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = NEG_BIG;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float x = acc_row(i, lane) <= lim[qt] ? S[qt][i] : -INFINITY;
+        S[qt][i] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * g.scale_log2;
+      mnew[qt] = mx;
+      grow |= mx > m[qt] + RESCALE_GAP;
+    }
+    if (__ballot(grow)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float mn = fmaxf(m[qt], mnew[qt]);
+        const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
+        m[qt] = mn;
+        l[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) O[dt][qt][i] *= alpha;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < C::NV; ++i) {
-      const int c = tid + 256 * i, r = c % C::KC, cc = c / C::KC;
-      const T* e = reinterpret_cast<const T*>(&Vr[i]);
+    for (int qt = 0; qt < QT; ++qt) {
+      float ls = 0.f;
 #pragma unroll
-      for (int j = 0; j < C::EPC; ++j) Vt[(cc * C::EPC + j) * C::LDV + r] = e[j];
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(S[qt][i], g.scale_log2, -m[qt]));
+        S[qt][i] = p;
+        ls += p;
+      }
+      l[qt] += ls;
+    }
+    frag_t<T> Pf[2][QT];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) Pf[kk][qt] = acc_frag<T>(S[qt], kk);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const frag_t<T> a = lds_col_frag<T>(Vs, C::LDK, kt * 32 + kk * 16, dt * 32, lane);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) mma(O[dt][qt], a, Pf[kk][qt]);
+      }
     }
   };
 
   if (nst > 0) { load_stage(0); store_stage(0); }
   __syncthreads();
 
+  // The loop body is straight-line: the stage after the last re-reads the
+  // last stage (valid memory) into the unused buffer, and fully masked tiles
+  // of the diagonal block are computed with every key masked.
   for (int s = 0; s < nst; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nst) load_stage(s + 1);
+    load_stage(s + 1 < nst ? s + 1 : s);
     const int J = sel[s >> 1] - kb0;
     const int kpos0 = J * 128 + (s & 1) * C::KC;
-    if (active && kpos0 <= qbase + 32 * QT - 1) {
-      const T* Ks = smem + buf * C::STAGE;
-      const T* Vt = Ks + C::KS;
-      const bool need_mask = (J == diag);
+    const T* Ks = smem + buf * C::STAGE;
+    const T* Vs = Ks + C::KS;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int kpos = kpos0 + kt * 32;
-        if (kpos > qbase + 32 * QT - 1) break;           // rest of the stage is masked
-        // ---- S^T = K Q^T for 32 keys (rows) x queries (cols) ----
-        f32x16 S[QT];
+    for (int kt = 0; kt < 2; ++kt) {
+      int lim[QT];
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) S[qt] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const frag_t<T> a = ld8(Ks + (kt * 32 + col) * C::LDK + ks * 16 + hi * 8);
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) mma(S[qt], a, Qf[qt][ks]);
-        }
-        // ---- online softmax (base 2), one query column per lane ----
-        float alpha[QT];
-        bool rescale = false;
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          const int qpos = qbase + qt * 32 + col;
-          float mx = NEG_BIG;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float x = S[qt][i] * g.scale_log2;
-            if (need_mask && kpos + acc_row(i, lane) > qpos) x = -INFINITY;
-            S[qt][i] = x;
-            mx = fmaxf(mx, x);
-          }
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          const float mnew = fmaxf(m[qt], mx);
-          alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - mnew);
-          m[qt] = mnew;
-          float ls = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(S[qt][i] - mnew);
-            S[qt][i] = p;
-            ls += p;
-          }
-          l[qt] = l[qt] * alpha[qt] + ls;
-          rescale |= alpha[qt] != 1.f;
-        }
-        if (__ballot(rescale)) {
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) O[dt][qt][i] *= alpha[qt];
-        }
-        // ---- O^T += V^T P^T ----
-        frag_t<T> Pf[2][QT];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) Pf[kk][qt] = acc_frag<T>(S[qt], kk);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const T* vrow = Vt + (dt * 32 + col) * C::LDV + kt * 32 + hi * 4;
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const frag_t<T> a = ld4x2(vrow + kk * 16, vrow + kk * 16 + 8);
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt) mma(O[dt][qt], a, Pf[kk][qt]);
-          }
-        }
-      }
+      for (int qt = 0; qt < QT; ++qt)
+        lim[qt] = (J == diag) ? qbase + qt * 32 + col - (kpos0 + kt * 32) : 1024;
+      if (active) step(Ks, Vs, kt, lim);
     }
-    if (s + 1 < nst) store_stage(buf ^ 1);
+    store_stage(buf ^ 1);
     __syncthreads();
   }
 
@@ -260,9 +265,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(
           store4<T>(dst + d0, O[dt][qt][i4 * 4 + 0] * inv, O[dt][qt][i4 * 4 + 1] * inv,
                     O[dt][qt][i4 * 4 + 2] * inv, O[dt][qt][i4 * 4 + 3] * inv);
         }
-      if (hi == 0) {
-        lse[(int64_t)h * g.T + t] = (m[qt] + log2f(lt)) * LN2;
-      }
+      if (hi == 0) lse[(int64_t)h * g.T + t] = (m[qt] + log2f(lt)) * LN2;
     }
   }
 }
@@ -361,7 +364,7 @@ static hipError_t fwd_dispatch(const Geo& g, const void* q, const void* k, const
   if (nblk == 0) return hipSuccess;
   { ProfScope _ps("fwd", s);
   hipLaunchKernelGGL(fn, dim3((unsigned)nblk), dim3(256), C::LDS_BYTES, s, (const T*)q, (const T*)k,
-                     (const T*)v, (const T*)qp, (const T*)kp, q2k_idx, q2k_cnt, (T*)o, lse, lse_p, g); }
+                     (const T*)v, q2k_idx, q2k_cnt, (T*)o, lse, g); }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int per_wg = 4 / (g.Bq / 32);

@@ -54,8 +54,8 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
   if (c.heads_q % c.heads_kv != 0)
     return fail(MSA_ERR_INVALID_ARG, "heads_q (%d) must be a multiple of heads_kv (%d)", c.heads_q, c.heads_kv);
   const int G = c.heads_q / c.heads_kv;
-  if (G > 4 && G % 4 != 0)
-    return fail(MSA_ERR_UNSUPPORTED, "group size %d: groups above 4 must be a multiple of 4", G);
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(MSA_ERR_UNSUPPORTED, "group size %d not built (heads_q / heads_kv must be 1, 2, 4 or 8)", G);
   if (c.dtype != MSA_BF16 && c.dtype != MSA_F32) return fail(MSA_ERR_INVALID_ARG, "unknown dtype %d", c.dtype);
   const bool dims_ok = (c.head_dim == 128 && c.proxy_dim == 64 && c.dtype == MSA_BF16) ||
                        (c.head_dim == 64 && c.proxy_dim == 32);

@@ -16,7 +16,7 @@
 // accumulator tile is row  s*16 + ((j >> 2) << 3) + ((l >> 5) << 2) + (j & 3),
 // so the accumulator's elements [8s, 8s+8) are directly a fragment whose
 // slots are the accumulator's rows.  The operand paired with it is read from a
-// transposed tile as two runs of 4 contiguous elements.
+// row-major LDS tile with lds_col_frag() (LDS transpose reads for bf16).
 //
 // bf16 tiles use v_mfma_f32_32x32x16_bf16.  fp32 tiles use eight
 // v_mfma_f32_32x32x2f32 steps per k-slice (step j contracts slot pair j).
@@ -99,6 +99,45 @@ __device__ __forceinline__ frag_t<T> acc_frag(const f32x16& acc, int s) {
   frag_t<T> r;
 #pragma unroll
   for (int j = 0; j < 8; ++j) r[j] = from_f32<T>(acc[s * 8 + j]);
+  return r;
+}
+
+// One gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of
+// 16 lanes, every lane supplies the address of 4 consecutive 16-bit values;
+// lane i of the group receives element (i % 4) of the values supplied by
+// lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12, in that order.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_tr4(const bf16* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<bf16*>(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// Operand fragment in accumulator slots read from a row-major LDS tile X
+// (ld elements per row) whose rows are the contraction index: lane l gets
+// column n0 + (l & 31) and rows k0 + ((j >> 2) << 3) + ((l >> 5) << 2) + (j & 3)
+// for element j.  It pairs with acc_frag() of an accumulator tile whose rows
+// are the same contraction index.  bf16: two transpose reads, where source
+// lane s of group g reads row k0 + 4 (l >> 5) + (s >> 2) (and that + 8),
+// columns n0 + 16 (g & 1) + 4 (s & 3) .. + 3.  fp32: eight scalar reads.
+template <typename T>
+__device__ __forceinline__ frag_t<T> lds_col_frag(const T* X, int ld, int k0, int n0, int lane);
+template <>
+__device__ __forceinline__ bf16x8 lds_col_frag<bf16>(const bf16* X, int ld, int k0, int n0, int lane) {
+  const int s = lane & 15, g = lane >> 4, hi = lane >> 5;
+  const bf16* p = X + (k0 + hi * 4 + (s >> 2)) * ld + n0 + 16 * (g & 1) + 4 * (s & 3);
+  const bf16x4 a = lds_tr4(p), b = lds_tr4(p + 8 * ld);
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { r[j] = a[j]; r[j + 4] = b[j]; }
+  return r;
+}
+template <>
+__device__ __forceinline__ f32x8 lds_col_frag<float>(const float* X, int ld, int k0, int n0, int lane) {
+  const int c = n0 + (lane & 31), hi = lane >> 5;
+  f32x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = X[(k0 + ((j >> 2) << 3) + hi * 4 + (j & 3)) * ld + c];
   return r;
 }
 
