@@ -63,12 +63,13 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, con
 // ---------------------------------------------------------------------------
 template <typename T, int D, int DP>
 struct DqCfg {
-  static constexpr int KC = 64, PAD = 8, EPC = 16 / (int)sizeof(T);
-  static constexpr int LDK = D + PAD, LDP = DP + PAD;
-  static constexpr int KS = KC * LDK, KPS = KC * LDP;
+  static constexpr int KC = 64;
+  typedef Tile<T, D> TK;                          // K and V rows
+  typedef Tile<T, DP> TP;                         // kp rows
+  static constexpr int KS = KC * D, KPS = KC * DP;
   static constexpr int STAGE = 2 * KS + KPS;
   static constexpr int LDS_BYTES = 2 * STAGE * (int)sizeof(T);
-  static constexpr int CPR = D / EPC, CPRP = DP / EPC;
+  static constexpr int EPC = TK::EPC, CPR = TK::CPR, CPRP = TP::CPR;
   static constexpr int NK = KC * CPR / 256, NP = KC * CPRP / 256;
   static_assert(NK >= 1 && NP >= 1, "tile split");
   static_assert(4 * DP * 32 * 4 <= LDS_BYTES, "reduction scratch");
@@ -82,6 +83,8 @@ __global__ __launch_bounds__(256) void dq_kernel(
     const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_cnt,
     float* __restrict__ dq, float* __restrict__ dqp, float* __restrict__ cpart, Geo g) {
   typedef DqCfg<T, D, DP> C;
+  typedef typename C::TK TK;
+  typedef typename C::TP TP;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* smem = reinterpret_cast<T*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -133,11 +136,13 @@ __global__ __launch_bounds__(256) void dq_kernel(
 #pragma unroll
   for (int dt = 0; dt < DP / 32; ++dt) Cp[dt] = zero16();
 
+  // stages: 64-key halves of the selected blocks; the diagonal block is last
   int nst = 2 * cnt;
-  if (cnt > 0 && diag * 128 + 64 > I * g.Bq + g.Bq - 1) nst -= 1;
+  if (diag * 128 + 64 > I * g.Bq + g.Bq - 1) nst -= 1;
+  const int nst_plain = 2 * (cnt - 1);
 
   uint4 Kr[C::NK], Vr[C::NK], Pr[C::NP];
-  auto load_stage = [&](int s) {
+  auto load_stage = [&](int s) __attribute__((always_inline)) {
     const int J = sel[s >> 1] - kb0;
     const int key0 = J * 128 + (s & 1) * C::KC;
 #pragma unroll
@@ -154,37 +159,35 @@ __global__ __launch_bounds__(256) void dq_kernel(
                       : make_uint4(0, 0, 0, 0);
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int buf) __attribute__((always_inline)) {
     T* Ks = smem + buf * C::STAGE;
     T* Vs = Ks + C::KS;
     T* KPs = Vs + C::KS;
 #pragma unroll
     for (int i = 0; i < C::NK; ++i) {
       const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR;
-      *reinterpret_cast<uint4*>(Ks + r * C::LDK + cc * C::EPC) = Kr[i];
-      *reinterpret_cast<uint4*>(Vs + r * C::LDK + cc * C::EPC) = Vr[i];
+      *reinterpret_cast<uint4*>(Ks + TK::off(r, cc * C::EPC)) = Kr[i];
+      *reinterpret_cast<uint4*>(Vs + TK::off(r, cc * C::EPC)) = Vr[i];
     }
 #pragma unroll
     for (int i = 0; i < C::NP; ++i) {
       const int c = tid + 256 * i, r = c / C::CPRP, cc = c % C::CPRP;
-      *reinterpret_cast<uint4*>(KPs + r * C::LDP + cc * C::EPC) = Pr[i];
+      *reinterpret_cast<uint4*>(KPs + TP::off(r, cc * C::EPC)) = Pr[i];
     }
   };
 
-  // one 32-key tile of a stage
-  auto tile = [&](const T* Ks, const T* Vs, const T* KPs, int kt, int kpos, bool assigned, auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
+  // one 32-key tile of a stage; lim: key row r visible iff r <= lim
+  auto tile = [&](const T* Ks, const T* Vs, const T* KPs, int kt, int lim, bool assigned) __attribute__((always_inline)) {
     f32x16 S = zero16(), dP = zero16();
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      mma(S, ld8(Ks + (kt * 32 + col) * C::LDK + ks * 16 + hi * 8), Qf[ks]);
-      mma(dP, ld8(Vs + (kt * 32 + col) * C::LDK + ks * 16 + hi * 8), dOf[ks]);
+      mma(S, TK::row8(Ks, kt * 32 + col, ks * 16 + hi * 8), Qf[ks]);
+      mma(dP, TK::row8(Vs, kt * 32 + col, ks * 16 + hi * 8), dOf[ks]);
     }
-    const int lim = qpos - kpos;                         // key row r is visible iff r <= lim
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float p = __builtin_amdgcn_exp2f(fmaf(S[i], g.scale_log2, -lse2));
-      if (MASK && acc_row(i, lane) > lim) p = 0.f;
+      p = acc_row(i, lane) <= lim ? p : 0.f;
       S[i] = p;
       dP[i] = p * (dP[i] - dl);
     }
@@ -192,19 +195,17 @@ __global__ __launch_bounds__(256) void dq_kernel(
     for (int kk = 0; kk < 2; ++kk) {
       const frag_t<T> bs = acc_frag<T>(dP, kk);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        mma(dQ[dt], lds_col_frag<T>(Ks, C::LDK, kt * 32 + kk * 16, dt * 32, lane), bs);
+      for (int dt = 0; dt < D / 32; ++dt) mma(dQ[dt], TK::col(Ks, kt * 32 + kk * 16, dt * 32, lane), bs);
     }
     // proxy: E = [assigned] Q - P / G ;  C^T += kp^T E^T
     if (assigned) {
       f32x16 Y = zero16();
 #pragma unroll
-      for (int ks = 0; ks < DP / 16; ++ks)
-        mma(Y, ld8(KPs + (kt * 32 + col) * C::LDP + ks * 16 + hi * 8), QPf[ks]);
+      for (int ks = 0; ks < DP / 16; ++ks) mma(Y, TP::row8(KPs, kt * 32 + col, ks * 16 + hi * 8), QPf[ks]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], g.pscale_log2, -lsep2));
-        if (MASK && acc_row(i, lane) > lim) qv = 0.f;
+        qv = acc_row(i, lane) <= lim ? qv : 0.f;
         S[i] = qv - S[i] * invG;
       }
     } else {
@@ -215,37 +216,33 @@ __global__ __launch_bounds__(256) void dq_kernel(
     for (int kk = 0; kk < 2; ++kk) {
       const frag_t<T> be = acc_frag<T>(S, kk);
 #pragma unroll
-      for (int dt = 0; dt < DP / 32; ++dt)
-        mma(Cp[dt], lds_col_frag<T>(KPs, C::LDP, kt * 32 + kk * 16, dt * 32, lane), be);
+      for (int dt = 0; dt < DP / 32; ++dt) mma(Cp[dt], TP::col(KPs, kt * 32 + kk * 16, dt * 32, lane), be);
     }
   };
-
-  if (nst > 0) { load_stage(0); store_stage(0); }
-  __syncthreads();
-
-  for (int s = 0; s < nst; ++s) {
+  auto stage_body = [&](int s, bool masked) __attribute__((always_inline)) {
     const int buf = s & 1;
-    if (s + 1 < nst) load_stage(s + 1);
-    const int J = sel[s >> 1] - kb0;
-    const int kpos0 = J * 128 + (s & 1) * C::KC;
-    if (active && kpos0 <= qbase + 31) {
-      const T* Ks = smem + buf * C::STAGE;
-      const T* Vs = Ks + C::KS;
-      const T* KPs = Vs + C::KS;
+    load_stage(s + 1 < nst ? s + 1 : s);
+    const T* Ks = smem + buf * C::STAGE;
+    const T* Vs = Ks + C::KS;
+    const T* KPs = Vs + C::KS;
+    const int kpos0 = (sel[s >> 1] - kb0) * 128 + (s & 1) * C::KC;
+    if (active) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const int kpos = kpos0 + kt * 32;
-        const bool assigned = ((s * 2 + kt) % g.G) == hl;
-        if (kpos > qbase + 31) break;                     // every key of the tile follows every query
-        if (J == diag && kpos + 31 > qbase)
-          tile(Ks, Vs, KPs, kt, kpos, assigned, std::true_type());
-        else
-          tile(Ks, Vs, KPs, kt, kpos, assigned, std::false_type());
+        const int lim = masked ? qpos - (kpos0 + kt * 32) : 1024;
+        tile(Ks, Vs, KPs, kt, lim, ((s * 2 + kt) % g.G) == hl);
       }
     }
-    if (s + 1 < nst) store_stage(buf ^ 1);
+    store_stage(buf ^ 1);
     __syncthreads();
-  }
+  };
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  int s = 0;
+  for (; s < nst_plain; ++s) stage_body(s, false);
+  for (; s < nst; ++s) stage_body(s, true);
 
   // dQ out (fp32)
   if (active && qpos < L) {
@@ -319,17 +316,26 @@ __global__ void dqp_reduce_kernel(const float* __restrict__ cpart, float* __rest
 // ---------------------------------------------------------------------------
 template <typename T, int D, int DP>
 struct KvCfg {
-  static constexpr int QC = 32, PAD = 8, EPC = 16 / (int)sizeof(T);
-  static constexpr int LDQ = D + PAD, LDP = DP + PAD;
-  static constexpr int QS = QC * LDQ, PS = QC * LDP;
+  static constexpr int QC = 32;                   // queries per stage
+  static constexpr int NBUF = 4;                  // LDS ring of stages
+  static constexpr int AHEAD = NBUF - 1;          // stages in flight ahead of the one computed
+  typedef Tile<T, D> TQ;                          // Q and dO rows
+  typedef Tile<T, DP> TP;                         // qp rows
+  static constexpr int QS = QC * D, PS = QC * DP;
   static constexpr int STAGE_T = 2 * QS + PS;                        // elements of T
   static constexpr int FL_OFF = ((STAGE_T * (int)sizeof(T) + 15) / 16) * 16;
-  static constexpr int STAGE_BYTES = FL_OFF + 3 * QC * 4;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-  static constexpr int CPR = D / EPC, CPRP = DP / EPC;
-  static constexpr int NQ = QC * CPR / 256, NP = (QC * CPRP + 255) / 256;
-  static constexpr int NPE = QC * CPRP;                             // proxy chunks per stage
-  static_assert(NQ >= 1 && NP >= 1, "tile split");
+  static constexpr int STAGE_BYTES = FL_OFF + 4 * QC * 4;            // lse, D, lse_p, spare
+  static constexpr int LDS_BYTES = NBUF * STAGE_BYTES;
+  static constexpr int EPC = TQ::EPC;
+  // copies per wave per stage: Q and dO rows, one vector of floats, and the
+  // qp rows at the last head of a chunk
+  static constexpr int QROWS_PER_COPY = 64 / TQ::CPR;                // rows one wave copy covers
+  static constexpr int NQCOPY = QC / (4 * QROWS_PER_COPY);           // per tensor per wave
+  static constexpr int PROWS_PER_COPY = 64 / TP::CPR;
+  static constexpr int NPCOPY = (QC + 4 * PROWS_PER_COPY - 1) / (4 * PROWS_PER_COPY);
+  static_assert(QC % PROWS_PER_COPY == 0, "copy split");
+  static constexpr int COPIES = 2 * NQCOPY + 1;
+  static_assert(NQCOPY >= 1 && QC % (4 * QROWS_PER_COPY) == 0, "copy split");
 };
 
 template <typename T, int D, int DP, int G>
@@ -340,6 +346,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
     const int32_t* __restrict__ k2q_ptr, const int32_t* __restrict__ k2q_idx,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dkp, Geo g) {
   typedef KvCfg<T, D, DP> C;
+  typedef typename C::TQ TQ;
+  typedef typename C::TP TP;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hi = lane >> 5;
@@ -377,61 +385,53 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
 #pragma unroll
   for (int dt = 0; dt < DP / 32; ++dt) dKp[dt] = zero16();
 
-  uint4 Qr[C::NQ], Dr[C::NQ], Pr[C::NP];
-  float lr = 0.f, dlr = 0.f, lpr = 0.f;
-  // Stage = (list entry li, query chunk c, head hl); with_qp for the chunk's last head.
-  auto load_stage = [&](int li, int c, int hl, bool with_qp) {
+  // Copy the stage (list entry li, query chunk c, head hl) into ring slot buf.
+  // Rows past the document end are clamped to its last row (valid memory);
+  // such rows are masked in the compute.  Every wave issues the same number of
+  // copies per stage (COPIES, + NPCOPY at a chunk's last head), which the
+  // vmcnt waits below rely on.
+  auto issue_stage = [&](int buf, int li, int c, int hl, bool with_qp) __attribute__((always_inline)) {
+    unsigned char* base = smem_raw + buf * C::STAGE_BYTES;
     const int I = lst[li] - qb0;
     const int h = grp * G + hl;
     const int row0 = I * g.Bq + c * 32;
 #pragma unroll
-    for (int i = 0; i < C::NQ; ++i) {
-      const int e = tid + 256 * i, r = e / C::CPR, cc = e % C::CPR, pos = row0 + r;
-      const int64_t off = ((int64_t)(t0 + pos) * g.Hq + h) * D + cc * C::EPC;
-      Qr[i] = pos < L ? *reinterpret_cast<const uint4*>(q + off) : make_uint4(0, 0, 0, 0);
-      Dr[i] = pos < L ? *reinterpret_cast<const uint4*>(dout + off) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < C::NQCOPY; ++j) {
+      const int rfirst = (wave * C::NQCOPY + j) * C::QROWS_PER_COPY;
+      const int r = rfirst + lane / TQ::CPR;
+      const int p = lane % TQ::CPR;
+      const int pos = row0 + r < L ? row0 + r : L - 1;
+      const int64_t off = ((int64_t)(t0 + pos) * g.Hq + h) * D + swz<TQ::CPR>(r, p) * C::EPC;
+      dma16(q + off, base + rfirst * D * (int)sizeof(T));
+      dma16(dout + off, base + (C::QS + rfirst * D) * (int)sizeof(T));
     }
     if (with_qp) {
 #pragma unroll
-      for (int i = 0; i < C::NP; ++i) {
-        const int e = tid + 256 * i, r = e / C::CPRP, cc = e % C::CPRP, pos = row0 + r;
-        if (e < C::NPE)
-          Pr[i] = pos < L ? *reinterpret_cast<const uint4*>(qp + ((int64_t)(t0 + pos) * g.Hkv + grp) * DP + cc * C::EPC)
-                          : make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < C::NPCOPY; ++j) {
+        // with fewer rows than copies, the extra waves repeat the first rows
+        const int rfirst = ((wave * C::NPCOPY + j) % (C::QC / C::PROWS_PER_COPY)) * C::PROWS_PER_COPY;
+        const int r = rfirst + lane / TP::CPR;
+        const int p = lane % TP::CPR;
+        const int rr = r;
+        const int pos = row0 + rr < L ? row0 + rr : L - 1;
+        const int64_t off = ((int64_t)(t0 + pos) * g.Hkv + grp) * DP + swz<TP::CPR>(rr, p) * C::EPC;
+        dma16(qp + off, base + (2 * C::QS + rfirst * DP) * (int)sizeof(T));
       }
     }
-    if (tid < C::QC) {
-      const int pos = row0 + tid;
-      const bool ok = pos < L;
-      const int64_t t = t0 + (ok ? pos : 0);
-      lr = ok ? lse[(int64_t)h * g.T + t] * LOG2E : INFINITY;   // rows past the end get P = 0
-      dlr = ok ? delta[(int64_t)h * g.T + t] : 0.f;
-      lpr = (ok && with_qp) ? lse_p[(int64_t)grp * g.T + t] * LOG2E : INFINITY;
+    // one float vector per wave (lse, D, lse_p, and lse_p again into the
+    // spare slot): 32 lanes x 4 bytes, the other lanes inactive so nothing
+    // lands outside the wave's 128-byte slot
+    if (lane < C::QC) {
+      const int pos = row0 + lane < L ? row0 + lane : L - 1;
+      const int64_t t = t0 + pos;
+      const float* src = wave == 0 ? lse + (int64_t)h * g.T + t
+                       : wave == 1 ? delta + (int64_t)h * g.T + t
+                       : lse_p + (int64_t)grp * g.T + t;
+      dma4(src, base + C::FL_OFF + wave * C::QC * 4);
     }
-  };
-  auto store_stage = [&](int buf, bool with_qp) {
-    unsigned char* base = smem_raw + buf * C::STAGE_BYTES;
-    T* Qs = reinterpret_cast<T*>(base);
-    T* dOs = Qs + C::QS;
-    T* Ps = dOs + C::QS;
-    float* fl = reinterpret_cast<float*>(base + C::FL_OFF);
-#pragma unroll
-    for (int i = 0; i < C::NQ; ++i) {
-      const int e = tid + 256 * i, r = e / C::CPR, cc = e % C::CPR;
-      *reinterpret_cast<uint4*>(Qs + r * C::LDQ + cc * C::EPC) = Qr[i];
-      *reinterpret_cast<uint4*>(dOs + r * C::LDQ + cc * C::EPC) = Dr[i];
-    }
-    if (with_qp) {
-#pragma unroll
-      for (int i = 0; i < C::NP; ++i) {
-        const int e = tid + 256 * i, r = e / C::CPRP, cc = e % C::CPRP;
-        if (e < C::NPE) *reinterpret_cast<uint4*>(Ps + r * C::LDP + cc * C::EPC) = Pr[i];
-      }
-    }
-    if (tid < C::QC) { fl[tid] = lr; fl[C::QC + tid] = dlr; fl[2 * C::QC + tid] = lpr; }
   };
   // per-lane values of the 16 query rows held by accumulator elements
-  auto rows16 = [&](const float* f, float (&out)[16]) {
+  auto rows16 = [&](const float* f, float (&out)[16]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(f + acc_row(i4 * 4, lane));
@@ -439,24 +439,25 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
       for (int j = 0; j < 4; ++j) out[i4 * 4 + j] = x[j];
     }
   };
-  // rows below lim_base are queries that precede this lane's key (masked)
-  auto main_part = [&](const unsigned char* base, int lim_base) {
+  // masked: query row r counts iff lo <= r < hi_ (causal lower bound from
+  // this lane's key, upper bound from the document end)
+  auto main_part = [&](const unsigned char* base, int lo, int hi_, bool masked) __attribute__((always_inline)) {
     const T* Qs = reinterpret_cast<const T*>(base);
     const T* dOs = Qs + C::QS;
     const float* fl = reinterpret_cast<const float*>(base + C::FL_OFF);
     f32x16 S = zero16(), dP = zero16();
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      mma(S, ld8(Qs + col * C::LDQ + ks * 16 + hi * 8), Kf[ks]);
-      mma(dP, ld8(dOs + col * C::LDQ + ks * 16 + hi * 8), Vf[ks]);
+      mma(S, TQ::row8(Qs, col, ks * 16 + hi * 8), Kf[ks]);
+      mma(dP, TQ::row8(dOs, col, ks * 16 + hi * 8), Vf[ks]);
     }
     float lr16[16], dl16[16];
     rows16(fl, lr16);
     rows16(fl + C::QC, dl16);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float p = __builtin_amdgcn_exp2f(fmaf(S[i], g.scale_log2, -lr16[i]));
-      p = acc_row(i, lane) >= lim_base ? p : 0.f;
+      float p = __builtin_amdgcn_exp2f(fmaf(S[i], g.scale_log2, -lr16[i] * LOG2E));
+      if (masked) p = (acc_row(i, lane) >= lo && acc_row(i, lane) < hi_) ? p : 0.f;
       S[i] = p;
       dP[i] = p * (dP[i] - dl16[i]) * g.scale;             // dS with the softmax scale of dK folded in
       Tacc[i] += p;
@@ -467,65 +468,92 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
       const frag_t<T> as = acc_frag<T>(dP, kk);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        mma(dV[dt], ap, lds_col_frag<T>(dOs, C::LDQ, kk * 16, dt * 32, lane));
-        mma(dK[dt], as, lds_col_frag<T>(Qs, C::LDQ, kk * 16, dt * 32, lane));
+        mma(dV[dt], ap, TQ::col(dOs, kk * 16, dt * 32, lane));
+        mma(dK[dt], as, TQ::col(Qs, kk * 16, dt * 32, lane));
       }
     }
   };
-  auto proxy_part = [&](const unsigned char* base, int lim_base) {
+  auto proxy_part = [&](const unsigned char* base, int lo, int hi_, bool masked) __attribute__((always_inline)) {
     const T* Ps = reinterpret_cast<const T*>(base) + 2 * C::QS;
     const float* fl = reinterpret_cast<const float*>(base + C::FL_OFF);
     f32x16 Y = zero16();
 #pragma unroll
-    for (int ks = 0; ks < DP / 16; ++ks) mma(Y, ld8(Ps + col * C::LDP + ks * 16 + hi * 8), KPf[ks]);
+    for (int ks = 0; ks < DP / 16; ++ks) mma(Y, TP::row8(Ps, col, ks * 16 + hi * 8), KPf[ks]);
     float lp16[16];
     rows16(fl + 2 * C::QC, lp16);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], g.pscale_log2, -lp16[i]));
-      qv = acc_row(i, lane) >= lim_base ? qv : 0.f;
+      float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], g.pscale_log2, -lp16[i] * LOG2E));
+      if (masked) qv = (acc_row(i, lane) >= lo && acc_row(i, lane) < hi_) ? qv : 0.f;
       Y[i] = lam_ps * (qv - Tacc[i] * invG);                 // lam * s_p * dY
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const frag_t<T> ay = acc_frag<T>(Y, kk);
 #pragma unroll
-      for (int dt = 0; dt < DP / 32; ++dt) mma(dKp[dt], ay, lds_col_frag<T>(Ps, C::LDP, kk * 16, dt * 32, lane));
+      for (int dt = 0; dt < DP / 32; ++dt) mma(dKp[dt], ay, TP::col(Ps, kk * 16, dt * 32, lane));
     }
   };
 
-  // Outer loop over (list entry, query chunk); the G heads of a chunk are
-  // unrolled so the loop body is straight-line.  The stage after the last one
-  // re-reads the last chunk (always valid memory) into the unused buffer.
+  // Stages run in list order over chunks (list entry, 32-query chunk) with the
+  // G heads of a chunk unrolled; the ring holds AHEAD stages in flight.
+  // Masked chunks: the leading entries whose diagonal is this KV block (the
+  // list is ascending) and chunks that reach past the document end (only the
+  // last entry can).  The stage index after the last re-reads the last chunk.
   const int nchunk = len * nch;
-  if (nchunk > 0) {
-    load_stage(0, 0, 0, G == 1);
-    store_stage(0, G == 1);
+  int nmask = 0;
+  while (nmask < len && nmask < 2 && (((lst[nmask] - qb0) * g.Bq) >> 7) == J) ++nmask;
+  const int nchunk_lead = nmask * nch;
+  const bool tail = len > 0 && (lst[len - 1] - qb0 + 1) * g.Bq > L;
+  const int nchunk_plain_end = tail ? (len - 1) * nch : nchunk;
+
+  // stage s = ci * G + hl  ->  (li, c, hl); counters advance incrementally
+  int fli = 0, fc = 0, fhl = 0;           // next stage to issue
+  int fs = 0;                             // its index
+  const int nst = nchunk * G;
+  auto issue_next = [&]() __attribute__((always_inline)) {
+    const bool wqp = fhl == G - 1;
+    int li = fli, c = fc, hl = fhl;
+    if (fs >= nst) {                       // past the end: re-read the last stage
+      li = len - 1; c = nch - 1; hl = G - 1;
+    }
+    issue_stage(fs % C::NBUF, li, c, hl, wqp);
+    ++fs;
+    if (++fhl == G) { fhl = 0; if (++fc == nch) { fc = 0; ++fli; } }
+  };
+  if (nst > 0) {
+#pragma unroll
+    for (int j = 0; j < C::AHEAD; ++j) issue_next();
   }
-  __syncthreads();
   int li = 0, c = 0;
-  for (int ci = 0; ci < nchunk; ++ci) {
+  auto chunk_body = [&](int ci, bool masked) __attribute__((always_inline)) {
     const int I = lst[li] - qb0;
     const int qpos0 = I * g.Bq + c * 32;
-    const int lim_base = (J == ((I * g.Bq) >> 7)) ? kpos - qpos0 : -1024;
-    int nli = li, nc = c + 1;
-    if (nc == nch) { nc = 0; ++nli; }
-    if (nli == len) { nli = li; nc = c; }
-#pragma unroll
-    for (int hl = 0; hl < G; ++hl) {
-      const int buf = (G % 2 == 0) ? (hl & 1) : ((ci * G + hl) & 1);
-      const unsigned char* base = smem_raw + buf * C::STAGE_BYTES;
-      if (hl + 1 < G) load_stage(li, c, hl + 1, hl + 1 == G - 1);
-      else load_stage(nli, nc, 0, G == 1);
-      main_part(base, lim_base);
-      if (hl == G - 1) proxy_part(base, lim_base);
-      store_stage(buf ^ 1, (hl + 1 < G) ? (hl + 1 == G - 1) : (G == 1));
+    const int lo = kpos - qpos0, hi_ = L - qpos0;
+    static_for<G>([&](auto hlc) __attribute__((always_inline)) {
+      constexpr int hl = decltype(hlc)::value;
+      // stage ci*G + hl must have landed: the AHEAD - 1 later stages in
+      // flight issued COPIES (+ NPCOPY at their chunk's last head) each
+      constexpr int later = []() {
+        int n = 0;
+        for (int j = 1; j < C::AHEAD; ++j) n += C::COPIES + (((hl + j) % G == G - 1) ? C::NPCOPY : 0);
+        return n;
+      }();
+      wait_vmcnt<later>();
       __syncthreads();
-    }
+      issue_next();
+      const int s = ci * G + hl;
+      const unsigned char* base = smem_raw + (s % C::NBUF) * C::STAGE_BYTES;
+      main_part(base, lo, hi_, masked);
+      if constexpr (hl == G - 1) proxy_part(base, lo, hi_, masked);
+    });
     Tacc = zero16();
-    li = nli;
-    c = nc;
-  }
+    if (++c == nch) { c = 0; ++li; }
+  };
+  int ci = 0;
+  for (; ci < nchunk_lead && ci < nchunk; ++ci) chunk_body(ci, true);
+  for (; ci < nchunk_plain_end; ++ci) chunk_body(ci, false);
+  for (; ci < nchunk; ++ci) chunk_body(ci, true);
 
   // outputs: lane holds column d = dt*32 + col for 16 key rows
 #pragma unroll

@@ -50,14 +50,12 @@ __device__ __forceinline__ void store4<float>(float* dst, float a, float b, floa
 
 template <typename T, int D, int DP, int QT>
 struct FwdCfg {
-  static constexpr int KC = 64;                         // keys per stage
-  static constexpr int EPC = 16 / (int)sizeof(T);        // elements per 16-byte chunk
-  static constexpr int PAD = 8;
-  static constexpr int LDK = D + PAD;                    // K and V rows [KC][LDK]
-  static constexpr int KS = KC * LDK;
+  static constexpr int KC = 64;                          // keys per stage
+  typedef Tile<T, D> TK;                                 // K and V rows, swizzled
+  static constexpr int KS = KC * D;
   static constexpr int STAGE = 2 * KS;
   static constexpr int LDS_BYTES = 2 * STAGE * (int)sizeof(T);
-  static constexpr int CPR = D / EPC;                    // chunks per row
+  static constexpr int EPC = TK::EPC, CPR = TK::CPR;
   static constexpr int NK = KC * CPR / 256;              // chunks per thread per tensor
 };
 
@@ -67,6 +65,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(
     const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_cnt,
     T* __restrict__ o, float* __restrict__ lse, Geo g) {
   typedef FwdCfg<T, D, DP, QT> C;
+  typedef typename C::TK TK;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* smem = reinterpret_cast<T*>(smem_raw);
   static_assert(C::NK >= 1, "tile split");
@@ -113,22 +112,15 @@ __global__ __launch_bounds__(256) void fwd_kernel(
     }
   }
 
-  f32x16 O[D / 32][QT];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) O[dt][qt] = zero16();
-  float m[QT], l[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) { m[qt] = NEG_BIG; l[qt] = 0.f; }
-
-  // stages: two 64-key halves per selected block; the second half of the
-  // diagonal block is dropped when every query of the block precedes it.
+  // Stages are 64-key halves of the selected blocks, ascending; the diagonal
+  // block (always the last) needs the causal mask, the others never do.  Its
+  // second half is dropped when every query of the block precedes it.
   int nst = 2 * cnt;
-  if (cnt > 0 && diag * 128 + 64 > I * g.Bq + g.Bq - 1) nst -= 1;
+  if (diag * 128 + 64 > I * g.Bq + g.Bq - 1) nst -= 1;
+  const int nst_plain = 2 * (cnt - 1);
 
   uint4 Kr[C::NK], Vr[C::NK];
-  auto load_stage = [&](int s) {
+  auto load_stage = [&](int s) __attribute__((always_inline)) {
     const int J = sel[s >> 1] - kb0;
     const int key0 = J * 128 + (s & 1) * C::KC;
 #pragma unroll
@@ -139,69 +131,52 @@ __global__ __launch_bounds__(256) void fwd_kernel(
       Vr[i] = key < L ? *reinterpret_cast<const uint4*>(v + off) : make_uint4(0, 0, 0, 0);
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int buf) __attribute__((always_inline)) {
     T* Ks = smem + buf * C::STAGE;
     T* Vs = Ks + C::KS;
 #pragma unroll
     for (int i = 0; i < C::NK; ++i) {
       const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR;
-      *reinterpret_cast<uint4*>(Ks + r * C::LDK + cc * C::EPC) = Kr[i];
-      *reinterpret_cast<uint4*>(Vs + r * C::LDK + cc * C::EPC) = Vr[i];
+      *reinterpret_cast<uint4*>(Ks + TK::off(r, cc * C::EPC)) = Kr[i];
+      *reinterpret_cast<uint4*>(Vs + TK::off(r, cc * C::EPC)) = Vr[i];
     }
   };
 
-  // One 32-key step: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  // lim: key row r of the tile is visible to query column qt iff r <= lim[qt]
-  // (a large value when nothing is masked).  The running maximum m used for
-  // the exponentials is only raised when a row's true maximum exceeds it by
-  // more than RESCALE_GAP (base 2): P then stays below 2^RESCALE_GAP, the
-  // result is the same after the final division by l, and the accumulator
-  // rescale (VALU work on O) is rare.
-  constexpr float RESCALE_GAP = 8.f;
-  auto step = [&](const T* Ks, const T* Vs, int kt, const int (&lim)[QT]) {
-    f32x16 S[QT];
+  // S^T = K Q^T for 32 keys (rows) of the stage in buffer Ks, masked if asked
+  auto scores = [&](const T* Ks, int kt, int kpos, bool masked, f32x16 (&S)[QT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) S[qt] = zero16();
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const frag_t<T> a = ld8(Ks + (kt * 32 + col) * C::LDK + ks * 16 + hi * 8);
+      const frag_t<T> a = TK::row8(Ks, kt * 32 + col, ks * 16 + hi * 8);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) mma(S[qt], a, Qf[qt][ks]);
     }
-    bool grow = false;
-    float mnew[QT];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float mx = NEG_BIG;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float x = acc_row(i, lane) <= lim[qt] ? S[qt][i] : -INFINITY;
-        S[qt][i] = x;
-        mx = fmaxf(mx, x);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * g.scale_log2;
-      mnew[qt] = mx;
-      grow |= mx > m[qt] + RESCALE_GAP;
-    }
-    if (__ballot(grow)) {
+    if (masked) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const float mn = fmaxf(m[qt], mnew[qt]);
-        const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
-        m[qt] = mn;
-        l[qt] *= alpha;
+        const int lim = qbase + qt * 32 + col - kpos;    // key row r visible iff r <= lim
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) O[dt][qt][i] *= alpha;
+        for (int i = 0; i < 16; ++i) S[qt][i] = acc_row(i, lane) <= lim ? S[qt][i] : -INFINITY;
       }
     }
+  };
+
+  // Accumulation with a fixed reference maximum mref (base 2) per query
+  // column: P = exp2(s * scale_log2 - mref), l += sum P, O^T += V^T P^T.  No
+  // rescaling: with mref taken from real scores of the row, P stays finite
+  // unless a later score exceeds it by ~128 (base 2); l is checked afterwards.
+  f32x16 O[D / 32][QT];
+  float l[QT], mref[QT], mtrue[QT];
+  auto accumulate = [&](const T* Ks, const T* Vs, int kt, int kpos, bool masked) __attribute__((always_inline)) {
+    f32x16 S[QT];
+    scores(Ks, kt, kpos, masked, S);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       float ls = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(S[qt][i], g.scale_log2, -m[qt]));
+        const float p = __builtin_amdgcn_exp2f(fmaf(S[qt][i], g.scale_log2, -mref[qt]));
         S[qt][i] = p;
         ls += p;
       }
@@ -216,36 +191,106 @@ __global__ __launch_bounds__(256) void fwd_kernel(
     for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const frag_t<T> a = lds_col_frag<T>(Vs, C::LDK, kt * 32 + kk * 16, dt * 32, lane);
+        const frag_t<T> a = TK::col(Vs, kt * 32 + kk * 16, dt * 32, lane);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) mma(O[dt][qt], a, Pf[kk][qt]);
       }
     }
   };
-
-  if (nst > 0) { load_stage(0); store_stage(0); }
-  __syncthreads();
-
-  // The loop body is straight-line: the stage after the last re-reads the
-  // last stage (valid memory) into the unused buffer, and fully masked tiles
-  // of the diagonal block are computed with every key masked.
-  for (int s = 0; s < nst; ++s) {
-    const int buf = s & 1;
-    load_stage(s + 1 < nst ? s + 1 : s);
-    const int J = sel[s >> 1] - kb0;
-    const int kpos0 = J * 128 + (s & 1) * C::KC;
-    const T* Ks = smem + buf * C::STAGE;
-    const T* Vs = Ks + C::KS;
+  auto row_max = [&](const f32x16 (&S)[QT], float (&mx)[QT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      int lim[QT];
+    for (int qt = 0; qt < QT; ++qt) {
+      float m = NEG_BIG;
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-        lim[qt] = (J == diag) ? qbase + qt * 32 + col - (kpos0 + kt * 32) : 1024;
-      if (active) step(Ks, Vs, kt, lim);
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, S[qt][i]);
+      mx[qt] = fmaxf(m, __shfl_xor(m, 32, 64)) * g.scale_log2;
     }
-    store_stage(buf ^ 1);
+  };
+  auto track_max = [&](const T* Ks, const T* Vs, int kt, int kpos, bool masked) __attribute__((always_inline)) {
+    f32x16 S[QT];
+    float mx[QT];
+    scores(Ks, kt, kpos, masked, S);
+    row_max(S, mx);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) mtrue[qt] = fmaxf(mtrue[qt], mx[qt]);
+  };
+
+  // One pass over every stage; stage 0 must already sit in buffer 0.  The
+  // stage after the last re-reads the last one (valid memory) into the unused
+  // buffer, so each loop body is straight-line.
+  auto pass = [&](auto work) __attribute__((always_inline)) {
+    int s = 0;
+    for (; s < nst_plain; ++s) {
+      const int buf = s & 1;
+      load_stage(s + 1 < nst ? s + 1 : s);
+      const T* Ks = smem + buf * C::STAGE;
+      const T* Vs = Ks + C::KS;
+      const int kpos0 = (sel[s >> 1] - kb0) * 128 + (s & 1) * C::KC;
+      if (active) {
+        work(Ks, Vs, 0, kpos0, false);
+        work(Ks, Vs, 1, kpos0 + 32, false);
+      }
+      store_stage(buf ^ 1);
+      __syncthreads();
+    }
+    for (; s < nst; ++s) {
+      const int buf = s & 1;
+      load_stage(s + 1 < nst ? s + 1 : s);
+      const T* Ks = smem + buf * C::STAGE;
+      const T* Vs = Ks + C::KS;
+      const int kpos0 = diag * 128 + (s & 1) * C::KC;
+      if (active) {
+        work(Ks, Vs, 0, kpos0, true);
+        work(Ks, Vs, 1, kpos0 + 32, true);
+      }
+      store_stage(buf ^ 1);
+      __syncthreads();
+    }
+  };
+  auto restage0 = [&]() __attribute__((always_inline)) {
+    load_stage(0);
+    store_stage(0);
     __syncthreads();
+  };
+
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) O[dt][qt] = zero16();
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) { l[qt] = 0.f; mref[qt] = NEG_BIG; mtrue[qt] = NEG_BIG; }
+
+  restage0();
+  // reference maximum: the first 32 keys of the list (never all masked for a
+  // valid query: the list's lowest block starts at or before the query block)
+  if (active) {
+    f32x16 S[QT];
+    scores(smem, 0, (sel[0] - kb0) * 128, sel[0] - kb0 == diag, S);
+    row_max(S, mref);
+  }
+  pass(accumulate);
+
+  // fallback when a later score exceeded the reference by too much (never for
+  // ordinary inputs): find the true row maxima, then accumulate again
+  bool bad = false;
+  if (active) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
+      bad |= !(lt < 1.8446744e19f);                     // 2^64; also catches inf and nan
+    }
+  }
+  if (__syncthreads_or(bad)) {
+    restage0();
+    pass(track_max);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) O[dt][qt] = zero16();
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) { l[qt] = 0.f; mref[qt] = mtrue[qt]; }
+    restage0();
+    pass(accumulate);
   }
 
   if (!active) return;
@@ -265,7 +310,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(
           store4<T>(dst + d0, O[dt][qt][i4 * 4 + 0] * inv, O[dt][qt][i4 * 4 + 1] * inv,
                     O[dt][qt][i4 * 4 + 2] * inv, O[dt][qt][i4 * 4 + 3] * inv);
         }
-      if (hi == 0) lse[(int64_t)h * g.T + t] = (m[qt] + log2f(lt)) * LN2;
+      if (hi == 0) lse[(int64_t)h * g.T + t] = (mref[qt] + log2f(lt)) * LN2;
     }
   }
 }

@@ -24,6 +24,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace msa {
 
 typedef __bf16 bf16;
@@ -139,6 +142,95 @@ __device__ __forceinline__ f32x8 lds_col_frag<float>(const float* X, int ld, int
 #pragma unroll
   for (int j = 0; j < 8; ++j) r[j] = X[(k0 + ((j >> 2) << 3) + hi * 4 + (j & 3)) * ld + c];
   return r;
+}
+
+// ---------------------------------------------------------------------------
+// Row-major LDS tiles without padding whose 16-byte chunks are XOR-swizzled by
+// row.  gfx950's LDS has 64 four-byte banks and serves 16 lanes per cycle for
+// 16-byte reads and 32 lanes per cycle for 8-byte reads; these swizzles make
+// both access patterns used here conflict-free: a 16-byte read of the same
+// chunk from 16 consecutive rows, and the transpose reads of lds_col_frag
+// (4 consecutive rows x 32 bytes per 16-lane group).
+//   16 chunks per row (256 B): chunk ^ ((r & 3) << 2 | (r >> 2) & 3)
+//    8 chunks per row (128 B): chunk ^ (((r >> 1) & 1) << 2 | (r >> 2) & 3)
+//   fewer chunks: no swizzle (only the small fp32 / d = 64 tiles)
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int chunk) {
+  if constexpr (CPR >= 16) return chunk ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  else if constexpr (CPR == 8) return chunk ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  else return chunk;
+}
+template <typename T, int COLS>
+struct Tile {
+  static constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+  static constexpr int CPR = COLS / EPC;            // chunks per row
+  static constexpr int ELEMS_PER_ROW = COLS;
+  __device__ static __forceinline__ int off(int r, int c) {
+    return r * COLS + swz<CPR>(r, c / EPC) * EPC + (c % EPC);
+  }
+  // 8 consecutive elements of row r starting at column c (c % 8 == 0)
+  __device__ static __forceinline__ frag_t<T> row8(const T* X, int r, int c);
+  // transposed fragment: see lds_col_frag
+  __device__ static __forceinline__ frag_t<T> col(const T* X, int k0, int n0, int lane);
+};
+template <typename T, int COLS>
+__device__ __forceinline__ frag_t<T> Tile<T, COLS>::row8(const T* X, int r, int c) {
+  if constexpr (sizeof(T) == 2) {
+    return ld8(X + off(r, c));
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(X + off(r, c));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(X + off(r, c + 4));
+    f32x8 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { v[j] = a[j]; v[j + 4] = b[j]; }
+    return v;
+  }
+}
+template <typename T, int COLS>
+__device__ __forceinline__ frag_t<T> Tile<T, COLS>::col(const T* X, int k0, int n0, int lane) {
+  if constexpr (sizeof(T) == 2) {
+    const int s = lane & 15, g = lane >> 4, hi = lane >> 5;
+    const int r = k0 + hi * 4 + (s >> 2);
+    const int c = n0 + 16 * (g & 1) + 4 * (s & 3);
+    const bf16x4 a = lds_tr4(X + off(r, c)), b = lds_tr4(X + off(r + 8, c));
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { v[j] = a[j]; v[j + 4] = b[j]; }
+    return v;
+  } else {
+    const int c = n0 + (lane & 31), hi = lane >> 5;
+    f32x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = X[off(k0 + ((j >> 2) << 3) + hi * 4 + (j & 3), c)];
+    return v;
+  }
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Asynchronous global -> LDS copies (gfx950 global_load_lds).  Lane l's bytes
+// land at lds_wave_base + l * size; lds_wave_base must be wave-uniform.  They
+// are counted by vmcnt like other vector loads, so a stage is known to have
+// landed once vmcnt has dropped to the number of loads issued after it.
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
+}
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima; gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // Row of accumulator element i for lane l (see the layout note above).

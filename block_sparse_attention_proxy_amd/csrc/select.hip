@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void proxy_scores_kernel(const T* __restrict__
     float stash0 = 0.f, stash1 = 0.f;
 
     frag_t<T> Bc[4][KSL];
-    auto load_b = [&](int J, frag_t<T> (&Bf)[4][KSL]) {
+    auto load_b = [&](int J, frag_t<T> (&Bf)[4][KSL]) __attribute__((always_inline)) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const T* src = kp + ((int64_t)(t0 + J * 128 + kt * 32 + col) * Hp + grp) * DP + hi8;
