@@ -10,9 +10,9 @@
 // dkp = s_p dY^T qp.
 //
 // Kernels, in launch order:
-//   delta_kernel   D = rowsum(dO * O) per (head, token)
 //   dq_kernel      query-major over the same block lists as the forward:
-//                  dQ, and the proxy term sum_u (Q - P/G) kp per head
+//                  D = rowsum(dO * O) (kept for the KV-major pass), dQ, and
+//                  the proxy term sum_u (Q - P/G) kp per head
 //   dqp_reduce     sums the per-head proxy terms when a group spans
 //                  several workgroups (G > 4)
 //   dkdv_kernel    KV-major over the inverted lists: dK, dV and dkp, each
@@ -38,55 +38,44 @@ __device__ __forceinline__ int find_doc(const int32_t* a, int n, int x) {
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
-                                                    float* __restrict__ delta, Geo g) {
-  const int64_t n = (int64_t)g.T * g.Hq;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = e / g.Hq;
-    const int h = (int)(e % g.Hq);
-    const T* a = o + e * D;
-    const T* b = dout + e * D;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int d = 0; d < D; ++d) acc += to_f32(a[d]) * to_f32(b[d]);
-    delta[(int64_t)h * g.T + t] = acc;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // dQ kernel: a workgroup serves (group, query block, 4 units); a wave owns 32
 // queries of one head.  Stages are 64-key halves of the selected blocks with
-// K, V and kp rows in LDS; K^T and kp^T fragments come from the same tiles
-// through LDS transpose reads.
+// K, V and kp rows copied global -> LDS by DMA one stage ahead; K^T and kp^T
+// fragments come from the same tiles through LDS transpose reads.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int DP>
 struct DqCfg {
-  static constexpr int KC = 64;
+  static constexpr int KC = 64;                   // keys per stage
+  static constexpr int NBUF = 3;                  // LDS ring of stages (one workgroup per CU)
+  static constexpr int AHEAD = NBUF - 1;
   typedef Tile<T, D> TK;                          // K and V rows
   typedef Tile<T, DP> TP;                         // kp rows
   static constexpr int KS = KC * D, KPS = KC * DP;
-  static constexpr int STAGE = 2 * KS + KPS;
-  static constexpr int LDS_BYTES = 2 * STAGE * (int)sizeof(T);
-  static constexpr int EPC = TK::EPC, CPR = TK::CPR, CPRP = TP::CPR;
-  static constexpr int NK = KC * CPR / 256, NP = KC * CPRP / 256;
-  static_assert(NK >= 1 && NP >= 1, "tile split");
+  static constexpr int STAGE = 2 * KS + KPS;      // elements of T
+  static constexpr int STAGE_BYTES = STAGE * (int)sizeof(T);
+  static constexpr int LDS_BYTES = NBUF * STAGE_BYTES;
+  static constexpr int EPC = TK::EPC;
+  static constexpr int KROWS_PER_COPY = 64 / TK::CPR, PROWS_PER_COPY = 64 / TP::CPR;
+  static constexpr int NKCOPY = KC / (4 * KROWS_PER_COPY);          // per tensor per wave
+  static constexpr int NPCOPY = KC / (4 * PROWS_PER_COPY);
+  static constexpr int COPIES = 2 * NKCOPY + NPCOPY;
+  static_assert(NKCOPY >= 1 && NPCOPY >= 1, "copy split");
+  static_assert(KC % (4 * KROWS_PER_COPY) == 0 && KC % (4 * PROWS_PER_COPY) == 0, "copy split");
   static_assert(4 * DP * 32 * 4 <= LDS_BYTES, "reduction scratch");
 };
 
 template <typename T, int D, int DP>
 __global__ __launch_bounds__(256) void dq_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ qp, const T* __restrict__ kp, const float* __restrict__ lse,
-    const float* __restrict__ lse_p, const T* __restrict__ dout, const float* __restrict__ delta,
-    const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_cnt,
-    float* __restrict__ dq, float* __restrict__ dqp, float* __restrict__ cpart, Geo g) {
+    const T* __restrict__ qp, const T* __restrict__ kp, const T* __restrict__ o,
+    const float* __restrict__ lse, const float* __restrict__ lse_p, const T* __restrict__ dout,
+    float* __restrict__ delta, const int32_t* __restrict__ q2k_idx,
+    const int32_t* __restrict__ q2k_cnt, float* __restrict__ dq, float* __restrict__ dqp,
+    float* __restrict__ cpart, Geo g) {
   typedef DqCfg<T, D, DP> C;
   typedef typename C::TK TK;
   typedef typename C::TP TP;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  T* smem = reinterpret_cast<T*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hi = lane >> 5;
   const int NU = g.G * (g.Bq / 32);
@@ -114,70 +103,78 @@ __global__ __launch_bounds__(256) void dq_kernel(
   const int qrow = qpos < L ? qpos : L - 1;
   const int64_t tq = t0 + qrow;
 
-  frag_t<T> Qf[D / 16], dOf[D / 16], QPf[DP / 16];
-  float lse2 = 0.f, dl = 0.f, lsep2 = 0.f;
-  if (active) {
-    const T* sq = q + (tq * g.Hq + h) * D + hi * 8;
-    const T* sd = dout + (tq * g.Hq + h) * D + hi * 8;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) { Qf[ks] = ld8(sq + ks * 16); dOf[ks] = ld8(sd + ks * 16); }
-    const T* sp = qp + (tq * g.Hkv + grp) * DP + hi * 8;
-#pragma unroll
-    for (int ks = 0; ks < DP / 16; ++ks) QPf[ks] = ld8(sp + ks * 16);
-    lse2 = lse[(int64_t)h * g.T + tq] * LOG2E;
-    dl = delta[(int64_t)h * g.T + tq];
-    lsep2 = lse_p[(int64_t)grp * g.T + tq] * LOG2E;
-  }
-  const float invG = 1.f / (float)g.G;
-
-  f32x16 dQ[D / 32], Cp[DP / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) dQ[dt] = zero16();
-#pragma unroll
-  for (int dt = 0; dt < DP / 32; ++dt) Cp[dt] = zero16();
-
   // stages: 64-key halves of the selected blocks; the diagonal block is last
   int nst = 2 * cnt;
   if (diag * 128 + 64 > I * g.Bq + g.Bq - 1) nst -= 1;
   const int nst_plain = 2 * (cnt - 1);
 
-  uint4 Kr[C::NK], Vr[C::NK], Pr[C::NP];
-  auto load_stage = [&](int s) __attribute__((always_inline)) {
-    const int J = sel[s >> 1] - kb0;
-    const int key0 = J * 128 + (s & 1) * C::KC;
+  // Copy stage s (clamped to the last) into ring slot s % NBUF.  Key rows past
+  // the document end are clamped to its last row; they only occur in the
+  // diagonal block, where the causal mask removes them.
+  auto issue = [&](int s) __attribute__((always_inline)) {
+    const int ss = s < nst ? s : nst - 1;
+    const uint32_t base = lds_offset(smem_raw) + (s % C::NBUF) * C::STAGE_BYTES;
+    const int key0 = (sel[ss >> 1] - kb0) * 128 + (ss & 1) * C::KC;
 #pragma unroll
-    for (int i = 0; i < C::NK; ++i) {
-      const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR, key = key0 + r;
-      const int64_t off = ((int64_t)(t0 + key) * g.Hkv + grp) * D + cc * C::EPC;
-      Kr[i] = key < L ? *reinterpret_cast<const uint4*>(k + off) : make_uint4(0, 0, 0, 0);
-      Vr[i] = key < L ? *reinterpret_cast<const uint4*>(v + off) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < C::NKCOPY; ++j) {
+      const int rfirst = (wave * C::NKCOPY + j) * C::KROWS_PER_COPY;
+      const int r = rfirst + lane / TK::CPR, p = lane % TK::CPR;
+      const int key = key0 + r < L ? key0 + r : L - 1;
+      const int64_t off = ((int64_t)(t0 + key) * g.Hkv + grp) * D + swz<TK::CPR>(r, p) * C::EPC;
+      dma16(k + off, base + rfirst * D * (int)sizeof(T));
+      dma16(v + off, base + (C::KS + rfirst * D) * (int)sizeof(T));
     }
 #pragma unroll
-    for (int i = 0; i < C::NP; ++i) {
-      const int c = tid + 256 * i, r = c / C::CPRP, cc = c % C::CPRP, key = key0 + r;
-      Pr[i] = key < L ? *reinterpret_cast<const uint4*>(kp + ((int64_t)(t0 + key) * g.Hkv + grp) * DP + cc * C::EPC)
-                      : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_stage = [&](int buf) __attribute__((always_inline)) {
-    T* Ks = smem + buf * C::STAGE;
-    T* Vs = Ks + C::KS;
-    T* KPs = Vs + C::KS;
-#pragma unroll
-    for (int i = 0; i < C::NK; ++i) {
-      const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR;
-      *reinterpret_cast<uint4*>(Ks + TK::off(r, cc * C::EPC)) = Kr[i];
-      *reinterpret_cast<uint4*>(Vs + TK::off(r, cc * C::EPC)) = Vr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::NP; ++i) {
-      const int c = tid + 256 * i, r = c / C::CPRP, cc = c % C::CPRP;
-      *reinterpret_cast<uint4*>(KPs + TP::off(r, cc * C::EPC)) = Pr[i];
+    for (int j = 0; j < C::NPCOPY; ++j) {
+      const int rfirst = (wave * C::NPCOPY + j) * C::PROWS_PER_COPY;
+      const int r = rfirst + lane / TP::CPR, p = lane % TP::CPR;
+      const int key = key0 + r < L ? key0 + r : L - 1;
+      const int64_t off = ((int64_t)(t0 + key) * g.Hkv + grp) * DP + swz<TP::CPR>(r, p) * C::EPC;
+      dma16(kp + off, base + (2 * C::KS + rfirst * DP) * (int)sizeof(T));
     }
   };
+  frag_t<T> Qf[D / 16], dOf[D / 16], QPf[DP / 16];
+  float lse2 = 0.f, dl = 0.f, lsep2 = 0.f;
+  if (active) {
+    const T* sq = q + (tq * g.Hq + h) * D + hi * 8;
+    const T* sd = dout + (tq * g.Hq + h) * D + hi * 8;
+    const T* so = o + (tq * g.Hq + h) * D + hi * 8;
+    float part = 0.f;                               // this lane's half of rowsum(dO * O)
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      Qf[ks] = ld8(sq + ks * 16);
+      dOf[ks] = ld8(sd + ks * 16);
+      const frag_t<T> of = ld8(so + ks * 16);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part = fmaf(to_f32(dOf[ks][j]), to_f32(of[j]), part);
+    }
+    dl = part + __shfl_xor(part, 32, 64);
+    if (hi == 0 && qpos < L) delta[(int64_t)h * g.T + t0 + qpos] = dl;
+    const T* sp = qp + (tq * g.Hkv + grp) * DP + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < DP / 16; ++ks) QPf[ks] = ld8(sp + ks * 16);
+    lse2 = lse[(int64_t)h * g.T + tq] * LOG2E;
+    lsep2 = lse_p[(int64_t)grp * g.T + tq] * LOG2E;
+  }
+  // The register loads above complete before the first copies are issued, so
+  // that the copies are the only vector-memory operations in flight in the
+  // loop (the vmcnt waits there count only them).
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int j = 0; j < C::AHEAD; ++j) issue(j);
 
-  // one 32-key tile of a stage; lim: key row r visible iff r <= lim
-  auto tile = [&](const T* Ks, const T* Vs, const T* KPs, int kt, int lim, bool assigned) __attribute__((always_inline)) {
+  // dQ^T, and the proxy terms kept apart: Cq^T += kp^T Q^T over the tiles this
+  // head is assigned, Cp^T += kp^T P^T over every tile; the head's share of
+  // the proxy gradient is Cq - Cp / G.
+  f32x16 dQ[D / 32], Cq[DP / 32], Cp[DP / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) dQ[dt] = zero16();
+#pragma unroll
+  for (int dt = 0; dt < DP / 32; ++dt) { Cq[dt] = zero16(); Cp[dt] = zero16(); }
+
+  // one 32-key tile of a stage; key row r is visible iff r <= lim
+  auto tile = [&](const T* Ks, const T* Vs, const T* KPs, int kt, int lim, bool masked,
+                  bool assigned) __attribute__((always_inline)) {
     f32x16 S = zero16(), dP = zero16();
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
@@ -187,17 +184,19 @@ __global__ __launch_bounds__(256) void dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float p = __builtin_amdgcn_exp2f(fmaf(S[i], g.scale_log2, -lse2));
-      p = acc_row(i, lane) <= lim ? p : 0.f;
+      if (masked) p = acc_row(i, lane) <= lim ? p : 0.f;
       S[i] = p;
       dP[i] = p * (dP[i] - dl);
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const frag_t<T> bs = acc_frag<T>(dP, kk);
+      const frag_t<T> bp = acc_frag<T>(S, kk);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) mma(dQ[dt], TK::col(Ks, kt * 32 + kk * 16, dt * 32, lane), bs);
+#pragma unroll
+      for (int dt = 0; dt < DP / 32; ++dt) mma(Cp[dt], TP::col(KPs, kt * 32 + kk * 16, dt * 32, lane), bp);
     }
-    // proxy: E = [assigned] Q - P / G ;  C^T += kp^T E^T
     if (assigned) {
       f32x16 Y = zero16();
 #pragma unroll
@@ -205,44 +204,43 @@ __global__ __launch_bounds__(256) void dq_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], g.pscale_log2, -lsep2));
-        qv = acc_row(i, lane) <= lim ? qv : 0.f;
-        S[i] = qv - S[i] * invG;
+        if (masked) qv = acc_row(i, lane) <= lim ? qv : 0.f;
+        Y[i] = qv;
       }
-    } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) S[i] = -S[i] * invG;
-    }
+      for (int kk = 0; kk < 2; ++kk) {
+        const frag_t<T> bq = acc_frag<T>(Y, kk);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const frag_t<T> be = acc_frag<T>(S, kk);
-#pragma unroll
-      for (int dt = 0; dt < DP / 32; ++dt) mma(Cp[dt], TP::col(KPs, kt * 32 + kk * 16, dt * 32, lane), be);
+        for (int dt = 0; dt < DP / 32; ++dt) mma(Cq[dt], TP::col(KPs, kt * 32 + kk * 16, dt * 32, lane), bq);
+      }
     }
   };
   auto stage_body = [&](int s, bool masked) __attribute__((always_inline)) {
-    const int buf = s & 1;
-    load_stage(s + 1 < nst ? s + 1 : s);
-    const T* Ks = smem + buf * C::STAGE;
+    wait_vmcnt<C::COPIES * (C::AHEAD - 1)>();
+    __syncthreads();
+    issue(s + C::AHEAD);
+    const T* Ks = reinterpret_cast<const T*>(smem_raw + (s % C::NBUF) * C::STAGE_BYTES);
     const T* Vs = Ks + C::KS;
     const T* KPs = Vs + C::KS;
     const int kpos0 = (sel[s >> 1] - kb0) * 128 + (s & 1) * C::KC;
     if (active) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int lim = masked ? qpos - (kpos0 + kt * 32) : 1024;
-        tile(Ks, Vs, KPs, kt, lim, ((s * 2 + kt) % g.G) == hl);
-      }
+      for (int kt = 0; kt < 2; ++kt)
+        tile(Ks, Vs, KPs, kt, qpos - (kpos0 + kt * 32), masked, ((s * 2 + kt) % g.G) == hl);
     }
-    store_stage(buf ^ 1);
-    __syncthreads();
   };
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
   int s = 0;
   for (; s < nst_plain; ++s) stage_body(s, false);
   for (; s < nst; ++s) stage_body(s, true);
+  wait_vmcnt<0>();
+  __syncthreads();
+  f32x16 Cd[DP / 32];
+  const float invG = 1.f / (float)g.G;
+#pragma unroll
+  for (int dt = 0; dt < DP / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Cd[dt][i] = Cq[dt][i] - Cp[dt][i] * invG;
 
   // dQ out (fp32)
   if (active && qpos < L) {
@@ -263,7 +261,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
 #pragma unroll
     for (int dt = 0; dt < DP / 32; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) red[(wave * DP + dt * 32 + acc_row(i, lane)) * 32 + col] = Cp[dt][i];
+      for (int i = 0; i < 16; ++i) red[(wave * DP + dt * 32 + acc_row(i, lane)) * 32 + col] = Cd[dt][i];
   }
   __syncthreads();
   const int u_lo = wgi * 4;
@@ -391,7 +389,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
   // copies per stage (COPIES, + NPCOPY at a chunk's last head), which the
   // vmcnt waits below rely on.
   auto issue_stage = [&](int buf, int li, int c, int hl, bool with_qp) __attribute__((always_inline)) {
-    unsigned char* base = smem_raw + buf * C::STAGE_BYTES;
+    const uint32_t base = lds_offset(smem_raw) + buf * C::STAGE_BYTES;
     const int I = lst[li] - qb0;
     const int h = grp * G + hl;
     const int row0 = I * g.Bq + c * 32;
@@ -605,20 +603,13 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
     attr = true;
   }
   hipError_t e;
-  const int64_t nd = (int64_t)g.T * g.Hq;
-  if (nd > 0) {
-    { ProfScope _ps("bwd_delta", s);
-    hipLaunchKernelGGL((delta_kernel<T, D>), dim3(grid_for_b(nd, 256)), dim3(256), 0, s,
-                       (const T*)o, (const T*)dout, w.delta, g); }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   const int NU = g.G * (g.Bq / 32);
   const int64_t nq = (int64_t)g.Hkv * g.nqb * ((NU + 3) / 4);
   if (nq > 0) {
     { ProfScope _ps("bwd_dq", s);
     hipLaunchKernelGGL((dq_kernel<T, D, DP>), dim3((unsigned)nq), dim3(256), CQ::LDS_BYTES, s,
-                       (const T*)q, (const T*)k, (const T*)v, (const T*)qp, (const T*)kp, lse, lse_p,
-                       (const T*)dout, w.delta, q2k_idx, q2k_cnt, dq, dqp, w.cpart, g); }
+                       (const T*)q, (const T*)k, (const T*)v, (const T*)qp, (const T*)kp, (const T*)o,
+                       lse, lse_p, (const T*)dout, w.delta, q2k_idx, q2k_cnt, dq, dqp, w.cpart, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (g.G > 4 && g.T > 0) {

@@ -217,14 +217,41 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Asynchronous global -> LDS copies (gfx950 global_load_lds).  Lane l's bytes
-// land at lds_wave_base + l * size; lds_wave_base must be wave-uniform.  They
-// are counted by vmcnt like other vector loads, so a stage is known to have
-// landed once vmcnt has dropped to the number of loads issued after it.
-__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+// land at LDS byte address lds + l * size; lds must be wave-uniform.  The
+// copies are counted by vmcnt like other vector loads, so a stage is known to
+// have landed once vmcnt has dropped to the number of loads issued after it;
+// the callers wait for that explicitly (wait_vmcnt) and then barrier.
+//
+// The copies are issued from inline assembly on purpose.  Through the
+// compiler builtin, a workgroup barrier waits for every copy in flight (the
+// copies count as LDS stores), which serialises the ring of stages.  Hidden
+// from the compiler, the copies can only make its own vmcnt waits more
+// conservative: vector loads retire in order, so loads it does not know of
+// only delay the point where its counts are reached.  M0 carries the LDS
+// address; it is saved and restored around the copy, with the one wait state
+// the hardware needs between writing M0 and the copy reading it.  The
+// "memory" clobber keeps LDS reads of earlier stages from moving past a copy.
+__device__ __forceinline__ uint32_t lds_offset(const void* shared_array) {
+  // only for pointers taken directly from a __shared__ array
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)shared_array;
 }
-__device__ __forceinline__ void dma4(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds))
+      : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds))
+      : "memory");
 }
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima; gfx9 encoding)
 template <int N>
