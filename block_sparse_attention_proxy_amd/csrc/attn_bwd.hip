@@ -69,9 +69,9 @@ __global__ __launch_bounds__(256) void dq_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ qp, const T* __restrict__ kp, const T* __restrict__ o,
     const float* __restrict__ lse, const float* __restrict__ lse_p, const T* __restrict__ dout,
-    float* __restrict__ delta, const int32_t* __restrict__ q2k_idx,
-    const int32_t* __restrict__ q2k_cnt, float* __restrict__ dq, float* __restrict__ dqp,
-    float* __restrict__ cpart, Geo g) {
+    float* __restrict__ delta, float* __restrict__ lse2_out, float* __restrict__ lsep2_out,
+    const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_cnt,
+    float* __restrict__ dq, float* __restrict__ dqp, float* __restrict__ cpart, Geo g) {
   typedef DqCfg<T, D, DP> C;
   typedef typename C::TK TK;
   typedef typename C::TP TP;
@@ -149,12 +149,17 @@ __global__ __launch_bounds__(256) void dq_kernel(
       for (int j = 0; j < 8; ++j) part = fmaf(to_f32(dOf[ks][j]), to_f32(of[j]), part);
     }
     dl = part + __shfl_xor(part, 32, 64);
-    if (hi == 0 && qpos < L) delta[(int64_t)h * g.T + t0 + qpos] = dl;
     const T* sp = qp + (tq * g.Hkv + grp) * DP + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < DP / 16; ++ks) QPf[ks] = ld8(sp + ks * 16);
     lse2 = lse[(int64_t)h * g.T + tq] * LOG2E;
     lsep2 = lse_p[(int64_t)grp * g.T + tq] * LOG2E;
+    // per-query values the KV-major pass reads: D and both LSEs in log2 units
+    if (hi == 0 && qpos < L) {
+      delta[(int64_t)h * g.T + tq] = dl;
+      lse2_out[(int64_t)h * g.T + tq] = lse2;
+      if (hl == 0) lsep2_out[(int64_t)grp * g.T + tq] = lsep2;
+    }
   }
   // The register loads above complete before the first copies are issued, so
   // that the copies are the only vector-memory operations in flight in the
@@ -318,12 +323,13 @@ struct KvCfg {
   static constexpr int NBUF = 4;                  // LDS ring of stages
   static constexpr int AHEAD = NBUF - 1;          // stages in flight ahead of the one computed
   typedef Tile<T, D> TQ;                          // Q and dO rows
-  typedef Tile<T, DP> TP;                         // qp rows
+  typedef Tile<T, DP> TP;                         // qp rows, and the block's kp rows
   static constexpr int QS = QC * D, PS = QC * DP;
   static constexpr int STAGE_T = 2 * QS + PS;                        // elements of T
   static constexpr int FL_OFF = ((STAGE_T * (int)sizeof(T) + 15) / 16) * 16;
-  static constexpr int STAGE_BYTES = FL_OFF + 4 * QC * 4;            // lse, D, lse_p, spare
-  static constexpr int LDS_BYTES = NBUF * STAGE_BYTES;
+  static constexpr int STAGE_BYTES = FL_OFF + 4 * QC * 4;            // lse2, D, lsep2, spare
+  static constexpr int KP_OFF = NBUF * STAGE_BYTES;                  // kp rows of the KV block
+  static constexpr int LDS_BYTES = KP_OFF + 128 * DP * (int)sizeof(T);
   static constexpr int EPC = TQ::EPC;
   // copies per wave per stage: Q and dO rows, one vector of floats, and the
   // qp rows at the last head of a chunk
@@ -331,7 +337,8 @@ struct KvCfg {
   static constexpr int NQCOPY = QC / (4 * QROWS_PER_COPY);           // per tensor per wave
   static constexpr int PROWS_PER_COPY = 64 / TP::CPR;
   static constexpr int NPCOPY = (QC + 4 * PROWS_PER_COPY - 1) / (4 * PROWS_PER_COPY);
-  static_assert(QC % PROWS_PER_COPY == 0, "copy split");
+  static constexpr int NKPCOPY = 32 / PROWS_PER_COPY;                // a wave's 32 kp rows
+  static_assert(QC % PROWS_PER_COPY == 0 && 32 % PROWS_PER_COPY == 0, "copy split");
   static constexpr int COPIES = 2 * NQCOPY + 1;
   static_assert(NQCOPY >= 1 && QC % (4 * QROWS_PER_COPY) == 0, "copy split");
 };
@@ -339,8 +346,8 @@ struct KvCfg {
 template <typename T, int D, int DP, int G>
 __global__ __launch_bounds__(256) void dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ qp, const T* __restrict__ kp, const float* __restrict__ lse,
-    const float* __restrict__ lse_p, const T* __restrict__ dout, const float* __restrict__ delta,
+    const T* __restrict__ qp, const T* __restrict__ kp, const float* __restrict__ lse2,
+    const float* __restrict__ lsep2, const T* __restrict__ dout, const float* __restrict__ delta,
     const int32_t* __restrict__ k2q_ptr, const int32_t* __restrict__ k2q_idx,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dkp, Geo g) {
   typedef KvCfg<T, D, DP> C;
@@ -365,18 +372,27 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
   const int len = ptr[KB + 1] - ptr[KB];
   const int nch = g.Bq / 32;
   const float invG = 1.f / (float)G;
-  const float lam_ps = g.lam * g.pscale;
+  const T* KPs = reinterpret_cast<const T*>(smem_raw + C::KP_OFF);
 
-  frag_t<T> Kf[D / 16], Vf[D / 16], KPf[DP / 16];
+  // K and V of this lane's key stay in registers as B fragments; the kp rows
+  // of the wave's 32 keys go to LDS (read only at a chunk's last head).
+  frag_t<T> Kf[D / 16], Vf[D / 16];
   {
     const T* sk = k + (tk * g.Hkv + grp) * D + hi * 8;
     const T* sv = v + (tk * g.Hkv + grp) * D + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) { Kf[ks] = ld8(sk + ks * 16); Vf[ks] = ld8(sv + ks * 16); }
-    const T* sp = kp + (tk * g.Hkv + grp) * DP + hi * 8;
-#pragma unroll
-    for (int ks = 0; ks < DP / 16; ++ks) KPf[ks] = ld8(sp + ks * 16);
   }
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int j = 0; j < C::NKPCOPY; ++j) {
+    const int rfirst = wave * 32 + j * C::PROWS_PER_COPY;
+    const int r = rfirst + lane / TP::CPR, p = lane % TP::CPR;
+    const int key = J * 128 + r < L ? J * 128 + r : L - 1;
+    dma16(kp + ((int64_t)(t0 + key) * g.Hkv + grp) * DP + swz<TP::CPR>(r, p) * C::EPC,
+          lds_offset(smem_raw) + C::KP_OFF + rfirst * DP * (int)sizeof(T));
+  }
+
   f32x16 dK[D / 32], dV[D / 32], dKp[DP / 32], Tacc = zero16();
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) { dK[dt] = zero16(); dV[dt] = zero16(); }
@@ -410,35 +426,35 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
         const int rfirst = ((wave * C::NPCOPY + j) % (C::QC / C::PROWS_PER_COPY)) * C::PROWS_PER_COPY;
         const int r = rfirst + lane / TP::CPR;
         const int p = lane % TP::CPR;
-        const int rr = r;
-        const int pos = row0 + rr < L ? row0 + rr : L - 1;
-        const int64_t off = ((int64_t)(t0 + pos) * g.Hkv + grp) * DP + swz<TP::CPR>(rr, p) * C::EPC;
+        const int pos = row0 + r < L ? row0 + r : L - 1;
+        const int64_t off = ((int64_t)(t0 + pos) * g.Hkv + grp) * DP + swz<TP::CPR>(r, p) * C::EPC;
         dma16(qp + off, base + (2 * C::QS + rfirst * DP) * (int)sizeof(T));
       }
     }
-    // one float vector per wave (lse, D, lse_p, and lse_p again into the
+    // one float vector per wave (lse2, D, lsep2, and lsep2 again into the
     // spare slot): 32 lanes x 4 bytes, the other lanes inactive so nothing
     // lands outside the wave's 128-byte slot
     if (lane < C::QC) {
       const int pos = row0 + lane < L ? row0 + lane : L - 1;
       const int64_t t = t0 + pos;
-      const float* src = wave == 0 ? lse + (int64_t)h * g.T + t
+      const float* src = wave == 0 ? lse2 + (int64_t)h * g.T + t
                        : wave == 1 ? delta + (int64_t)h * g.T + t
-                       : lse_p + (int64_t)grp * g.T + t;
+                       : lsep2 + (int64_t)grp * g.T + t;
       dma4(src, base + C::FL_OFF + wave * C::QC * 4);
     }
   };
-  // per-lane values of the 16 query rows held by accumulator elements
-  auto rows16 = [&](const float* f, float (&out)[16]) __attribute__((always_inline)) {
+  // the 8 query rows held by accumulator elements [8kk, 8kk + 8)
+  auto rows8 = [&](const float* f, int kk, float (&out)[8]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(f + acc_row(i4 * 4, lane));
+    for (int i4 = 0; i4 < 2; ++i4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(f + acc_row(kk * 8 + i4 * 4, lane));
 #pragma unroll
       for (int j = 0; j < 4; ++j) out[i4 * 4 + j] = x[j];
     }
   };
   // masked: query row r counts iff lo <= r < hi_ (causal lower bound from
-  // this lane's key, upper bound from the document end)
+  // this lane's key, upper bound from the document end).  The softmax scale
+  // of dK and lam * s_p of dkp are applied once, at the end.
   auto main_part = [&](const unsigned char* base, int lo, int hi_, bool masked) __attribute__((always_inline)) {
     const T* Qs = reinterpret_cast<const T*>(base);
     const T* dOs = Qs + C::QS;
@@ -449,19 +465,22 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
       mma(S, TQ::row8(Qs, col, ks * 16 + hi * 8), Kf[ks]);
       mma(dP, TQ::row8(dOs, col, ks * 16 + hi * 8), Vf[ks]);
     }
-    float lr16[16], dl16[16];
-    rows16(fl, lr16);
-    rows16(fl + C::QC, dl16);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float p = __builtin_amdgcn_exp2f(fmaf(S[i], g.scale_log2, -lr16[i] * LOG2E));
-      if (masked) p = (acc_row(i, lane) >= lo && acc_row(i, lane) < hi_) ? p : 0.f;
-      S[i] = p;
-      dP[i] = p * (dP[i] - dl16[i]) * g.scale;             // dS with the softmax scale of dK folded in
-      Tacc[i] += p;
-    }
+    // two halves: the products of the first half run while the second
+    // half's exponentials are computed
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      float lr[8], dl[8];
+      rows8(fl, kk, lr);
+      rows8(fl + C::QC, kk, dl);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = kk * 8 + j;
+        float p = __builtin_amdgcn_exp2f(fmaf(S[i], g.scale_log2, -lr[j]));
+        if (masked) p = (acc_row(i, lane) >= lo && acc_row(i, lane) < hi_) ? p : 0.f;
+        S[i] = p;
+        dP[i] = p * (dP[i] - dl[j]);
+        Tacc[i] += p;
+      }
       const frag_t<T> ap = acc_frag<T>(S, kk);
       const frag_t<T> as = acc_frag<T>(dP, kk);
 #pragma unroll
@@ -476,17 +495,19 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
     const float* fl = reinterpret_cast<const float*>(base + C::FL_OFF);
     f32x16 Y = zero16();
 #pragma unroll
-    for (int ks = 0; ks < DP / 16; ++ks) mma(Y, TP::row8(Ps, col, ks * 16 + hi * 8), KPf[ks]);
-    float lp16[16];
-    rows16(fl + 2 * C::QC, lp16);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], g.pscale_log2, -lp16[i] * LOG2E));
-      if (masked) qv = (acc_row(i, lane) >= lo && acc_row(i, lane) < hi_) ? qv : 0.f;
-      Y[i] = lam_ps * (qv - Tacc[i] * invG);                 // lam * s_p * dY
-    }
+    for (int ks = 0; ks < DP / 16; ++ks)
+      mma(Y, TP::row8(Ps, col, ks * 16 + hi * 8), TP::row8(KPs, wave * 32 + col, ks * 16 + hi * 8));
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      float lp[8];
+      rows8(fl + 2 * C::QC, kk, lp);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = kk * 8 + j;
+        float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], g.pscale_log2, -lp[j]));
+        if (masked) qv = (acc_row(i, lane) >= lo && acc_row(i, lane) < hi_) ? qv : 0.f;
+        Y[i] = fmaf(-invG, Tacc[i], qv);                     // dY / (lam * s_p)
+      }
       const frag_t<T> ay = acc_frag<T>(Y, kk);
 #pragma unroll
       for (int dt = 0; dt < DP / 32; ++dt) mma(dKp[dt], ay, TP::col(Ps, kk * 16, dt * 32, lane));
@@ -531,7 +552,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
     static_for<G>([&](auto hlc) __attribute__((always_inline)) {
       constexpr int hl = decltype(hlc)::value;
       // stage ci*G + hl must have landed: the AHEAD - 1 later stages in
-      // flight issued COPIES (+ NPCOPY at their chunk's last head) each
+      // flight issued COPIES (+ NPCOPY at their chunk's last head) each.
+      // The kp rows were issued before the first stage, so they have landed
+      // by the first wait.
       constexpr int later = []() {
         int n = 0;
         for (int j = 1; j < C::AHEAD; ++j) n += C::COPIES + (((hl + j) % G == G - 1) ? C::NPCOPY : 0);
@@ -552,8 +575,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
   for (; ci < nchunk_lead && ci < nchunk; ++ci) chunk_body(ci, true);
   for (; ci < nchunk_plain_end; ++ci) chunk_body(ci, false);
   for (; ci < nchunk; ++ci) chunk_body(ci, true);
+  // copies issued past the last stage must land before the workgroup ends
+  wait_vmcnt<0>();
 
   // outputs: lane holds column d = dt*32 + col for 16 key rows
+  const float lam_ps = g.lam * g.pscale;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int key = J * 128 + wave * 32 + acc_row(i, lane);
@@ -563,12 +589,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
       float* pv = dv + (t * g.Hkv + grp) * D;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        pk[dt * 32 + col] = dK[dt][i];
+        pk[dt * 32 + col] = dK[dt][i] * g.scale;
         pv[dt * 32 + col] = dV[dt][i];
       }
       float* pp = dkp + (t * g.Hkv + grp) * DP;
 #pragma unroll
-      for (int dt = 0; dt < DP / 32; ++dt) pp[dt * 32 + col] = dKp[dt][i];
+      for (int dt = 0; dt < DP / 32; ++dt) pp[dt * 32 + col] = dKp[dt][i] * lam_ps;
     }
   }
 }
@@ -609,7 +635,8 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
     { ProfScope _ps("bwd_dq", s);
     hipLaunchKernelGGL((dq_kernel<T, D, DP>), dim3((unsigned)nq), dim3(256), CQ::LDS_BYTES, s,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)qp, (const T*)kp, (const T*)o,
-                       lse, lse_p, (const T*)dout, w.delta, q2k_idx, q2k_cnt, dq, dqp, w.cpart, g); }
+                       lse, lse_p, (const T*)dout, w.delta, w.lse2, w.lsep2, q2k_idx, q2k_cnt, dq, dqp,
+                       w.cpart, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (g.G > 4 && g.T > 0) {
@@ -623,8 +650,8 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
     { ProfScope _ps("bwd_dkdv", s);
 #define MSA_LAUNCH_DKDV(GG)                                                                          \
     hipLaunchKernelGGL((dkdv_kernel<T, D, DP, GG>), dim3((unsigned)nk), dim3(256), CK::LDS_BYTES, s, \
-                       (const T*)q, (const T*)k, (const T*)v, (const T*)qp, (const T*)kp, lse, lse_p,  \
-                       (const T*)dout, w.delta, k2q_ptr, k2q_idx, dk, dv, dkp, g)
+                       (const T*)q, (const T*)k, (const T*)v, (const T*)qp, (const T*)kp, w.lse2,      \
+                       w.lsep2, (const T*)dout, w.delta, k2q_ptr, k2q_idx, dk, dv, dkp, g)
     switch (g.G) {
       case 1: MSA_LAUNCH_DKDV(1); break;
       case 2: MSA_LAUNCH_DKDV(2); break;

@@ -39,7 +39,7 @@ int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Plan {
   msa::Geo g{};
   msa_layout lay{};
-  int64_t off_qb0, off_kb0, off_s0, off_order, off_unit0, off_counts, off_cursor, off_delta,
+  int64_t off_qb0, off_kb0, off_s0, off_order, off_unit0, off_counts, off_cursor, off_delta, off_lse2, off_lsep2,
       off_cpart;
 };
 
@@ -124,6 +124,8 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
   P->off_counts = off; off = align_up(off + 4 * (int64_t)c.heads_kv * nkb);
   P->off_cursor = off; off = align_up(off + 4 * (int64_t)c.heads_kv * nkb);
   P->off_delta = off;  off = align_up(off + 4 * (int64_t)c.heads_q * vl->total_tokens);
+  P->off_lse2 = off;   off = align_up(off + 4 * (int64_t)c.heads_q * vl->total_tokens);
+  P->off_lsep2 = off;  off = align_up(off + 4 * (int64_t)c.heads_kv * vl->total_tokens);
   P->off_cpart = off;
   if (G > 4) off = align_up(off + 4 * (int64_t)c.heads_kv * (G / 4) * vl->total_tokens * c.proxy_dim);
 
@@ -156,6 +158,8 @@ msa_status bind_workspace(Plan* P, void* ws, size_t ws_bytes, msa::Work* w) {
     w->counts = reinterpret_cast<int32_t*>(base + P->off_counts);
     w->cursor = reinterpret_cast<int32_t*>(base + P->off_cursor);
     w->delta = reinterpret_cast<float*>(base + P->off_delta);
+    w->lse2 = reinterpret_cast<float*>(base + P->off_lse2);
+    w->lsep2 = reinterpret_cast<float*>(base + P->off_lsep2);
     w->cpart = reinterpret_cast<float*>(base + P->off_cpart);
   }
   return MSA_OK;

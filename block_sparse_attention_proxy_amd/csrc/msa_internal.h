@@ -31,6 +31,8 @@ struct Work {
   int32_t* counts;                   // [Hkv * nkb]
   int32_t* cursor;                   // [Hkv * nkb]
   float* delta;                      // [Hq * T]       rowsum(dO * O)
+  float* lse2;                       // [Hq * T]       main LSE in log2 units
+  float* lsep2;                      // [Hkv * T]      proxy LSE in log2 units
   float* cpart;                      // [Hkv * nhg * T * DP] proxy-gradient partials (G > 4)
 };
 
