@@ -404,7 +404,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
   // such rows are masked in the compute.  Every wave issues the same number of
   // copies per stage (COPIES, + NPCOPY at a chunk's last head), which the
   // vmcnt waits below rely on.
-  auto issue_stage = [&](int buf, int li, int c, int hl, bool with_qp) __attribute__((always_inline)) {
+  auto issue_stage = [&](int buf, int li, int c, int hl, auto with_qp_c) __attribute__((always_inline)) {
+    constexpr bool with_qp = decltype(with_qp_c)::value;
     const uint32_t base = lds_offset(smem_raw) + buf * C::STAGE_BYTES;
     const int I = lst[li] - qb0;
     const int h = grp * G + hl;
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
       dma16(q + off, base + rfirst * D * (int)sizeof(T));
       dma16(dout + off, base + (C::QS + rfirst * D) * (int)sizeof(T));
     }
-    if (with_qp) {
+    if constexpr (with_qp) {
 #pragma unroll
       for (int j = 0; j < C::NPCOPY; ++j) {
         // with fewer rows than copies, the extra waves repeat the first rows
@@ -465,53 +466,107 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
       mma(S, TQ::row8(Qs, col, ks * 16 + hi * 8), Kf[ks]);
       mma(dP, TQ::row8(dOs, col, ks * 16 + hi * 8), Vf[ks]);
     }
-    // two halves: the products of the first half run while the second
-    // half's exponentials are computed
+    // Two halves (accumulator elements [8kk, 8kk + 8), 16 query rows each).
+    // The operands of both halves are read early; the products of the first
+    // half are interleaved with the exponentials of the second.
+    float lr[2][8], dl[2][8];
+    frag_t<T> bv[2][D / 32], bk[2][D / 32];
+    auto read_half = [&](int kk) __attribute__((always_inline)) {
+      rows8(fl, kk, lr[kk]);
+      rows8(fl + C::QC, kk, dl[kk]);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      float lr[8], dl[8];
-      rows8(fl, kk, lr);
-      rows8(fl + C::QC, kk, dl);
+      for (int dt = 0; dt < D / 32; ++dt) {
+        bv[kk][dt] = TQ::col(dOs, kk * 16, dt * 32, lane);
+        bk[kk][dt] = TQ::col(Qs, kk * 16, dt * 32, lane);
+      }
+    };
+    frag_t<T> ap[2], as[2];
+    auto softmax_half = [&](int kk) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = kk * 8 + j;
-        float p = __builtin_amdgcn_exp2f(fmaf(S[i], g.scale_log2, -lr[j]));
+        float p = __builtin_amdgcn_exp2f(fmaf(S[i], g.scale_log2, -lr[kk][j]));
         if (masked) p = (acc_row(i, lane) >= lo && acc_row(i, lane) < hi_) ? p : 0.f;
+        dP[i] = p * (dP[i] - dl[kk][j]);
         S[i] = p;
-        dP[i] = p * (dP[i] - dl[j]);
         Tacc[i] += p;
       }
-      const frag_t<T> ap = acc_frag<T>(S, kk);
-      const frag_t<T> as = acc_frag<T>(dP, kk);
+      ap[kk] = acc_frag<T>(S, kk);
+      as[kk] = acc_frag<T>(dP, kk);
+    };
+    read_half(0);
+    softmax_half(0);
+    read_half(1);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        mma(dV[dt], ap, TQ::col(dOs, kk * 16, dt * 32, lane));
-        mma(dK[dt], as, TQ::col(Qs, kk * 16, dt * 32, lane));
+    for (int dt = 0; dt < D / 32; ++dt) {
+      mma(dV[dt], ap[0], bv[0][dt]);
+      mma(dK[dt], as[0], bk[0][dt]);
+    }
+    softmax_half(1);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      mma(dV[dt], ap[1], bv[1][dt]);
+      mma(dK[dt], as[1], bk[1][dt]);
+    }
+    if constexpr (D == 128 && sizeof(T) == 2) {
+      // row reads 6 ahead of the S/dP products; the remaining reads (LSE and
+      // D rows, transposed Q/dO fragments) behind the last of them; the
+      // second half's exponentials between the first half's products
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
+#pragma unroll
+      for (int j = 0; j < 10; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
       }
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, 48, 1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
     }
   };
   auto proxy_part = [&](const unsigned char* base, int lo, int hi_, bool masked) __attribute__((always_inline)) {
     const T* Ps = reinterpret_cast<const T*>(base) + 2 * C::QS;
     const float* fl = reinterpret_cast<const float*>(base + C::FL_OFF);
-    f32x16 Y = zero16();
+    __builtin_amdgcn_sched_barrier(0);
+    frag_t<T> ya[DP / 16], yb[DP / 16], bp[2][DP / 32];
+    float lp[2][8];
 #pragma unroll
-    for (int ks = 0; ks < DP / 16; ++ks)
-      mma(Y, TP::row8(Ps, col, ks * 16 + hi * 8), TP::row8(KPs, wave * 32 + col, ks * 16 + hi * 8));
+    for (int ks = 0; ks < DP / 16; ++ks) {
+      ya[ks] = TP::row8(Ps, col, ks * 16 + hi * 8);
+      yb[ks] = TP::row8(KPs, wave * 32 + col, ks * 16 + hi * 8);
+    }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      float lp[8];
-      rows8(fl + 2 * C::QC, kk, lp);
+      rows8(fl + 2 * C::QC, kk, lp[kk]);
+#pragma unroll
+      for (int dt = 0; dt < DP / 32; ++dt) bp[kk][dt] = TP::col(Ps, kk * 16, dt * 32, lane);
+    }
+    f32x16 Y = zero16();
+#pragma unroll
+    for (int ks = 0; ks < DP / 16; ++ks) mma(Y, ya[ks], yb[ks]);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = kk * 8 + j;
-        float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], g.pscale_log2, -lp[j]));
+        float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], g.pscale_log2, -lp[kk][j]));
         if (masked) qv = (acc_row(i, lane) >= lo && acc_row(i, lane) < hi_) ? qv : 0.f;
         Y[i] = fmaf(-invG, Tacc[i], qv);                     // dY / (lam * s_p)
       }
       const frag_t<T> ay = acc_frag<T>(Y, kk);
 #pragma unroll
-      for (int dt = 0; dt < DP / 32; ++dt) mma(dKp[dt], ay, TP::col(Ps, kk * 16, dt * 32, lane));
+      for (int dt = 0; dt < DP / 32; ++dt) mma(dKp[dt], ay, bp[kk][dt]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Stages run in list order over chunks (list entry, 32-query chunk) with the
@@ -527,22 +582,25 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
   const int nchunk_plain_end = tail ? (len - 1) * nch : nchunk;
 
   // stage s = ci * G + hl  ->  (li, c, hl); counters advance incrementally
-  int fli = 0, fc = 0, fhl = 0;           // next stage to issue
+  int fli = 0, fc = 0;                    // list entry and chunk of the next stage to issue
   int fs = 0;                             // its index
   const int nst = nchunk * G;
-  auto issue_next = [&]() __attribute__((always_inline)) {
-    const bool wqp = fhl == G - 1;
-    int li = fli, c = fc, hl = fhl;
-    if (fs >= nst) {                       // past the end: re-read the last stage
-      li = len - 1; c = nch - 1; hl = G - 1;
-    }
-    issue_stage(fs % C::NBUF, li, c, hl, wqp);
+  // The head of the stage issued next is known at compile time (stages go
+  // round the G heads in order); a stage past the end re-reads the last
+  // chunk with the same head, so every wave issues the same copies.
+  auto issue_next = [&](auto hl_c) __attribute__((always_inline)) {
+    constexpr int hl = decltype(hl_c)::value;
+    const bool past = fs >= nst;
+    const int li = past ? len - 1 : fli;
+    const int c = past ? nch - 1 : fc;
+    issue_stage(fs % C::NBUF, li, c, hl, std::integral_constant<bool, hl == G - 1>());
     ++fs;
-    if (++fhl == G) { fhl = 0; if (++fc == nch) { fc = 0; ++fli; } }
+    if (hl == G - 1) { if (++fc == nch) { fc = 0; ++fli; } }
   };
   if (nst > 0) {
-#pragma unroll
-    for (int j = 0; j < C::AHEAD; ++j) issue_next();
+    static_for<C::AHEAD>([&](auto jc) __attribute__((always_inline)) {
+      issue_next(std::integral_constant<int, decltype(jc)::value % G>());
+    });
   }
   int li = 0, c = 0;
   auto chunk_body = [&](int ci, bool masked) __attribute__((always_inline)) {
@@ -562,7 +620,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
       }();
       wait_vmcnt<later>();
       __syncthreads();
-      issue_next();
+      issue_next(std::integral_constant<int, (hl + C::AHEAD) % G>());
+      __builtin_amdgcn_sched_barrier(0);
       const int s = ci * G + hl;
       const unsigned char* base = smem_raw + (s % C::NBUF) * C::STAGE_BYTES;
       main_part(base, lo, hi_, masked);
