@@ -78,12 +78,14 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
+_HDR = ["block_sparse_attention_proxy_amd/csrc/msa_device.h", "block_sparse_attention_proxy_amd/csrc/msa_internal.h"]
 KERNEL_SOURCES = {
-    "proxy_scores": ["block_sparse_attention_proxy_amd/csrc/select.hip"],
-    "select": ["block_sparse_attention_proxy_amd/csrc/select.hip"],
-    "fwd": ["block_sparse_attention_proxy_amd/csrc/attn_fwd.hip"],
-    "bwd_dq": ["block_sparse_attention_proxy_amd/csrc/attn_bwd.hip"],
-    "bwd_dkdv": ["block_sparse_attention_proxy_amd/csrc/attn_bwd.hip"],
+    "proxy_scores": ["block_sparse_attention_proxy_amd/csrc/select.hip"] + _HDR,
+    "select": ["block_sparse_attention_proxy_amd/csrc/select.hip"] + _HDR,
+    "fwd": ["block_sparse_attention_proxy_amd/csrc/attn_fwd.hip"] + _HDR,
+    "proxy_lse": ["block_sparse_attention_proxy_amd/csrc/attn_fwd.hip"] + _HDR,
+    "bwd_dq": ["block_sparse_attention_proxy_amd/csrc/attn_bwd.hip"] + _HDR,
+    "bwd_dkdv": ["block_sparse_attention_proxy_amd/csrc/attn_bwd.hip"] + _HDR,
 }
 
 
@@ -153,6 +155,20 @@ def cpu_baseline(w, seqlens, x, budget_s, seed):
                       f"{dt:.1f} s wall", "seconds": dt}
 
 
+def calibrate_copy(mib):
+    """A plain copy kernel of known size: reads and writes mib MiB per launch."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n, "launches": 4}))
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,7 +178,12 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--report", default=None, help="also write the JSON (plus details) here")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of this many MiB, 4 times (the "
+                         "known-size reference for scaling HBM byte counters), then exit")
     a = ap.parse_args(argv)
+    if a.calibrate_copy:
+        return calibrate_copy(a.calibrate_copy)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (this path has no "
               "multi-GPU mode: each GPU would run the same op on its own documents).", file=sys.stderr)
