@@ -33,8 +33,10 @@
  *   - Block ids in q2k_idx / k2q_idx are global: document offset + local index.
  *   - Query head h uses KV group h / (Hq / Hkv).
  *   - All device pointers are caller-owned device memory, 16-byte aligned.
- *     The library allocates no device memory and keeps no state besides a
- *     thread-local error message.  Work is enqueued asynchronously on
+ *     The library allocates no device memory.  Its only state is a
+ *     thread-local error message, a per-device record that the kernels' LDS
+ *     limits were raised, and (only after msa_profile_enable) a thread-local
+ *     pool of timing events.  Work is enqueued asynchronously on
  *     `stream` (a hipStream_t; NULL = default stream); the caller keeps every
  *     buffer alive until that work completes.  Outputs are overwritten.
  *   - Errors: every argument is checked on the host before anything is
