@@ -111,9 +111,9 @@ __global__ __launch_bounds__(256) void dq_kernel(
   // Copy stage s (clamped to the last) into ring slot s % NBUF.  Key rows past
   // the document end are clamped to its last row; they only occur in the
   // diagonal block, where the causal mask removes them.
-  auto issue = [&](int s) __attribute__((always_inline)) {
+  auto issue = [&](int s, int slot) __attribute__((always_inline)) {
     const int ss = s < nst ? s : nst - 1;
-    const uint32_t base = lds_offset(smem_raw) + (s % C::NBUF) * C::STAGE_BYTES;
+    const uint32_t base = lds_offset(smem_raw) + slot * C::STAGE_BYTES;
     const int key0 = (sel[ss >> 1] - kb0) * 128 + (ss & 1) * C::KC;
 #pragma unroll
     for (int j = 0; j < C::NKCOPY; ++j) {
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
   // loop (the vmcnt waits there count only them).
   wait_vmcnt<0>();
 #pragma unroll
-  for (int j = 0; j < C::AHEAD; ++j) issue(j);
+  for (int j = 0; j < C::AHEAD; ++j) issue(j, j);
 
   // dQ^T, and the proxy terms kept apart: Cq^T += kp^T Q^T over the tiles this
   // head is assigned, Cp^T += kp^T P^T over every tile; the head's share of
@@ -177,39 +177,157 @@ __global__ __launch_bounds__(256) void dq_kernel(
 #pragma unroll
   for (int dt = 0; dt < DP / 32; ++dt) { Cq[dt] = zero16(); Cp[dt] = zero16(); }
 
-  // one 32-key tile of a stage; key row r is visible iff r <= lim
-  auto tile = [&](const T* Ks, const T* Vs, const T* KPs, int kt, int lim, bool masked,
-                  bool assigned) __attribute__((always_inline)) {
-    f32x16 S = zero16(), dP = zero16();
+  // One stage: two 32-key tiles.  Key row r of tile kt is visible to this
+  // lane's query iff r <= qpos - (first key of the tile); only the diagonal
+  // block's stages are masked.
+  //
+  // The main work of a stage is a fixed sequence of MFMAs, each with one
+  // operand read from LDS: S and dP of tile 0 (NA products: K and V rows),
+  // the same for tile 1, then dQ and the proxy term C_p of tile 0 (NB
+  // products: K^T and kp^T fragments), then of tile 1.  It is issued in that
+  // order with every LDS read LOOK products ahead of its use, tile 0's
+  // softmax spread between tile 1's S/dP products and tile 1's between tile
+  // 0's dQ products; scheduling fences keep that order.  The proxy term Q kp
+  // of a tile is computed by the one head it is assigned to, at the end.
+  // Byte offsets of this lane's LDS reads inside a stage, for the first tile
+  // and half (the swizzle depends on the row modulo 16 only, so other tiles
+  // and halves are constant offsets from these): row fragments of K/V (per
+  // 16-column step), the two transpose reads of a K^T and a kp^T fragment
+  // (per 32-column block), and row fragments of kp.
+  uint32_t oRow[D / 16], oColK[D / 32][2], oColP[DP / 32][2];
+  {
+    const int s16 = lane & 15, g4 = lane >> 4;
+    const int tr_r = hi * 4 + (s16 >> 2), tr_c = 16 * (g4 & 1) + 4 * (s16 & 3);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      mma(S, TK::row8(Ks, kt * 32 + col, ks * 16 + hi * 8), Qf[ks]);
-      mma(dP, TK::row8(Vs, kt * 32 + col, ks * 16 + hi * 8), dOf[ks]);
+    for (int ks = 0; ks < D / 16; ++ks) oRow[ks] = TK::off(col, ks * 16 + hi * 8) * (int)sizeof(T);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      oColK[dt][0] = TK::off(tr_r, dt * 32 + tr_c) * (int)sizeof(T);
+      oColK[dt][1] = TK::off(tr_r + 8, dt * 32 + tr_c) * (int)sizeof(T);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float p = __builtin_amdgcn_exp2f(fmaf(S[i], g.scale_log2, -lse2));
-      if (masked) p = acc_row(i, lane) <= lim ? p : 0.f;
-      S[i] = p;
-      dP[i] = p * (dP[i] - dl);
+    for (int dt = 0; dt < DP / 32; ++dt) {
+      oColP[dt][0] = TP::off(tr_r, dt * 32 + tr_c) * (int)sizeof(T);
+      oColP[dt][1] = TP::off(tr_r + 8, dt * 32 + tr_c) * (int)sizeof(T);
     }
+  }
+  constexpr int NA = 2 * (D / 16);                 // S and dP products per tile
+  constexpr int NB = 2 * (D / 32 + DP / 32);       // dQ and C_p products per tile
+  constexpr int NM = 2 * NA + 2 * NB;
+  constexpr int LOOK = 4;
+  auto stage_body = [&](int s, auto masked_c) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    wait_vmcnt<C::COPIES * (C::AHEAD - 1)>();
+    __syncthreads();
+    issue(s + C::AHEAD, (s + C::AHEAD) % C::NBUF);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!active) return;
+    const T* Ks = reinterpret_cast<const T*>(smem_raw + (s % C::NBUF) * C::STAGE_BYTES);
+    const T* Vs = Ks + C::KS;
+    const T* KPs = Vs + C::KS;
+    const int lim0 = qpos - ((sel[s >> 1] - kb0) * 128 + (s & 1) * C::KC);
+    f32x16 S[2], dP[2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const frag_t<T> bs = acc_frag<T>(dP, kk);
-      const frag_t<T> bp = acc_frag<T>(S, kk);
+    for (int kt = 0; kt < 2; ++kt) { S[kt] = zero16(); dP[kt] = zero16(); }
+    frag_t<T> bs[2][2], bp[2][2];                  // [tile][half] softmax outputs as operands
+    frag_t<T> opnd[NM];
+    // this stage's read bases: slot base + lane offset, one add each
+    uint32_t aRow[D / 16], aColK[D / 32][2], aColP[DP / 32][2];
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t sb = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)(lds_offset(smem_raw) + (s % C::NBUF) * C::STAGE_BYTES));
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) mma(dQ[dt], TK::col(Ks, kt * 32 + kk * 16, dt * 32, lane), bs);
+      for (int ks = 0; ks < D / 16; ++ks) aRow[ks] = lds_base_add(sb, oRow[ks]);
 #pragma unroll
-      for (int dt = 0; dt < DP / 32; ++dt) mma(Cp[dt], TP::col(KPs, kt * 32 + kk * 16, dt * 32, lane), bp);
+      for (int dt = 0; dt < D / 32; ++dt) {
+        aColK[dt][0] = lds_base_add(sb, oColK[dt][0]);
+        aColK[dt][1] = lds_base_add(sb, oColK[dt][1]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DP / 32; ++dt) {
+        aColP[dt][0] = lds_base_add(sb, oColP[dt][0]);
+        aColP[dt][1] = lds_base_add(sb, oColP[dt][1]);
+      }
     }
-    if (assigned) {
+    auto operand = [&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (sizeof(T) == 2) {
+        // tile, half and tensor offsets are constants on the stage's bases
+        if constexpr (m < 2 * NA) {
+          constexpr int kt = m / NA, j = m % NA, ks = j / 2;
+          constexpr int cst = ((j & 1) ? C::KS : 0) * 2 + kt * 32 * D * 2;
+          opnd[m] = lds_ld8<cst>(aRow[ks]);
+        } else {
+          constexpr int r = m - 2 * NA, kt = r / NB, kk = (r % NB) / (NB / 2), c = (r % NB) % (NB / 2);
+          if constexpr (c < D / 32) {
+            constexpr int cst = (kt * 32 + kk * 16) * D * 2;
+            opnd[m] = tr_pair_at<cst>(aColK[c][0], aColK[c][1]);
+          } else {
+            constexpr int cst = 2 * C::KS * 2 + (kt * 32 + kk * 16) * DP * 2;
+            opnd[m] = tr_pair_at<cst>(aColP[c - D / 32][0], aColP[c - D / 32][1]);
+          }
+        }
+      } else if constexpr (m < 2 * NA) {
+        constexpr int kt = m / NA, j = m % NA, ks = j / 2;
+        opnd[m] = TK::row8((j & 1) ? Vs : Ks, kt * 32 + col, ks * 16 + hi * 8);
+      } else {
+        constexpr int r = m - 2 * NA, kt = r / NB, kk = (r % NB) / (NB / 2), c = (r % NB) % (NB / 2);
+        if constexpr (c < D / 32) opnd[m] = TK::col(Ks, kt * 32 + kk * 16, c * 32, lane);
+        else opnd[m] = TP::col(KPs, kt * 32 + kk * 16, (c - D / 32) * 32, lane);
+      }
+    };
+    auto product = [&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < 2 * NA) {
+        constexpr int kt = m / NA, j = m % NA, ks = j / 2;
+        if constexpr (j & 1) mma(dP[kt], opnd[m], dOf[ks]);
+        else mma(S[kt], opnd[m], Qf[ks]);
+      } else {
+        constexpr int r = m - 2 * NA, kt = r / NB, kk = (r % NB) / (NB / 2), c = (r % NB) % (NB / 2);
+        if constexpr (c < D / 32) mma(dQ[c], opnd[m], bs[kt][kk]);
+        else mma(Cp[c - D / 32], opnd[m], bp[kt][kk]);
+      }
+    };
+    auto soft = [&](int kt, int i) __attribute__((always_inline)) {
+      float p = __builtin_amdgcn_exp2f(fmaf(S[kt][i], g.scale_log2, -lse2));
+      if (MASKED) p = acc_row(i, lane) <= lim0 - kt * 32 ? p : 0.f;
+      S[kt][i] = p;
+      dP[kt][i] = p * (dP[kt][i] - dl);
+    };
+    auto pack = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) { bs[kt][kk] = acc_frag<T>(dP[kt], kk); bp[kt][kk] = acc_frag<T>(S[kt], kk); }
+    };
+    static_for<LOOK>([&](auto mc) __attribute__((always_inline)) { operand(mc); });
+    static_for<NM>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      product(mc);
+      if constexpr (m + LOOK < NM) operand(std::integral_constant<int, m + LOOK>());
+      // tile 0's 16 softmax elements over tile 1's S/dP products, tile 1's
+      // over tile 0's dQ products
+      if constexpr (m >= NA && m < 2 * NA) {
+        constexpr int e0 = (m - NA) * 16 / NA, e1 = (m - NA + 1) * 16 / NA;
+#pragma unroll
+        for (int i = e0; i < e1; ++i) soft(0, i);
+        if constexpr (m == 2 * NA - 1) pack(0);
+      } else if constexpr (m >= 2 * NA && m < 2 * NA + NB) {
+        constexpr int e0 = (m - 2 * NA) * 16 / NB, e1 = (m - 2 * NA + 1) * 16 / NB;
+#pragma unroll
+        for (int i = e0; i < e1; ++i) soft(1, i);
+        if constexpr (m == 2 * NA + NB - 1) pack(1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      if (((s * 2 + kt) % g.G) != hl) continue;
       f32x16 Y = zero16();
 #pragma unroll
       for (int ks = 0; ks < DP / 16; ++ks) mma(Y, TP::row8(KPs, kt * 32 + col, ks * 16 + hi * 8), QPf[ks]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], g.pscale_log2, -lsep2));
-        if (masked) qv = acc_row(i, lane) <= lim ? qv : 0.f;
+        if (MASKED) qv = acc_row(i, lane) <= lim0 - kt * 32 ? qv : 0.f;
         Y[i] = qv;
       }
 #pragma unroll
@@ -220,24 +338,10 @@ __global__ __launch_bounds__(256) void dq_kernel(
       }
     }
   };
-  auto stage_body = [&](int s, bool masked) __attribute__((always_inline)) {
-    wait_vmcnt<C::COPIES * (C::AHEAD - 1)>();
-    __syncthreads();
-    issue(s + C::AHEAD);
-    const T* Ks = reinterpret_cast<const T*>(smem_raw + (s % C::NBUF) * C::STAGE_BYTES);
-    const T* Vs = Ks + C::KS;
-    const T* KPs = Vs + C::KS;
-    const int kpos0 = (sel[s >> 1] - kb0) * 128 + (s & 1) * C::KC;
-    if (active) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-        tile(Ks, Vs, KPs, kt, qpos - (kpos0 + kt * 32), masked, ((s * 2 + kt) % g.G) == hl);
-    }
-  };
 
   int s = 0;
-  for (; s < nst_plain; ++s) stage_body(s, false);
-  for (; s < nst; ++s) stage_body(s, true);
+  for (; s < nst_plain; ++s) stage_body(s, std::integral_constant<bool, false>());
+  for (; s < nst; ++s) stage_body(s, std::integral_constant<bool, true>());
   wait_vmcnt<0>();
   __syncthreads();
   f32x16 Cd[DP / 32];
@@ -674,18 +778,14 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
                                float* dkp, const Work& w, hipStream_t s) {
   typedef DqCfg<T, D, DP> CQ;
   typedef KvCfg<T, D, DP> CK;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)dq_kernel<T, D, DP>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, CQ::LDS_BYTES);
+  static LdsLimitOnce lds_limit;
+  {
+    const hipError_t e = lds_limit.ensure({{(const void*)dq_kernel<T, D, DP>, CQ::LDS_BYTES},
+                                           {(const void*)dkdv_kernel<T, D, DP, 1>, CK::LDS_BYTES},
+                                           {(const void*)dkdv_kernel<T, D, DP, 2>, CK::LDS_BYTES},
+                                           {(const void*)dkdv_kernel<T, D, DP, 4>, CK::LDS_BYTES},
+                                           {(const void*)dkdv_kernel<T, D, DP, 8>, CK::LDS_BYTES}});
     if (e != hipSuccess) return e;
-    const void* fns[] = {(const void*)dkdv_kernel<T, D, DP, 1>, (const void*)dkdv_kernel<T, D, DP, 2>,
-                         (const void*)dkdv_kernel<T, D, DP, 4>, (const void*)dkdv_kernel<T, D, DP, 8>};
-    for (const void* f : fns) {
-      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, CK::LDS_BYTES);
-      if (e != hipSuccess) return e;
-    }
-    attr = true;
   }
   hipError_t e;
   const int NU = g.G * (g.Bq / 32);

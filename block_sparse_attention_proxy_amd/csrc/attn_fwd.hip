@@ -397,12 +397,10 @@ static hipError_t fwd_dispatch(const Geo& g, const void* q, const void* k, const
   constexpr int QT = 2;
   typedef FwdCfg<T, D, DP, QT> C;
   auto fn = fwd_kernel<T, D, DP, QT>;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       C::LDS_BYTES);
+  static LdsLimitOnce lds_limit;
+  {
+    const hipError_t e = lds_limit.ensure({{(const void*)fn, C::LDS_BYTES}});
     if (e != hipSuccess) return e;
-    attr = true;
   }
   const int NU = g.G * (g.Bq / (32 * QT));
   const int64_t nblk = (int64_t)g.Hkv * g.nqb * ((NU + 3) / 4);

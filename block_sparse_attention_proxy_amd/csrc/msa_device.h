@@ -116,6 +116,39 @@ __device__ __forceinline__ bf16x4 lds_tr4(const bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// LDS reads at a 32-bit LDS byte address plus a compile-time offset.  The
+// base is meant to come from lds_base_add(): an add the compiler cannot take
+// apart, so that every read of a stage reuses the same base register and the
+// constant lands in the instruction's offset field.
+__device__ __forceinline__ uint32_t lds_base_add(uint32_t uniform_base, uint32_t lane_off) {
+  uint32_t r;
+  asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(uniform_base), "v"(lane_off));
+  return r;
+}
+typedef __attribute__((address_space(3))) const unsigned char lds_u8;
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_ld8(uint32_t base) {
+  typedef __attribute__((address_space(3))) const bf16x8 lds_v8;
+  return *reinterpret_cast<lds_v8*>(reinterpret_cast<lds_u8*>((uintptr_t)base) + OFF);
+}
+template <int OFF>
+__device__ __forceinline__ bf16x4 lds_tr4_at(uint32_t base) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(reinterpret_cast<lds_u8*>((uintptr_t)base) + OFF));
+  return __builtin_bit_cast(bf16x4, v);
+}
+// Two transpose reads (the rows of an accumulator-slot fragment and the rows
+// 8 further down) joined into one fragment.
+template <int OFF>
+__device__ __forceinline__ bf16x8 tr_pair_at(uint32_t a, uint32_t b) {
+  const bf16x4 x = lds_tr4_at<OFF>(a), y = lds_tr4_at<OFF>(b);
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { r[j] = x[j]; r[j + 4] = y[j]; }
+  return r;
+}
+
 // Operand fragment in accumulator slots read from a row-major LDS tile X
 // (ld elements per row) whose rows are the contraction index: lane l gets
 // column n0 + (l & 31) and rows k0 + ((j >> 2) << 3) + ((l >> 5) << 2) + (j & 3)

@@ -4,7 +4,33 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <initializer_list>
+#include <utility>
+
 namespace msa {
+
+// Raises the dynamic-LDS limit of a set of kernels once per device (the first
+// launch on each device does it; later launches skip it).  Thread-safe: a
+// race only repeats the idempotent attribute call.  Devices past the table
+// size are handled on every call.
+struct LdsLimitOnce {
+  static constexpr int MAX_DEV = 64;
+  std::atomic<unsigned char> done[MAX_DEV] = {};
+  hipError_t ensure(std::initializer_list<std::pair<const void*, int>> kernels) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < MAX_DEV;
+    if (cached && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+    for (const auto& k : kernels) {
+      e = hipFuncSetAttribute(k.first, hipFuncAttributeMaxDynamicSharedMemorySize, k.second);
+      if (e != hipSuccess) return e;
+    }
+    if (cached) done[dev].store(1, std::memory_order_release);
+    return hipSuccess;
+  }
+};
 
 // Geometry of one call, resolved on the host and passed to every kernel by value.
 struct Geo {
