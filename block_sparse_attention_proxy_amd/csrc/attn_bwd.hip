@@ -31,11 +31,6 @@ __device__ __forceinline__ int xcd_remap_b(int i, int n) {
   return x * per + (x < rem ? x : rem) + k;
 }
 
-__device__ __forceinline__ int find_doc(const int32_t* a, int n, int x) {
-  int lo = 0, hi = n;
-  while (hi - lo > 1) { int mid = (lo + hi) >> 1; if (a[mid] <= x) lo = mid; else hi = mid; }
-  return lo;
-}
 
 // ---------------------------------------------------------------------------
 // dQ kernel: a workgroup serves (group, query block, 4 units); a wave owns 32
@@ -89,7 +84,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
   const bool active = u < NU;
   const int hl = u % g.G, chunk = u / g.G;
   const int h = grp * g.G + hl;
-  const int b = find_doc(g.qb0, g.B, QB);
+  const int b = g.qdoc[QB];
   const int I = QB - g.qb0[b];
   const int t0 = g.cu[b];
   const int L = g.cu[b + 1] - t0;
@@ -463,7 +458,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
   const int bid = xcd_remap_b(blockIdx.x, gridDim.x);
   const int grp = bid / g.nkb;
   const int KB = bid % g.nkb;
-  const int b = find_doc(g.kb0, g.B, KB);
+  const int b = g.kdoc[KB];
   const int J = KB - g.kb0[b];
   const int t0 = g.cu[b];
   const int L = g.cu[b + 1] - t0;
@@ -734,10 +729,73 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
     Tacc = zero16();
     if (++c == nch) { c = 0; ++li; }
   };
+  // More than 4 heads: the heads of a chunk go in quads through a loop that is
+  // not unrolled, so the stage code exists once per ring slot (stage s sits in
+  // slot s % 4 = its head % 4).  Only the last quad carries the chunk's last
+  // head: its qp copy, the extra copies the waits of its neighbours allow for,
+  // and the proxy term are taken on a uniform branch.
+  auto issue_next_rt = [&](int hl, auto with_qp_c) __attribute__((always_inline)) {
+    constexpr bool with_qp = decltype(with_qp_c)::value;
+    const bool past = fs >= nst;
+    const int li_ = past ? len - 1 : fli;
+    const int c_ = past ? nch - 1 : fc;
+    issue_stage(fs % C::NBUF, li_, c_, hl, with_qp_c);
+    ++fs;
+    if constexpr (with_qp) {                     // branch-free, so the counters stay in registers
+      const bool wrap = fc + 1 == nch;
+      fli += wrap ? 1 : 0;
+      fc = wrap ? 0 : fc + 1;
+    }
+  };
+  auto chunk_body_quads = [&](bool masked) __attribute__((always_inline)) {
+    const int I = lst[li] - qb0;
+    const int qpos0 = I * g.Bq + c * 32;
+    const int lo = kpos - qpos0, hi_ = L - qpos0;
+    constexpr int NQ = G / 4;
+    constexpr int BASE_LATER = (C::AHEAD - 1) * C::COPIES;
+#pragma unroll 1
+    for (int hq = 0; hq < NQ; ++hq) {
+      const bool lastq = hq == NQ - 1;
+      static_for<4>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        // stages s + 1 and s + 2 are in flight; one of them is the chunk's
+        // last head (with its qp copy) when j is 1 or 2 in the last quad
+        if constexpr (j == 1 || j == 2) {
+          if (lastq) wait_vmcnt<BASE_LATER + C::NPCOPY>();
+          else wait_vmcnt<BASE_LATER>();
+        } else {
+          wait_vmcnt<BASE_LATER>();
+        }
+        __syncthreads();
+        if constexpr (j == 0) {
+          if (lastq) issue_next_rt(G - 1, std::true_type());
+          else issue_next_rt(hq * 4 + 3, std::false_type());
+        } else {
+          const int hn = hq * 4 + j + 3;
+          issue_next_rt(hn < G ? hn : hn - G, std::false_type());
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned char* base = smem_raw + j * C::STAGE_BYTES;
+        main_part(base, lo, hi_, masked);
+        if constexpr (j == 3) {
+          if (lastq) proxy_part(base, lo, hi_, masked);
+        }
+      });
+    }
+    Tacc = zero16();
+    const bool wrap = c + 1 == nch;
+    li += wrap ? 1 : 0;
+    c = wrap ? 0 : c + 1;
+  };
+  auto run_chunk = [&](int ci, bool masked) __attribute__((always_inline)) {
+    if constexpr (G > 4) chunk_body_quads(masked);
+    else chunk_body(ci, masked);
+  };
+  static_assert(G <= 4 || (G % 4 == 0 && C::NBUF == 4 && C::AHEAD == 3), "head quads");
   int ci = 0;
-  for (; ci < nchunk_lead && ci < nchunk; ++ci) chunk_body(ci, true);
-  for (; ci < nchunk_plain_end; ++ci) chunk_body(ci, false);
-  for (; ci < nchunk; ++ci) chunk_body(ci, true);
+  for (; ci < nchunk_lead && ci < nchunk; ++ci) run_chunk(ci, true);
+  for (; ci < nchunk_plain_end; ++ci) run_chunk(ci, false);
+  for (; ci < nchunk; ++ci) run_chunk(ci, true);
   // copies issued past the last stage must land before the workgroup ends
   wait_vmcnt<0>();
 

@@ -84,12 +84,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(
   const int hl = u % g.G, chunk = u / g.G;
   const int h = grp * g.G + hl;
 
-  int b;
-  {
-    int lo = 0, hi_ = g.B;
-    while (hi_ - lo > 1) { int mid = (lo + hi_) >> 1; if (g.qb0[mid] <= QB) lo = mid; else hi_ = mid; }
-    b = lo;
-  }
+  const int b = g.qdoc[QB];
   const int I = QB - g.qb0[b];
   const int t0 = g.cu[b];
   const int L = g.cu[b + 1] - t0;
@@ -333,9 +328,7 @@ __global__ __launch_bounds__(256) void proxy_lse_kernel(const T* __restrict__ qp
   const int c = wave % nwq;
   const int grp = (int)(item / g.nqb);
   const int QB = (int)(item % g.nqb);
-  int lo = 0, hi_ = g.B;
-  while (hi_ - lo > 1) { int mid = (lo + hi_) >> 1; if (g.qb0[mid] <= QB) lo = mid; else hi_ = mid; }
-  const int b = lo;
+  const int b = g.qdoc[QB];
   const int I = QB - g.qb0[b];
   const int t0 = g.cu[b];
   const int L = g.cu[b + 1] - t0;

@@ -39,7 +39,7 @@ int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Plan {
   msa::Geo g{};
   msa_layout lay{};
-  int64_t off_qb0, off_kb0, off_s0, off_order, off_unit0, off_counts, off_cursor, off_delta, off_lse2, off_lsep2,
+  int64_t off_qb0, off_kb0, off_s0, off_order, off_unit0, off_qdoc, off_kdoc, off_counts, off_cursor, off_delta, off_lse2, off_lsep2,
       off_cpart;
 };
 
@@ -121,6 +121,8 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
   P->off_s0 = off;     off = align_up(off + 8 * (B + 1));
   P->off_order = off;  off = align_up(off + 4 * B);
   P->off_unit0 = off;  off = align_up(off + 4 * (B + 1));
+  P->off_qdoc = off;   off = align_up(off + 4 * nqb);
+  P->off_kdoc = off;   off = align_up(off + 4 * nkb);
   P->off_counts = off; off = align_up(off + 4 * (int64_t)c.heads_kv * nkb);
   P->off_cursor = off; off = align_up(off + 4 * (int64_t)c.heads_kv * nkb);
   P->off_delta = off;  off = align_up(off + 4 * (int64_t)c.heads_q * vl->total_tokens);
@@ -154,6 +156,8 @@ msa_status bind_workspace(Plan* P, void* ws, size_t ws_bytes, msa::Work* w) {
   P->g.s0 = reinterpret_cast<int64_t*>(base + P->off_s0);
   P->g.order = reinterpret_cast<int32_t*>(base + P->off_order);
   P->g.unit0 = reinterpret_cast<int32_t*>(base + P->off_unit0);
+  P->g.qdoc = reinterpret_cast<int32_t*>(base + P->off_qdoc);
+  P->g.kdoc = reinterpret_cast<int32_t*>(base + P->off_kdoc);
   if (w) {
     w->counts = reinterpret_cast<int32_t*>(base + P->off_counts);
     w->cursor = reinterpret_cast<int32_t*>(base + P->off_cursor);

@@ -50,6 +50,8 @@ struct Geo {
   int64_t* s0;                       // [B + 1] score-rectangle offset
   int32_t* order;                    // [B]     documents by length, longest first
   int32_t* unit0;                    // [B + 1] first scoring unit, in that order
+  int32_t* qdoc;                     // [nqb] document of each global query block
+  int32_t* kdoc;                     // [nkb] document of each global KV block
 };
 
 // Workspace regions (byte offsets are computed by the host layout routine).

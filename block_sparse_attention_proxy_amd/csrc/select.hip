@@ -110,10 +110,30 @@ __global__ __launch_bounds__(256) void meta_kernel(Geo g) {
   }
 }
 
+// Document of every global query block and KV block, so that kernels find
+// their document with one load instead of a search over the document table.
+__global__ __launch_bounds__(256) void docmap_kernel(Geo g) {
+  const int64_t n = (int64_t)g.nqb + g.nkb;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    if (e < g.nqb) g.qdoc[e] = find_segment<int32_t>(g.qb0, g.B, (int32_t)e);
+    else g.kdoc[e - g.nqb] = find_segment<int32_t>(g.kb0, g.B, (int32_t)(e - g.nqb));
+  }
+}
+
 hipError_t launch_meta(const Geo& g, hipStream_t s) {
   { ProfScope _ps("meta", s);
-  hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(256), 0, s, g);
-  return hipGetLastError(); }
+  hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(256), 0, s, g); }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)g.nqb + g.nkb;
+  if (n > 0) {
+    { ProfScope _ps("meta", s);
+    hipLaunchKernelGGL(docmap_kernel, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)),
+                       dim3(256), 0, s, g); }
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 // ---------------------------------------------------------------------------
@@ -264,6 +284,61 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Orders LDS traffic inside one wave (each wave owns its histogram, so no
+// workgroup barrier is needed).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Second half of an 8-bit radix step of the selection: given the wave's
+// histogram h of the digit at `shift` (over the keys matching prefix under
+// pmask), find the digit of the rem-th largest key.  Returns that bin's
+// count; updates prefix, pmask and rem.
+__device__ __forceinline__ uint32_t radix_scan(uint32_t* h, int lane, int shift, uint32_t& prefix,
+                                               uint32_t& pmask, int& rem) {
+  wave_lds_sync();
+  const uint32_t h0 = h[4 * lane + 0], h1 = h[4 * lane + 1], h2 = h[4 * lane + 2], h3 = h[4 * lane + 3];
+  const int c = (int)(h0 + h1 + h2 + h3);
+  int incl = c;                                   // inclusive suffix sum over lanes >= lane
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_down(incl, o, 64);
+    if (lane + o < 64) incl += t;
+  }
+  int above = incl - c;                           // count in bins of higher lanes
+  int found = -1, newrem = 0;
+  uint32_t cnt = 0;
+  const uint32_t hb[4] = {h0, h1, h2, h3};
+#pragma unroll
+  for (int q = 3; q >= 0; --q) {
+    if (found < 0 && above < rem && rem <= above + (int)hb[q]) { found = q; newrem = rem - above; cnt = hb[q]; }
+    above += (int)hb[q];
+  }
+  const uint64_t m = __ballot(found >= 0);
+  const int src = __ffsll((unsigned long long)m) - 1;
+  const int digit = __shfl(4 * lane + found, src, 64);
+  rem = __shfl(newrem, src, 64);
+  prefix |= (uint32_t)digit << shift;
+  pmask |= 255u << shift;
+  const uint32_t bin = (uint32_t)__shfl((int)cnt, src, 64);
+  wave_lds_sync();
+  return bin;
+}
+__device__ __forceinline__ void hist_clear(uint32_t* h, int lane) {
+  for (int i = lane; i < 256; i += 64) h[i] = 0;
+  wave_lds_sync();
+}
+
+// Selection: one wave per (group, query block).  The (k-1)-th largest
+// candidate key is found by 8-bit radix steps; candidates above it are taken,
+// and among keys equal to it the lowest block indices.  Rows of up to
+// 64 * SEL_REG candidates are read once into registers; the radix starts at
+// the highest bit where the row's keys differ and stops as soon as the bin
+// holding the (k-1)-th key is taken whole.  Longer rows re-read the scores in
+// every step.
+constexpr int SEL_REG = 32;
+
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ scores,
                                                      int32_t* __restrict__ q2k_idx,
                                                      int32_t* __restrict__ q2k_cnt, Geo g) {
@@ -271,86 +346,108 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  const bool active = row < (int64_t)g.Hkv * g.nqb;
-  int grp = 0, QB = 0, b = 0, I = 0, diag = 0, nk = 0, kb0 = 0, ncand = 0, rem = 0, full = 1;
-  const float* srow = nullptr;
-  if (active) {
-    grp = (int)(row / g.nqb);
-    QB = (int)(row % g.nqb);
-    b = find_segment<int32_t>(g.qb0, g.B, QB);
-    I = QB - g.qb0[b];
-    const int L = g.cu[b + 1] - g.cu[b];
-    nk = (L + 127) >> 7;
-    kb0 = g.kb0[b];
-    diag = (I * g.Bq) >> 7;
-    full = (diag + 1) <= g.topk + g.lw;
-    if (!full) {
-      ncand = diag - g.lw;
-      rem = g.topk - 1;
-      srow = scores + (int64_t)grp * g.score_elems + g.s0[b] + (int64_t)I * nk;
-    }
-  }
-  uint32_t prefix = 0, pmask = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = lane; i < 256; i += 64) hist[wave][i] = 0;
-    __syncthreads();
-    if (rem > 0) {
-      for (int j = lane; j < ncand; j += 64) {
-        uint32_t key = order_key(srow[j]);
-        if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
-      }
-    }
-    __syncthreads();
-    if (rem > 0) {
-      uint32_t h0 = hist[wave][4 * lane + 0], h1 = hist[wave][4 * lane + 1];
-      uint32_t h2 = hist[wave][4 * lane + 2], h3 = hist[wave][4 * lane + 3];
-      int c = (int)(h0 + h1 + h2 + h3);
-      int incl = c;  // inclusive suffix sum over lanes >= lane
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        int t = __shfl_down(incl, o, 64);
-        if (lane + o < 64) incl += t;
-      }
-      int above = incl - c;     // count in bins of higher lanes
-      int found = -1, newrem = 0;
-      uint32_t hb[4] = {h0, h1, h2, h3};
-#pragma unroll
-      for (int q = 3; q >= 0; --q) {
-        if (found < 0 && above < rem && rem <= above + (int)hb[q]) { found = q; newrem = rem - above; }
-        above += (int)hb[q];
-      }
-      uint64_t m = __ballot(found >= 0);
-      int src = __ffsll((unsigned long long)m) - 1;
-      int digit = __shfl(4 * lane + found, src, 64);
-      rem = __shfl(newrem, src, 64);
-      prefix |= (uint32_t)digit << shift;
-      pmask |= 255u << shift;
-    }
-  }
-  if (!active) return;
+  if (row >= (int64_t)g.Hkv * g.nqb) return;      // no workgroup barriers in this kernel
+  const int grp = (int)(row / g.nqb);
+  const int QB = (int)(row % g.nqb);
+  const int b = g.qdoc[QB];
+  const int I = QB - g.qb0[b];
+  const int L = g.cu[b + 1] - g.cu[b];
+  const int nk = (L + 127) >> 7;
+  const int kb0 = g.kb0[b];
+  const int diag = (I * g.Bq) >> 7;
   int32_t* out = q2k_idx + ((int64_t)grp * g.nqb + QB) * g.stride;
+  uint32_t* h = hist[wave];
   int pos = 0;
-  if (full) {
+  if ((diag + 1) <= g.topk + g.lw) {              // every block up to the diagonal
     for (int j = lane; j <= diag; j += 64) out[j] = kb0 + j;
     pos = diag + 1;
   } else {
-    const uint32_t theta = prefix;
-    int eq_taken = 0;
-    for (int base = 0; base < ncand; base += 64) {
-      const int j = base + lane;
-      uint32_t key = 0;
-      if (j < ncand) key = order_key(srow[j]);
-      const bool valid = j < ncand && (g.topk > 1);
-      const bool gt = valid && key > theta;
-      const bool eq = valid && key == theta;
-      const uint64_t eqm = __ballot(eq);
-      const int eq_rank = eq_taken + __popcll(eqm & lanes_below(lane));
-      const bool take = gt || (eq && eq_rank < rem);
-      const uint64_t tm = __ballot(take);
-      if (take) out[pos + __popcll(tm & lanes_below(lane))] = kb0 + j;
-      pos += __popcll(tm);
-      eq_taken += __popcll(eqm);
+    const int ncand = diag - g.lw;
+    const float* srow = scores + (int64_t)grp * g.score_elems + g.s0[b] + (int64_t)I * nk;
+    int rem = g.topk - 1;
+    uint32_t prefix = 0, pmask = 0;
+    bool whole_bin = false;                       // the threshold's bin is taken whole
+    if (ncand <= 64 * SEL_REG) {
+      uint32_t key[SEL_REG];
+      uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+      for (int r = 0; r < SEL_REG; ++r) {
+        if (r * 64 >= ncand) break;
+        const int j = r * 64 + lane;
+        key[r] = j < ncand ? order_key(srow[j]) : 0u;
+        if (j < ncand) { kmin = min(kmin, key[r]); kmax = max(kmax, key[r]); }
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+      }
+      if (rem > 0) {
+        if (kmin == kmax) {
+          prefix = kmin;                          // all keys equal: lowest indices win
+          pmask = 0xffffffffu;
+        } else {
+          const int top = 31 - __clz(kmin ^ kmax);          // highest bit where keys differ
+          const int first = top >= 24 ? 24 : top >= 16 ? 16 : top >= 8 ? 8 : 0;
+          pmask = first == 24 ? 0u : (0xffffffffu << (first + 8));
+          prefix = kmin & pmask;
+          for (int shift = first; shift >= 0; shift -= 8) {
+            hist_clear(h, lane);
+#pragma unroll
+            for (int r = 0; r < SEL_REG; ++r) {
+              if (r * 64 >= ncand) break;
+              if (r * 64 + lane < ncand && (key[r] & pmask) == prefix)
+                atomicAdd(&h[(key[r] >> shift) & 255u], 1u);
+            }
+            const uint32_t cnt = radix_scan(h, lane, shift, prefix, pmask, rem);
+            if ((int)cnt == rem) { whole_bin = true; break; }
+          }
+        }
+      }
+      // emit in ascending block order
+      int eq_taken = 0;
+#pragma unroll
+      for (int r = 0; r < SEL_REG; ++r) {
+        if (r * 64 >= ncand) break;
+        const int j = r * 64 + lane;
+        const bool valid = j < ncand && rem > 0;
+        const uint32_t km = key[r] & pmask;
+        const bool gt = valid && (whole_bin ? km >= prefix : key[r] > prefix);
+        const bool eq = valid && !whole_bin && key[r] == prefix;
+        const uint64_t eqm = __ballot(eq);
+        const int eq_rank = eq_taken + __popcll(eqm & lanes_below(lane));
+        const bool take = gt || (eq && eq_rank < rem);
+        const uint64_t tm = __ballot(take);
+        if (take) out[pos + __popcll(tm & lanes_below(lane))] = kb0 + j;
+        pos += __popcll(tm);
+        eq_taken += __popcll(eqm);
+      }
+    } else {
+      if (rem > 0) {
+        for (int shift = 24; shift >= 0; shift -= 8) {
+          hist_clear(h, lane);
+          for (int j = lane; j < ncand; j += 64) {
+            const uint32_t key = order_key(srow[j]);
+            if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+          }
+          radix_scan(h, lane, shift, prefix, pmask, rem);
+        }
+      }
+      int eq_taken = 0;
+      for (int base = 0; base < ncand; base += 64) {
+        const int j = base + lane;
+        const uint32_t key = j < ncand ? order_key(srow[j]) : 0u;
+        const bool valid = j < ncand && rem > 0;
+        const bool gt = valid && key > prefix;
+        const bool eq = valid && key == prefix;
+        const uint64_t eqm = __ballot(eq);
+        const int eq_rank = eq_taken + __popcll(eqm & lanes_below(lane));
+        const bool take = gt || (eq && eq_rank < rem);
+        const uint64_t tm = __ballot(take);
+        if (take) out[pos + __popcll(tm & lanes_below(lane))] = kb0 + j;
+        pos += __popcll(tm);
+        eq_taken += __popcll(eqm);
+      }
     }
     for (int j = lane; j <= g.lw; j += 64) out[pos + j] = kb0 + diag - g.lw + j;
     pos += g.lw + 1;

@@ -111,3 +111,6 @@ def test_kernel_resources_reported():
         log(f"  {r['name']:32s} vgprs {r['vgprs']:4d} lds {r['lds_bytes']:7d} scratch {r['scratch_bytes']:4d} "
             f"wg/CU {r['workgroups_per_cu']}")
         assert r["workgroups_per_cu"] >= 1, r
+        # no register spills: spill traffic goes through the same vector-memory
+        # counter that the LDS-copy rings wait on, and serialises them
+        assert r["scratch_bytes"] == 0, r
