@@ -60,6 +60,11 @@ def flop_model(w, seqlens, scored_pairs):
         "scoring": 2 * dp * Hp * scored_pairs,
         "fwd_counted": 4 * d * Hq * n + 2 * dp * Hp * n,
         "bwd_counted": 10 * d * Hq * n + 6 * dp * Hp * n,
+        # what the split backward executes: S and dP are recomputed in both
+        # passes (14 d per head), the query-major pass also forms P kp per
+        # head for the group-mean term, and each pass recomputes Y and applies
+        # one proxy product per group
+        "bwd_executed": 14 * d * Hq * n + 2 * dp * Hq * n + 8 * dp * Hp * n,
         # per-kernel algorithmic work
         "k:proxy_scores": 2 * dp * Hp * scored_pairs,
         "k:fwd": 4 * d * Hq * n,
@@ -246,6 +251,13 @@ def main(argv=None):
     value = total_flops / (step_ms * 1e-3) / 1e12
     attn_ms = stages.get("fwd", 0.0) + stages.get("bwd", 0.0)
     attn_tflops = (f["fwd_counted"] + f["bwd_counted"]) / (attn_ms * 1e-3) / 1e12 if attn_ms else None
+    bwd_ms = stages.get("bwd", 0.0)
+    bwd_rates = None
+    if bwd_ms:
+        bwd_rates = {"counted_tflops": round(f["bwd_counted"] / (bwd_ms * 1e-3) / 1e12, 2),
+                     "executed_tflops": round(f["bwd_executed"] / (bwd_ms * 1e-3) / 1e12, 2),
+                     "executed_mfma_frac": round(f["bwd_executed"] / (bwd_ms * 1e-3) / 1e12
+                                                / MFMA_BF16_PEAK_TFLOPS, 4)}
 
     dom = max(ROOFLINE_KERNELS, key=lambda k: per_kernel.get(k, {}).get("avg_ms", 0.0) *
               per_kernel.get(k, {}).get("launches_per_step", 0.0))
@@ -297,6 +309,7 @@ def main(argv=None):
         "attn_fwd_bwd_tflops": None if attn_tflops is None else round(attn_tflops, 2),
         "attn_mfma_frac": None if attn_tflops is None else round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "selection_roofline": selection,
+        "bwd_rates": bwd_rates,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in sorted(per_kernel.items())},
         "flops": {k: v for k, v in f.items() if not k.startswith("k:")},

@@ -268,11 +268,15 @@ hipError_t launch_proxy_scores(const Geo& g, int is_bf16, const void* qp, const 
 // selection: one wave per (group, query block)
 // ---------------------------------------------------------------------------
 //
-// The k - 1 best candidates are found by a 4-pass, 8-bit radix select of the
-// (k-1)-th largest order-preserving key; keys above it are taken, and of the
-// keys equal to it the lowest block indices, up to k - 1 in total.  The pick
-// is emitted in ascending block order with a ballot prefix count, followed by
-// the forced window and diagonal blocks, then -1 padding.
+// The k - 1 best candidates are those at or above a cut in the order (score
+// descending, block index ascending).  The cut is found on order-preserving
+// integer keys by radix steps over 8-bit windows: the first window starts at
+// the highest bit where the row's keys differ, a histogram of the window's
+// digit locates the bin that holds the (k-1)-th key, and that bin is then
+// resolved exactly: taken whole when all of it is needed, ranked member by
+// member when it holds at most 64 keys, else split by the next window.  The
+// pick is emitted in ascending block order with a ballot prefix count,
+// followed by the forced window and diagonal blocks, then -1 padding.
 
 __device__ __forceinline__ uint32_t order_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -284,65 +288,95 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Orders LDS traffic inside one wave (each wave owns its histogram, so no
+// Orders LDS traffic inside one wave (each wave owns its LDS area, so no
 // workgroup barrier is needed).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 }
 
-// Second half of an 8-bit radix step of the selection: given the wave's
-// histogram h of the digit at `shift` (over the keys matching prefix under
-// pmask), find the digit of the rem-th largest key.  Returns that bin's
-// count; updates prefix, pmask and rem.
-__device__ __forceinline__ uint32_t radix_scan(uint32_t* h, int lane, int shift, uint32_t& prefix,
-                                               uint32_t& pmask, int& rem) {
-  wave_lds_sync();
-  const uint32_t h0 = h[4 * lane + 0], h1 = h[4 * lane + 1], h2 = h[4 * lane + 2], h3 = h[4 * lane + 3];
-  const int c = (int)(h0 + h1 + h2 + h3);
-  int incl = c;                                   // inclusive suffix sum over lanes >= lane
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_down(incl, o, 64);
-    if (lane + o < 64) incl += t;
-  }
-  int above = incl - c;                           // count in bins of higher lanes
-  int found = -1, newrem = 0;
-  uint32_t cnt = 0;
-  const uint32_t hb[4] = {h0, h1, h2, h3};
-#pragma unroll
-  for (int q = 3; q >= 0; --q) {
-    if (found < 0 && above < rem && rem <= above + (int)hb[q]) { found = q; newrem = rem - above; cnt = hb[q]; }
-    above += (int)hb[q];
-  }
-  const uint64_t m = __ballot(found >= 0);
-  const int src = __ffsll((unsigned long long)m) - 1;
-  const int digit = __shfl(4 * lane + found, src, 64);
-  rem = __shfl(newrem, src, 64);
-  prefix |= (uint32_t)digit << shift;
-  pmask |= 255u << shift;
-  const uint32_t bin = (uint32_t)__shfl((int)cnt, src, 64);
-  wave_lds_sync();
-  return bin;
+// Lane shifts within rows of 16 lanes; a lane whose source lies outside its
+// row keeps `old`.
+template <int SHIFT>
+__device__ __forceinline__ uint32_t row_shr(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, 0x110 + SHIFT, 0xf, 0xf, false);
 }
-__device__ __forceinline__ void hist_clear(uint32_t* h, int lane) {
-  for (int i = lane; i < 256; i += 64) h[i] = 0;
+__device__ __forceinline__ uint32_t rd_lane(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  v = min(v, row_shr<1>(0xffffffffu, v));
+  v = min(v, row_shr<2>(0xffffffffu, v));
+  v = min(v, row_shr<4>(0xffffffffu, v));
+  v = min(v, row_shr<8>(0xffffffffu, v));
+  return min(min(rd_lane(v, 15), rd_lane(v, 31)), min(rd_lane(v, 47), rd_lane(v, 63)));
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, row_shr<1>(0u, v));
+  v = max(v, row_shr<2>(0u, v));
+  v = max(v, row_shr<4>(0u, v));
+  v = max(v, row_shr<8>(0u, v));
+  return max(max(rd_lane(v, 15), rd_lane(v, 31)), max(rd_lane(v, 47), rd_lane(v, 63)));
+}
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x, int lane) {
+  x += row_shr<1>(0u, x);
+  x += row_shr<2>(0u, x);
+  x += row_shr<4>(0u, x);
+  x += row_shr<8>(0u, x);
+  const uint32_t r0 = rd_lane(x, 15), r1 = rd_lane(x, 31), r2 = rd_lane(x, 47);
+  const int row = lane >> 4;
+  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// Per-wave LDS: a 256-bin histogram (bin 255 - v counts digit v, so that lane
+// l reads the four bins of digits 255 - 4l ... 252 - 4l, highest first) and
+// room for the 64 members of a threshold bin.
+struct SelLds {
+  uint32_t hist[256];
+  uint32_t mkey[64];
+  int32_t mj[64];
+};
+
+__device__ __forceinline__ void hist_clear(SelLds& w, int lane) {
+  reinterpret_cast<uint4*>(w.hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
   wave_lds_sync();
 }
 
-// Selection: one wave per (group, query block).  The (k-1)-th largest
-// candidate key is found by 8-bit radix steps; candidates above it are taken,
-// and among keys equal to it the lowest block indices.  Rows of up to
-// 64 * SEL_REG candidates are read once into registers; the radix starts at
-// the highest bit where the row's keys differ and stops as soon as the bin
-// holding the (k-1)-th key is taken whole.  Longer rows re-read the scores in
-// every step.
+// Given the histogram of one window's digit (over the keys that match the
+// decided prefix), find the bin of the rem-th largest key: its digit, how
+// many of its keys are still needed (rem, updated) and how many it holds.
+__device__ __forceinline__ void radix_pick(SelLds& w, int lane, uint32_t& digit, int& rem, int& cnt) {
+  wave_lds_sync();
+  const uint4 hv = reinterpret_cast<const uint4*>(w.hist)[lane];
+  const uint32_t hb[4] = {hv.x, hv.y, hv.z, hv.w};
+  const uint32_t c = hv.x + hv.y + hv.z + hv.w;
+  int above = (int)(wave_incl_sum(c, lane) - c);  // keys in the bins of lower lanes (higher digits)
+  int found = -1, nrem = 0, fcnt = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (found < 0 && above < rem && rem <= above + (int)hb[q]) { found = q; nrem = rem - above; fcnt = (int)hb[q]; }
+    above += (int)hb[q];
+  }
+  const int src = __ffsll((unsigned long long)__ballot(found >= 0)) - 1;
+  digit = 255u - (uint32_t)(4 * src + (int)rd_lane((uint32_t)found, src));
+  rem = (int)rd_lane((uint32_t)nrem, src);
+  cnt = (int)rd_lane((uint32_t)fcnt, src);
+  wave_lds_sync();
+}
+
+// Emission modes of the register path.
+enum SelMode { SEL_WHOLE = 0, SEL_CUT = 1, SEL_EQ = 2 };
+
+// Selection: one wave per (group, query block).  Rows of up to 64 * SEL_REG
+// candidates are read once into registers; longer rows re-read the scores in
+// each of four fixed 8-bit steps.
 constexpr int SEL_REG = 32;
 
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ scores,
                                                      int32_t* __restrict__ q2k_idx,
                                                      int32_t* __restrict__ q2k_cnt, Geo g) {
-  __shared__ uint32_t hist[4][256];
+  __shared__ SelLds lds[4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
@@ -356,7 +390,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
   const int kb0 = g.kb0[b];
   const int diag = (I * g.Bq) >> 7;
   int32_t* out = q2k_idx + ((int64_t)grp * g.nqb + QB) * g.stride;
-  uint32_t* h = hist[wave];
+  SelLds& w = lds[wave];
   int pos = 0;
   if ((diag + 1) <= g.topk + g.lw) {              // every block up to the diagonal
     for (int j = lane; j <= diag; j += 64) out[j] = kb0 + j;
@@ -366,7 +400,6 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
     const float* srow = scores + (int64_t)grp * g.score_elems + g.s0[b] + (int64_t)I * nk;
     int rem = g.topk - 1;
     uint32_t prefix = 0, pmask = 0;
-    bool whole_bin = false;                       // the threshold's bin is taken whole
     if (ncand <= 64 * SEL_REG) {
       uint32_t key[SEL_REG];
       uint32_t kmin = 0xffffffffu, kmax = 0u;
@@ -377,60 +410,106 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
         key[r] = j < ncand ? order_key(srow[j]) : 0u;
         if (j < ncand) { kmin = min(kmin, key[r]); kmax = max(kmax, key[r]); }
       }
+      kmin = wave_min(kmin);
+      kmax = wave_max(kmax);
+      int mode = SEL_EQ;
+      uint32_t cut_key = 0;
+      int cut_j = 0;
+      if (rem > 0 && kmin == kmax) {
+        prefix = kmin;                            // all keys equal: lowest indices win
+        pmask = 0xffffffffu;
+      } else if (rem > 0) {
+        int top = 31 - __clz(kmin ^ kmax);        // highest bit where the keys differ
+        pmask = ~((2u << top) - 1u);              // 0 when top is 31
+        prefix = kmin & pmask;
+        for (;;) {
+          const int lo = top >= 7 ? top - 7 : 0;
+          const uint32_t wmask = ((2u << top) - 1u) & ~((1u << lo) - 1u);
+          hist_clear(w, lane);
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-      }
-      if (rem > 0) {
-        if (kmin == kmax) {
-          prefix = kmin;                          // all keys equal: lowest indices win
-          pmask = 0xffffffffu;
-        } else {
-          const int top = 31 - __clz(kmin ^ kmax);          // highest bit where keys differ
-          const int first = top >= 24 ? 24 : top >= 16 ? 16 : top >= 8 ? 8 : 0;
-          pmask = first == 24 ? 0u : (0xffffffffu << (first + 8));
-          prefix = kmin & pmask;
-          for (int shift = first; shift >= 0; shift -= 8) {
-            hist_clear(h, lane);
+          for (int r = 0; r < SEL_REG; ++r) {
+            if (r * 64 >= ncand) break;
+            if (r * 64 + lane < ncand && (key[r] & pmask) == prefix)
+              atomicAdd(&w.hist[255u - ((key[r] >> lo) & 255u)], 1u);
+          }
+          uint32_t digit;
+          int cnt;
+          radix_pick(w, lane, digit, rem, cnt);
+          prefix |= (digit << lo) & wmask;
+          pmask |= wmask;
+          if (cnt == rem) { mode = SEL_WHOLE; break; }
+          if (cnt <= 64) {
+            // rank the bin's members (collected in ascending block order)
+            int base = 0;
 #pragma unroll
             for (int r = 0; r < SEL_REG; ++r) {
               if (r * 64 >= ncand) break;
-              if (r * 64 + lane < ncand && (key[r] & pmask) == prefix)
-                atomicAdd(&h[(key[r] >> shift) & 255u], 1u);
+              const int j = r * 64 + lane;
+              const bool in = j < ncand && (key[r] & pmask) == prefix;
+              const uint64_t m = __ballot(in);
+              if (in) {
+                const int p = base + __popcll(m & lanes_below(lane));
+                w.mkey[p] = key[r];
+                w.mj[p] = j;
+              }
+              base += __popcll(m);
             }
-            const uint32_t cnt = radix_scan(h, lane, shift, prefix, pmask, rem);
-            if ((int)cnt == rem) { whole_bin = true; break; }
+            wave_lds_sync();
+            const uint32_t K = lane < cnt ? w.mkey[lane] : 0u;
+            const int J = lane < cnt ? w.mj[lane] : 0;
+            int rank = 0;
+            for (int m = 0; m < cnt; ++m) {
+              const uint32_t Km = rd_lane(K, m);
+              rank += (Km > K || (Km == K && m < lane)) ? 1 : 0;
+            }
+            const int src = __ffsll((unsigned long long)__ballot(lane < cnt && rank == rem - 1)) - 1;
+            cut_key = rd_lane(K, src);
+            cut_j = (int)rd_lane((uint32_t)J, src);
+            mode = SEL_CUT;
+            break;
           }
+          if (lo == 0) break;                     // the whole key is decided: equal keys by index
+          top = lo - 1;
         }
       }
       // emit in ascending block order
-      int eq_taken = 0;
+      if (g.topk > 1) {
+        int eq_taken = 0;
 #pragma unroll
-      for (int r = 0; r < SEL_REG; ++r) {
-        if (r * 64 >= ncand) break;
-        const int j = r * 64 + lane;
-        const bool valid = j < ncand && rem > 0;
-        const uint32_t km = key[r] & pmask;
-        const bool gt = valid && (whole_bin ? km >= prefix : key[r] > prefix);
-        const bool eq = valid && !whole_bin && key[r] == prefix;
-        const uint64_t eqm = __ballot(eq);
-        const int eq_rank = eq_taken + __popcll(eqm & lanes_below(lane));
-        const bool take = gt || (eq && eq_rank < rem);
-        const uint64_t tm = __ballot(take);
-        if (take) out[pos + __popcll(tm & lanes_below(lane))] = kb0 + j;
-        pos += __popcll(tm);
-        eq_taken += __popcll(eqm);
+        for (int r = 0; r < SEL_REG; ++r) {
+          if (r * 64 >= ncand) break;
+          const int j = r * 64 + lane;
+          const bool valid = j < ncand;
+          bool take;
+          if (mode == SEL_WHOLE) {
+            take = valid && (key[r] & pmask) >= prefix;
+          } else if (mode == SEL_CUT) {
+            take = valid && (key[r] > cut_key || (key[r] == cut_key && j <= cut_j));
+          } else {
+            const bool eq = valid && key[r] == prefix;
+            const uint64_t eqm = __ballot(eq);
+            const int eq_rank = eq_taken + __popcll(eqm & lanes_below(lane));
+            take = (valid && key[r] > prefix) || (eq && eq_rank < rem);
+            eq_taken += __popcll(eqm);
+          }
+          const uint64_t tm = __ballot(take);
+          if (take) out[pos + __popcll(tm & lanes_below(lane))] = kb0 + j;
+          pos += __popcll(tm);
+        }
       }
     } else {
       if (rem > 0) {
         for (int shift = 24; shift >= 0; shift -= 8) {
-          hist_clear(h, lane);
+          hist_clear(w, lane);
           for (int j = lane; j < ncand; j += 64) {
             const uint32_t key = order_key(srow[j]);
-            if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+            if ((key & pmask) == prefix) atomicAdd(&w.hist[255u - ((key >> shift) & 255u)], 1u);
           }
-          radix_scan(h, lane, shift, prefix, pmask, rem);
+          uint32_t digit;
+          int cnt;
+          radix_pick(w, lane, digit, rem, cnt);
+          prefix |= digit << shift;
+          pmask |= 255u << shift;
         }
       }
       int eq_taken = 0;
