@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X published dense bf16/fp16
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 METRIC = "MSA fwd+bwd ms/step and TFLOP/s (selected FLOPs) at 128k–1M tok; % MFMA peak"
+PREFILL_METRIC = "MSA forward-only (prefill) ms and TFLOP/s (scoring + selected forward FLOPs)"
 ROOFLINE_KERNELS = ("proxy_scores", "fwd", "bwd_dq", "bwd_dkdv")
 
 
@@ -160,6 +161,76 @@ def cpu_baseline(w, seqlens, x, budget_s, seed):
                       f"{dt:.1f} s wall", "seconds": dt}
 
 
+def dense_compare(a, w, seqlens, x, msa, torch):
+    """The workload through the autograd API twice: with its top-k, and with
+    every causal block selected (dense).  Each is run once untimed, then
+    timed once: forward (scores, selection, forward) and backward separately.
+    Memory: bytes allocated between the end of the forward and the start of
+    the backward beyond the inputs (O, the LSEs, the block lists), and the
+    peak over the step."""
+    host = [int(c) for c in x["cu_seqlens"].cpu().tolist()]
+    names = ("q", "k", "v", "qp", "kp")
+    res = {}
+    for label, dense in (("sparse", False), ("dense", True)):
+        leaves = {n: x[n].detach().clone().requires_grad_(True) for n in names}
+
+        def forward():
+            return msa.msa_attention(*(leaves[n] for n in names), x["cu_seqlens"], topk=w.topk,
+                                     q_block=w.q_block, local_window=w.local_window,
+                                     proxy_loss_weight=w.proxy_loss_weight, cu_seqlens_host=host,
+                                     dense=dense)
+
+        for _ in range(max(a.warmup, 1)):
+            o = forward()
+            o.backward(x["dO"])
+            del o
+            for t in leaves.values():
+                t.grad = None
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        o = forward()
+        e[1].record()
+        torch.cuda.synchronize()
+        kept = torch.cuda.memory_allocated() - base
+        o.backward(x["dO"])
+        e[2].record()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        fwd_ms, bwd_ms = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
+        topk = max(-(-L // 128) for L in seqlens) if dense else w.topk
+        n = selected_pairs(seqlens, w.q_block, topk, w.local_window)
+        d, dp, Hq, Hp = w.head_dim, w.proxy_dim, w.heads_q, w.heads_kv
+        fwd_fl = 4 * d * Hq * n + 2 * dp * Hp * n
+        bwd_fl = 10 * d * Hq * n + 6 * dp * Hp * n
+        res[label] = {"topk": topk, "pairs_per_group": n, "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+                      "fwd_tflops": round(fwd_fl / (fwd_ms * 1e-3) / 1e12, 2),
+                      "bwd_tflops": round(bwd_fl / (bwd_ms * 1e-3) / 1e12, 2),
+                      "kept_bytes_fwd_to_bwd": int(kept), "peak_bytes_over_inputs": int(peak)}
+        del o, leaves
+        torch.cuda.synchronize()
+    T, Hq, d = sum(seqlens), w.heads_q, w.head_dim
+    esz = 2 if w.dtype == "bf16" else 4
+    fused = T * Hq * d * esz + T * Hq * 4          # a fused dense kernel keeps O and LSE only
+    sp, de = res["sparse"], res["dense"]
+    out = {"mode": "dense-compare", "workload": w.name, "total_tokens": T, "docs": len(seqlens),
+           "sparse": sp, "dense": de,
+           "speedup": {"fwd": round(de["fwd_ms"] / sp["fwd_ms"], 3), "bwd": round(de["bwd_ms"] / sp["bwd_ms"], 3),
+                       "step": round((de["fwd_ms"] + de["bwd_ms"]) / (sp["fwd_ms"] + sp["bwd_ms"]), 3)},
+           "kept_ratio_dense_over_sparse": round(de["kept_bytes_fwd_to_bwd"] / sp["kept_bytes_fwd_to_bwd"], 3),
+           "fused_dense_kept_bytes": fused,
+           "note": "dense = the same kernels with every causal block selected; fused_dense_kept_bytes "
+                   "is what a fused dense attention keeps (O and LSE)"}
+    line = json.dumps(out)
+    print(line, flush=True)
+    if a.report:
+        with open(a.report, "w") as fh:
+            fh.write(line + "\n")
+    return 0
+
+
 def calibrate_copy(mib):
     """A plain copy kernel of known size: reads and writes mib MiB per launch."""
     import torch
@@ -183,6 +254,11 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--report", default=None, help="also write the JSON (plus details) here")
+    ap.add_argument("--mode", choices=("train", "prefill", "dense-compare"), default="train",
+                    help="train: the training step (default); prefill: forward only (scores, "
+                         "selection, forward); dense-compare: the same workload once sparse and once "
+                         "with every causal block selected, through the autograd API, with the "
+                         "memory kept between forward and backward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB, 4 times (the "
                          "known-size reference for scaling HBM byte counters), then exit")
@@ -213,9 +289,13 @@ def main(argv=None):
     buf = msa.Buffers(cfg, vl, device="cuda", need_bwd=True)
     lay = buf.layout
 
+    if a.mode == "dense-compare":
+        return dense_compare(a, w, seqlens, x, msa, torch)
+
     def step():
         msa.run_forward(cfg, vl, x["q"], x["k"], x["v"], x["qp"], x["kp"], buf)
-        msa.run_backward(cfg, vl, x["q"], x["k"], x["v"], x["qp"], x["kp"], x["dO"], buf)
+        if a.mode == "train":
+            msa.run_backward(cfg, vl, x["q"], x["k"], x["v"], x["qp"], x["kp"], x["dO"], buf)
 
     for _ in range(a.warmup):
         step()
@@ -247,10 +327,14 @@ def main(argv=None):
     for k, v in per_kernel.items():
         if "k:" + k in f:
             v["tflops"] = f["k:" + k] / (v["avg_ms"] * 1e-3) / 1e12
-    total_flops = f["scoring"] + f["fwd_counted"] + f["bwd_counted"]
+    if a.mode == "prefill":
+        total_flops = f["scoring"] + f["fwd_counted"]
+    else:
+        total_flops = f["scoring"] + f["fwd_counted"] + f["bwd_counted"]
     value = total_flops / (step_ms * 1e-3) / 1e12
     attn_ms = stages.get("fwd", 0.0) + stages.get("bwd", 0.0)
-    attn_tflops = (f["fwd_counted"] + f["bwd_counted"]) / (attn_ms * 1e-3) / 1e12 if attn_ms else None
+    attn_flops = f["fwd_counted"] + (f["bwd_counted"] if a.mode == "train" else 0)
+    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12 if attn_ms else None
     bwd_ms = stages.get("bwd", 0.0)
     bwd_rates = None
     if bwd_ms:
@@ -259,7 +343,7 @@ def main(argv=None):
                      "executed_mfma_frac": round(f["bwd_executed"] / (bwd_ms * 1e-3) / 1e12
                                                 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
-    dom = max(ROOFLINE_KERNELS, key=lambda k: per_kernel.get(k, {}).get("avg_ms", 0.0) *
+    dom = max([k for k in ROOFLINE_KERNELS if k in per_kernel], key=lambda k: per_kernel.get(k, {}).get("avg_ms", 0.0) *
               per_kernel.get(k, {}).get("launches_per_step", 0.0))
     achieved = per_kernel[dom]["tflops"]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -283,11 +367,11 @@ def main(argv=None):
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": sel_bytes}
 
     cpu = None
-    if a.cpu_budget > 0:
+    if a.cpu_budget > 0 and a.mode == "train":
         cpu = cpu_baseline(w, seqlens, x, a.cpu_budget, a.seed)
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if a.mode == "train" else PREFILL_METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -313,6 +397,7 @@ def main(argv=None):
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in sorted(per_kernel.items())},
         "flops": {k: v for k, v in f.items() if not k.startswith("k:")},
+        "tokens_per_s": round(sum(seqlens) / (step_ms * 1e-3), 1),
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(t_gen, 2),
     }

@@ -21,8 +21,12 @@ class _MSAFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, qp, kp, cfg: Config, vl: Varlen):
         q, k, v, qp, kp = (t.contiguous() for t in (q, k, v, qp, kp))
-        buf = Buffers(cfg, vl, device=q.device, need_bwd=True)
+        buf = Buffers(cfg, vl, device=q.device, need_bwd=False)
         run_forward(cfg, vl, q, k, v, qp, kp, buf)
+        # keep O, the LSEs and the block lists; scores and workspace are
+        # released once the stream has consumed them (the caching allocator
+        # reuses them only for work ordered after this point on the stream)
+        buf.release_transients()
         ctx.cfg, ctx.vl, ctx.buf = cfg, vl, buf
         ctx.save_for_backward(q, k, v, qp, kp)
         return buf.o
@@ -31,10 +35,12 @@ class _MSAFunction(torch.autograd.Function):
     def backward(ctx, dout):
         q, k, v, qp, kp = ctx.saved_tensors
         buf = ctx.buf
+        buf.alloc_backward()
         run_backward(ctx.cfg, ctx.vl, q, k, v, qp, kp, dout.contiguous().to(q.dtype), buf)
         dt = q.dtype
-        return (buf.dq.to(dt), buf.dk.to(dt), buf.dv.to(dt), buf.dqp.to(dt), buf.dkp.to(dt),
-                None, None)
+        grads = (buf.dq.to(dt), buf.dk.to(dt), buf.dv.to(dt), buf.dqp.to(dt), buf.dkp.to(dt))
+        ctx.buf = None
+        return grads + (None, None)
 
 
 def msa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qp: torch.Tensor,

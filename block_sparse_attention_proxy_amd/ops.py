@@ -209,12 +209,36 @@ class Buffers:
         self.o = torch.empty((T, Hq, d), dtype=cfg.torch_dtype, **z)
         self.lse = torch.empty((Hq, T), dtype=f32, **z)
         self.lse_p = torch.empty((Hkv, T), dtype=f32, **z)
+        self._shape = (T, Hq, Hkv, d, dp, device)
         if need_bwd:
-            self.dq = torch.empty((T, Hq, d), dtype=f32, **z)
-            self.dk = torch.empty((T, Hkv, d), dtype=f32, **z)
-            self.dv = torch.empty((T, Hkv, d), dtype=f32, **z)
-            self.dqp = torch.empty((T, Hkv, dp), dtype=f32, **z)
-            self.dkp = torch.empty((T, Hkv, dp), dtype=f32, **z)
+            self.alloc_backward()
+
+    def alloc_backward(self):
+        """The gradient outputs (fp32) and, if released, the workspace."""
+        T, Hq, Hkv, d, dp, device = self._shape
+        f32, z = torch.float32, dict(device=device)
+        if getattr(self, "workspace", None) is None:
+            self.workspace = torch.empty(max(self.layout["workspace_bytes"], 16), dtype=torch.uint8, **z)
+        self.dq = torch.empty((T, Hq, d), dtype=f32, **z)
+        self.dk = torch.empty((T, Hkv, d), dtype=f32, **z)
+        self.dv = torch.empty((T, Hkv, d), dtype=f32, **z)
+        self.dqp = torch.empty((T, Hkv, dp), dtype=f32, **z)
+        self.dkp = torch.empty((T, Hkv, dp), dtype=f32, **z)
+
+    def release_transients(self):
+        """Drop what the backward does not read: the block scores and the
+        workspace (every call rebuilds its tables; the backward's per-query
+        vectors are written in the backward itself)."""
+        self.scores = None
+        self.workspace = None
+
+    def saved_bytes(self) -> dict:
+        """Bytes kept from the forward for the backward, besides the inputs."""
+        out = {}
+        for n in ("o", "lse", "lse_p", "q2k_idx", "q2k_cnt", "k2q_ptr", "k2q_idx"):
+            t = getattr(self, n)
+            out[n] = t.numel() * t.element_size()
+        return out
 
 
 def run_forward(cfg: Config, vl: Varlen, q, k, v, qp, kp, buf: Buffers, stream=None):

@@ -111,3 +111,27 @@ def test_python_wrappers_check_tensors():
     cpu = torch.zeros(256, 2, 32)
     with pytest.raises(ValueError, match="device tensor"):
         msa.msa_proxy_scores(cfg, vl, cpu, cpu, torch.zeros(2, 4), torch.zeros(16, dtype=torch.uint8))
+
+
+def test_buffer_lifetimes_and_saved_bytes():
+    """The autograd path keeps only O, the LSEs and the block lists from the
+    forward; scores and workspace are released, gradients come with the
+    backward.  Sizes follow the layout (host-side; CPU tensors stand in)."""
+    seqlens = (3000, 129, 5000)
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    T, Hq, Hkv, d, dp = int(cu[-1]), 8, 2, 64, 32
+    cfg = msa.Config(Hq, Hkv, d, dp, 128, 3, 2, dtype="bf16")
+    buf = msa.Buffers(cfg, msa.Varlen(torch.from_numpy(cu)), device="cpu", need_bwd=False)
+    lay = buf.layout
+    assert not hasattr(buf, "dq")
+    buf.release_transients()
+    assert buf.scores is None and buf.workspace is None
+    sb = buf.saved_bytes()
+    nqb, nkb, st = lay["total_qblocks"], lay["total_kvblocks"], lay["sel_stride"]
+    assert sb == {"o": T * Hq * d * 2, "lse": 4 * Hq * T, "lse_p": 4 * Hkv * T,
+                  "q2k_idx": 4 * Hkv * nqb * st, "q2k_cnt": 4 * Hkv * nqb,
+                  "k2q_ptr": 4 * Hkv * (nkb + 1), "k2q_idx": 4 * Hkv * lay["k2q_capacity"]}
+    buf.alloc_backward()
+    assert buf.workspace.numel() >= lay["workspace_bytes"]
+    assert tuple(buf.dq.shape) == (T, Hq, d) and tuple(buf.dkp.shape) == (T, Hkv, dp)
+    assert buf.dq.dtype == torch.float32
