@@ -42,6 +42,12 @@ Readings (the pages give no formulas):
       counts the diagonal: k - 1 candidates are added.  Total selected
       K = min(k + w, diag(I) + 1); when K = diag(I) + 1 every block 0..diag is
       taken and no score is needed.
+  R3d Dilation delta >= 1 [KC Under the hood names a configurable window and
+      dilation, nothing more]: the forced blocks are diag, diag - delta, ...,
+      diag - w*delta (those >= 0); the candidate pool is J < diag - w*delta
+      (the window's span); blocks inside the span that are not on its stride
+      are neither forced nor candidates.  When the pool holds at most k - 1
+      blocks all of it is taken and nothing is scored.  delta = 1 is R3.
   R4  Ranking key: score descending, then block index ascending (lower index
       wins an exact tie).  Lists are emitted ascending, padded with -1.
   R5  Attention set A_i = {u : block(u) selected for block(i), u <= i}
@@ -81,6 +87,7 @@ class Config:
     softmax_scale: Optional[float] = None
     proxy_scale: Optional[float] = None
     proxy_loss_weight: float = 1.0
+    dilation: int = 1
 
     @property
     def G(self) -> int:
@@ -134,18 +141,27 @@ def diag_block(I: int, cfg: Config) -> int:
     return (I * cfg.q_block) // cfg.kv_block
 
 
+def forced_blocks(I: int, cfg: Config) -> List[int]:
+    """The diagonal block and the window's blocks before it, ascending (R3, R3d)."""
+    dg = diag_block(I, cfg)
+    return sorted(dg - i * cfg.dilation for i in range(cfg.local_window + 1) if dg - i * cfg.dilation >= 0)
+
+
+def pool_size(I: int, cfg: Config) -> int:
+    """Blocks before the window's span: J < diag - w * delta (R3, R3d)."""
+    return max(0, diag_block(I, cfg) - cfg.local_window * cfg.dilation)
+
+
 def n_selected(I: int, cfg: Config) -> int:
-    """K = min(k + w, diag + 1) (R3)."""
-    return min(cfg.topk + cfg.local_window, diag_block(I, cfg) + 1)
+    """K = min(k - 1, pool) + forced; with delta = 1 this is min(k + w, diag + 1) (R3)."""
+    return min(cfg.topk - 1, pool_size(I, cfg)) + len(forced_blocks(I, cfg))
 
 
 def candidate_count(I: int, cfg: Config) -> int:
-    """Number of scored candidate blocks of query block I (0 when the row is
-    fully selected)."""
-    dg = diag_block(I, cfg)
-    if n_selected(I, cfg) == dg + 1:
-        return 0
-    return dg - cfg.local_window
+    """Number of scored candidate blocks of query block I (0 when the whole
+    pool is taken, which needs no score)."""
+    n = pool_size(I, cfg)
+    return n if n > cfg.topk - 1 else 0
 
 
 def _qrows(doc: Doc, I: int, cfg: Config) -> np.ndarray:
@@ -203,16 +219,16 @@ def proxy_block_scores(qp, kp, cu_seqlens, cfg: Config) -> np.ndarray:
 def select_row(cand_scores: np.ndarray, I: int, cfg: Config) -> List[int]:
     """Local block indices selected for query block I, ascending.
 
-    Forced: the diagonal block and the w blocks before it.  Then the k - 1
-    candidates with the highest score, an exact tie going to the lower block
-    index.  When k + w covers every block up to the diagonal, all of them."""
-    dg = diag_block(I, cfg)
-    K = n_selected(I, cfg)
-    if K == dg + 1:
-        return list(range(dg + 1))
-    forced = list(range(dg - cfg.local_window, dg + 1))
+    Forced: the diagonal block and the window's blocks (R3, R3d).  Then the
+    k - 1 candidates of the pool with the highest score, an exact tie going to
+    the lower block index.  When the pool holds at most k - 1 blocks, all of
+    it (with delta = 1: every block up to the diagonal)."""
+    forced = forced_blocks(I, cfg)
+    n = pool_size(I, cfg)
+    if n <= cfg.topk - 1:
+        return list(range(n)) + forced
     cands = list(range(len(cand_scores)))
-    assert len(cands) == dg - cfg.local_window
+    assert len(cands) == n
     ranked = sorted(cands, key=lambda J: (-float(cand_scores[J]), J))
     picked = ranked[: cfg.topk - 1]
     return sorted(picked + forced)

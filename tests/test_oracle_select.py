@@ -41,9 +41,9 @@ def brute_scores(qp, kp, seqlens, cfg):
         for g in range(cfg.heads_kv):
             for I in range(nq):
                 first_tok = I * cfg.q_block
-                forced_lo = first_tok // cfg.kv_block - cfg.local_window
-                n_avail = first_tok // cfg.kv_block + 1
-                if min(cfg.topk + cfg.local_window, n_avail) == n_avail:
+                # blocks before the window's span (w blocks, stride = dilation)
+                forced_lo = first_tok // cfg.kv_block - cfg.local_window * cfg.dilation
+                if max(0, forced_lo) <= cfg.topk - 1:
                     continue
                 for J in range(forced_lo):
                     best = -np.inf
@@ -58,11 +58,11 @@ def brute_scores(qp, kp, seqlens, cfg):
     return out
 
 
-@pytest.mark.parametrize("seqlens,q_block,w", [((700,), 64, 0), ((300, 0, 517), 128, 1),
-                                               ((640,), 64, 1)])
-def test_scores_match_bruteforce(seqlens, q_block, w):
+@pytest.mark.parametrize("seqlens,q_block,w,dil", [((700,), 64, 0, 1), ((300, 0, 517), 128, 1, 1),
+                                                   ((640,), 64, 1, 1), ((900,), 64, 1, 2)])
+def test_scores_match_bruteforce(seqlens, q_block, w, dil):
     rng = np.random.default_rng(1)
-    cfg = _cfg(q_block=q_block, local_window=w, topk=2)
+    cfg = _cfg(q_block=q_block, local_window=w, topk=2, dilation=dil)
     T = sum(seqlens)
     qp = _half_ints(rng, (T, cfg.heads_kv, cfg.proxy_dim))
     kp = _half_ints(rng, (T, cfg.heads_kv, cfg.proxy_dim))
@@ -110,6 +110,45 @@ def test_selection_rank_bruteforce(topk, w, q_block):
         assert sel == expect
 
 
+@pytest.mark.parametrize("topk,w,dil,q_block", [(3, 2, 3, 128), (4, 1, 2, 64), (2, 3, 2, 128), (1, 2, 4, 64)])
+def test_selection_dilation_bruteforce(topk, w, dil, q_block):
+    """Dilated window, written out independently: forced = diagonal minus
+    multiples of the dilation (w of them, those >= 0); a block before the
+    diagonal that is not forced is selectable only below the window's span
+    diag - w * dilation; of those the k - 1 best by rank, or all of them when
+    there are no more than k - 1."""
+    rng = np.random.default_rng(17)
+    cfg = _cfg(topk=topk, local_window=w, q_block=q_block, dilation=dil)
+    for trial in range(60):
+        I = int(rng.integers(0, 64))
+        dg = I * q_block // 128
+        forced = [J for J in range(dg + 1) if (dg - J) % dil == 0 and (dg - J) // dil <= w]
+        below = [J for J in range(dg + 1) if J < dg - w * dil]
+        gaps = [J for J in range(dg + 1) if J not in forced and J not in below]
+        nc = om.candidate_count(I, cfg)
+        sc = rng.integers(-3, 4, size=nc).astype(np.float64)
+        sel = om.select_row(sc, I, cfg)
+        if len(below) <= topk - 1:
+            assert nc == 0 and sel == sorted(below + forced)
+        else:
+            assert nc == len(below)
+            assert sel == sorted(rank_select(sc, nc, topk - 1) + forced)
+        assert not set(gaps) & set(sel)
+        assert om.n_selected(I, cfg) == len(sel)
+
+
+def test_dilation_one_is_the_contiguous_window():
+    for topk, w, q_block in [(3, 2, 128), (5, 0, 64), (2, 4, 64)]:
+        a = _cfg(topk=topk, local_window=w, q_block=q_block)
+        b = _cfg(topk=topk, local_window=w, q_block=q_block, dilation=1)
+        for I in range(80):
+            dg = om.diag_block(I, a)
+            assert om.n_selected(I, b) == min(topk + w, dg + 1)
+            assert om.candidate_count(I, b) == (0 if dg + 1 <= topk + w else dg - w)
+            sc = np.arange(om.candidate_count(I, b), dtype=np.float64)[::-1].copy()
+            assert om.select_row(sc, I, a) == om.select_row(sc, I, b)
+
+
 def test_all_ties_pick_lowest():
     """kp constant for every token: every candidate block of a row has the same
     score, so the picks are blocks 0 .. k-2."""
@@ -132,10 +171,12 @@ def test_all_ties_pick_lowest():
                 assert sel == [0, 1, 2] + [dg - 1, dg]
 
 
-def test_golden_hand_example():
-    with open(os.path.join(GOLDEN, "select_example.json")) as f:
+@pytest.mark.parametrize("name", ["select_example.json", "select_dilation_example.json"])
+def test_golden_hand_example(name):
+    with open(os.path.join(GOLDEN, name)) as f:
         ex = json.load(f)
-    cfg = _cfg(q_block=ex["q_block"], topk=ex["topk"], local_window=ex["local_window"])
+    cfg = _cfg(q_block=ex["q_block"], topk=ex["topk"], local_window=ex["local_window"],
+               dilation=ex.get("dilation", 1))
     for row in ex["rows"]:
         sel = om.select_row(np.asarray(row["candidate_scores"], dtype=np.float64), row["I"], cfg)
         assert sel == row["expected"], row
@@ -149,20 +190,27 @@ def _invariants(idx, cnt, cu, cfg):
                 QB = d.qb0 + I
                 sel = list(idx[g, QB, :cnt[g, QB]])
                 dg = om.diag_block(I, cfg) + d.kb0
-                assert cnt[g, QB] == min(cfg.topk + cfg.local_window, dg - d.kb0 + 1)
+                pool = max(0, dg - d.kb0 - cfg.local_window * cfg.dilation)
+                forced = [dg - i * cfg.dilation for i in range(cfg.local_window + 1)
+                          if dg - i * cfg.dilation >= d.kb0]
+                assert cnt[g, QB] == min(cfg.topk - 1, pool) + len(forced)
+                if cfg.dilation == 1:
+                    assert cnt[g, QB] == min(cfg.topk + cfg.local_window, dg - d.kb0 + 1)
                 assert all(x == -1 for x in idx[g, QB, cnt[g, QB]:])
                 assert sel == sorted(set(sel))                     # ascending, unique
                 assert all(d.kb0 <= x < d.kb0 + d.nk for x in sel)  # inside the document
                 assert all(x <= dg for x in sel)                   # causal
-                for f in range(max(d.kb0, dg - cfg.local_window), dg + 1):
+                for f in forced:
                     assert f in sel                                # diagonal + window
+                assert all(x in forced or x < d.kb0 + pool for x in sel)
 
 
-@pytest.mark.parametrize("seqlens,q_block,topk,w", [((1000, 300, 2000), 64, 4, 0),
-                                                    ((3000, 129), 128, 3, 2)])
-def test_selection_invariants_and_inverse(seqlens, q_block, topk, w):
+@pytest.mark.parametrize("seqlens,q_block,topk,w,dil", [((1000, 300, 2000), 64, 4, 0, 1),
+                                                        ((3000, 129), 128, 3, 2, 1),
+                                                        ((2600, 700), 64, 3, 2, 3)])
+def test_selection_invariants_and_inverse(seqlens, q_block, topk, w, dil):
     rng = np.random.default_rng(11)
-    cfg = _cfg(q_block=q_block, topk=topk, local_window=w)
+    cfg = _cfg(q_block=q_block, topk=topk, local_window=w, dilation=dil)
     T = sum(seqlens)
     qp = rng.standard_normal((T, cfg.heads_kv, cfg.proxy_dim))
     kp = rng.standard_normal((T, cfg.heads_kv, cfg.proxy_dim))
