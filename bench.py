@@ -35,11 +35,12 @@ PREFILL_METRIC = "MSA forward-only (prefill) ms and TFLOP/s (scoring + selected 
 ROOFLINE_KERNELS = ("proxy_scores", "fwd", "bwd_dq", "bwd_dkdv")
 
 
-def selected_pairs(seqlens, q_block, topk, window):
+def selected_pairs(seqlens, q_block, topk, window, dilation=1):
     """Exactly-valid (query, key) pairs attended per KV group (every group has
     the same count: the number of selected blocks depends only on the
     diagonal).  Non-diagonal selected blocks lie wholly before the query
-    block; the diagonal block contributes the causal triangle."""
+    block; the diagonal block contributes the causal triangle.  Selected
+    blocks: min(k - 1, blocks below the window's span) + the forced ones."""
     total = 0
     for L in seqlens:
         nq = -(-L // q_block)
@@ -47,7 +48,7 @@ def selected_pairs(seqlens, q_block, topk, window):
             lo = I * q_block
             rows = min(q_block, L - lo)
             diag = lo // 128
-            cnt = min(topk + window, diag + 1)
+            cnt = min(topk - 1, max(0, diag - window * dilation)) + min(window, diag // dilation) + 1
             first = lo - diag * 128 + 1           # keys of the diagonal block for query lo
             total += rows * 128 * (cnt - 1) + rows * first + rows * (rows - 1) // 2
     return total
@@ -55,7 +56,7 @@ def selected_pairs(seqlens, q_block, topk, window):
 
 def flop_model(w, seqlens, scored_pairs):
     d, dp, Hq, Hp = w.head_dim, w.proxy_dim, w.heads_q, w.heads_kv
-    n = selected_pairs(seqlens, w.q_block, w.topk, w.local_window)
+    n = selected_pairs(seqlens, w.q_block, w.topk, w.local_window, w.dilation)
     f = {
         "pairs_per_group": n,
         "scoring": 2 * dp * Hp * scored_pairs,
@@ -178,7 +179,7 @@ def dense_compare(a, w, seqlens, x, msa, torch):
             return msa.msa_attention(*(leaves[n] for n in names), x["cu_seqlens"], topk=w.topk,
                                      q_block=w.q_block, local_window=w.local_window,
                                      proxy_loss_weight=w.proxy_loss_weight, cu_seqlens_host=host,
-                                     dense=dense)
+                                     dense=dense, dilation=w.dilation)
 
         for _ in range(max(a.warmup, 1)):
             o = forward()
@@ -201,7 +202,8 @@ def dense_compare(a, w, seqlens, x, msa, torch):
         peak = torch.cuda.max_memory_allocated() - base
         fwd_ms, bwd_ms = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
         topk = max(-(-L // 128) for L in seqlens) if dense else w.topk
-        n = selected_pairs(seqlens, w.q_block, topk, w.local_window)
+        n = (selected_pairs(seqlens, w.q_block, topk, 0, 1) if dense
+             else selected_pairs(seqlens, w.q_block, topk, w.local_window, w.dilation))
         d, dp, Hq, Hp = w.head_dim, w.proxy_dim, w.heads_q, w.heads_kv
         fwd_fl = 4 * d * Hq * n + 2 * dp * Hp * n
         bwd_fl = 10 * d * Hq * n + 6 * dp * Hp * n
@@ -284,7 +286,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
     cfg = msa.Config(w.heads_q, w.heads_kv, w.head_dim, w.proxy_dim, w.q_block, w.topk, w.local_window,
-                     128, 0.0, 0.0, w.proxy_loss_weight, w.dtype)
+                     128, 0.0, 0.0, w.proxy_loss_weight, w.dtype, w.dilation)
     vl = msa.Varlen(x["cu_seqlens"], x["cu_seqlens"].cpu().numpy())
     buf = msa.Buffers(cfg, vl, device="cuda", need_bwd=True)
     lay = buf.layout
@@ -356,9 +358,9 @@ def main(argv=None):
     for L in seqlens:
         nq = -(-L // w.q_block)
         for I in range(nq):
-            diag = I * w.q_block // 128
-            if diag + 1 > w.topk + w.local_window:
-                n_cand_entries += diag - w.local_window
+            pool = I * w.q_block // 128 - w.local_window * w.dilation
+            if pool > w.topk - 1:
+                n_cand_entries += pool
     sel_bytes = w.heads_kv * (4 * n_cand_entries + 4 * lay["total_qblocks"] * (lay["sel_stride"] + 1))
     selection = None
     if "select" in per_kernel:
@@ -386,7 +388,8 @@ def main(argv=None):
         "config": {"workload": w.name, "total_tokens": int(sum(seqlens)), "docs": len(seqlens),
                    "heads_q": w.heads_q, "heads_kv": w.heads_kv, "head_dim": w.head_dim,
                    "proxy_dim": w.proxy_dim, "kv_block": 128, "q_block": w.q_block, "topk": w.topk,
-                   "local_window": w.local_window, "seed": a.seed, "parallelism": "single GPU"},
+                   "local_window": w.local_window, "dilation": w.dilation, "seed": a.seed,
+                   "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
         "stages_ms": {k: round(v, 3) for k, v in sorted(stages.items())},

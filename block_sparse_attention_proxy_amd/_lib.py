@@ -17,6 +17,7 @@ MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_HIP, MSA_ERR_WORKSPACE
 MSA_BF16, MSA_F32 = 0, 1
 
 # Every symbol include/msa.h declares.
+ABI_VERSION = 2        # include/msa.h MSA_ABI_VERSION; msa_config layout below
 EXPORTS = ("msa_abi_version", "msa_status_string", "msa_last_error", "msa_get_layout",
            "msa_proxy_scores", "msa_select_blocks", "msa_fwd", "msa_bwd", "msa_kernel_count",
            "msa_kernel_info", "msa_profile_enable", "msa_profile_collect", "msa_profile_entry")
@@ -26,7 +27,8 @@ class MsaConfig(ctypes.Structure):
     _fields_ = [("heads_q", c_int32), ("heads_kv", c_int32), ("head_dim", c_int32),
                 ("proxy_dim", c_int32), ("kv_block", c_int32), ("q_block", c_int32),
                 ("topk", c_int32), ("local_window", c_int32), ("softmax_scale", c_float),
-                ("proxy_scale", c_float), ("proxy_loss_weight", c_float), ("dtype", c_int32)]
+                ("proxy_scale", c_float), ("proxy_loss_weight", c_float), ("dtype", c_int32),
+                ("dilation", c_int32)]
 
 
 class MsaVarlen(ctypes.Structure):
@@ -64,6 +66,9 @@ def load():
     pc, pv, pl = POINTER(MsaConfig), POINTER(MsaVarlen), POINTER(MsaLayout)
     pi = POINTER(c_int32)
     lib.msa_abi_version.restype = c_int32
+    if lib.msa_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.msa_abi_version()}, this binding expects "
+                          f"{ABI_VERSION}: rebuild it with `python -m block_sparse_attention_proxy_amd.build`")
     lib.msa_status_string.restype = c_char_p
     lib.msa_status_string.argtypes = [c_int32]
     lib.msa_last_error.restype = c_char_p

@@ -47,11 +47,13 @@ def msa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qp: torch.T
                   kp: torch.Tensor, cu_seqlens: torch.Tensor, *, topk: int, q_block: int = 128,
                   local_window: int = 0, softmax_scale: Optional[float] = None,
                   proxy_scale: Optional[float] = None, proxy_loss_weight: float = 1.0,
-                  cu_seqlens_host: Optional[Sequence[int]] = None, dense: bool = False):
+                  cu_seqlens_host: Optional[Sequence[int]] = None, dense: bool = False,
+                  dilation: int = 1):
     """Block-sparse GQA attention with proxy-head block selection.
 
     q [T, Hq, d]; k, v [T, Hkv, d]; qp, kp [T, Hkv, dp]; cu_seqlens int32 [B+1].
-    ``dense=True`` selects every causal block (top-k = all blocks).
+    ``dense=True`` selects every causal block (top-k = all blocks; window and
+    dilation are then moot).  ``dilation`` spaces the forced window blocks (1 = contiguous window).
     """
     T, Hq, d = q.shape
     Hkv, dp = k.shape[1], qp.shape[2]
@@ -59,7 +61,8 @@ def msa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qp: torch.T
     if dense:
         longest = max(int(vl.host[i + 1] - vl.host[i]) for i in range(vl.batch)) if vl.batch else 0
         topk = max(1, -(-longest // 128))
+        local_window, dilation = 0, 1           # every block up to the diagonal
     cfg = Config(Hq, Hkv, d, dp, q_block, topk, local_window, 128, softmax_scale or 0.0,
                  proxy_scale or 0.0, proxy_loss_weight,
-                 "bf16" if q.dtype == torch.bfloat16 else "f32")
+                 "bf16" if q.dtype == torch.bfloat16 else "f32", dilation)
     return _MSAFunction.apply(q, k, v, qp, kp, cfg, vl)

@@ -69,6 +69,11 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
   if (c.local_window < 0) return fail(MSA_ERR_INVALID_ARG, "local_window must be >= 0 (got %d)", c.local_window);
   if ((int64_t)c.topk + c.local_window > (1 << 20))
     return fail(MSA_ERR_INVALID_ARG, "topk + local_window too large");
+  if (c.dilation < 0) return fail(MSA_ERR_INVALID_ARG, "dilation must be >= 0 (got %d)", c.dilation);
+  const int64_t dil = c.dilation > 1 ? c.dilation : 1;
+  if ((int64_t)c.local_window * dil > (1 << 20))
+    return fail(MSA_ERR_INVALID_ARG, "local_window * dilation too large");
+  const int64_t span = (int64_t)c.local_window * dil;
   if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale) || !(c.proxy_scale >= 0.f) ||
       !std::isfinite(c.proxy_scale) || !std::isfinite(c.proxy_loss_weight))
     return fail(MSA_ERR_INVALID_ARG, "scales must be finite and >= 0, the loss weight finite");
@@ -89,9 +94,10 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
     units += ((L + 127) / 128 + 1) / 2;
     for (int64_t I = 0; I < nq; ++I) {
       const int64_t diag = I * c.q_block / 128;
-      if (diag + 1 <= (int64_t)c.topk + c.local_window) continue;
+      const int64_t pool = diag - span;           // candidates: blocks below the window's span
+      if (pool <= (int64_t)c.topk - 1) continue;  // all of them are taken, no score needed
       const int64_t rows = std::min<int64_t>(c.q_block, L - I * c.q_block);
-      pairs += rows * (diag - c.local_window) * 128;
+      pairs += rows * pool * 128;
     }
   }
   if (cu[vl->batch] != vl->total_tokens)
@@ -105,6 +111,7 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
   msa::Geo& g = P->g;
   g.Hq = c.heads_q; g.Hkv = c.heads_kv; g.G = G; g.D = c.head_dim; g.DP = c.proxy_dim;
   g.Bq = c.q_block; g.topk = c.topk; g.lw = c.local_window; g.stride = c.topk + c.local_window;
+  g.dil = (int32_t)dil; g.span = (int32_t)span;
   g.B = vl->batch; g.T = vl->total_tokens; g.nqb = (int32_t)nqb; g.nkb = (int32_t)nkb;
   g.max_nq = (int32_t)max_nq; g.cap = nqb * g.stride; g.score_elems = se; g.n_units = (int32_t)units;
   g.scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.f / std::sqrt((float)c.head_dim);

@@ -36,6 +36,7 @@ struct LdsLimitOnce {
 struct Geo {
   int32_t Hq, Hkv, G, D, DP;
   int32_t Bq, topk, lw, stride;      // stride = topk + local_window
+  int32_t dil, span;                 // window dilation, span = lw * dil
   int32_t B, T, nqb, nkb;            // documents, tokens, total query / KV blocks
   int32_t max_nq;                    // largest per-document query-block count
   int64_t cap;                       // k2q capacity per group = nqb * stride

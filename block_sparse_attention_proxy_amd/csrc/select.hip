@@ -174,8 +174,8 @@ __global__ __launch_bounds__(256) void proxy_scores_kernel(const T* __restrict__
   for (int pass = 0; pass < 2; ++pass) {
     const int tile = pass == 0 ? p : nt - 1 - p;
     if (pass == 1 && tile == p) break;
-    if (tile + 1 <= g.topk + g.lw) continue;      // every block is selected; nothing to score
-    const int ncand = tile - g.lw;
+    const int ncand = tile - g.span;              // blocks below the window's span
+    if (ncand <= g.topk - 1) continue;            // all of them are taken; nothing to score
 
     frag_t<T> A[4][KSL];
 #pragma unroll
@@ -392,11 +392,12 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
   int32_t* out = q2k_idx + ((int64_t)grp * g.nqb + QB) * g.stride;
   SelLds& w = lds[wave];
   int pos = 0;
-  if ((diag + 1) <= g.topk + g.lw) {              // every block up to the diagonal
-    for (int j = lane; j <= diag; j += 64) out[j] = kb0 + j;
-    pos = diag + 1;
+  const int pool = diag - g.span;                 // candidates: blocks below the window's span
+  if (pool <= g.topk - 1) {                       // all of them are taken
+    for (int j = lane; j < pool; j += 64) out[j] = kb0 + j;
+    pos = pool > 0 ? pool : 0;
   } else {
-    const int ncand = diag - g.lw;
+    const int ncand = pool;
     const float* srow = scores + (int64_t)grp * g.score_elems + g.s0[b] + (int64_t)I * nk;
     int rem = g.topk - 1;
     uint32_t prefix = 0, pmask = 0;
@@ -528,9 +529,12 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
         eq_taken += __popcll(eqm);
       }
     }
-    for (int j = lane; j <= g.lw; j += 64) out[pos + j] = kb0 + diag - g.lw + j;
-    pos += g.lw + 1;
   }
+  // forced: the diagonal and the window's blocks diag - i * dil (i <= lw, >= 0),
+  // ascending; every one lies above the candidates
+  const int nf = (g.lw < diag / g.dil ? g.lw : diag / g.dil) + 1;
+  for (int t = lane; t < nf; t += 64) out[pos + t] = kb0 + diag - (nf - 1 - t) * g.dil;
+  pos += nf;
   for (int j = pos + lane; j < g.stride; j += 64) out[j] = -1;
   if (lane == 0) q2k_cnt[(int64_t)grp * g.nqb + QB] = pos;
 }

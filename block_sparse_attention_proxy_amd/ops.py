@@ -32,12 +32,13 @@ class Config:
     proxy_scale: float = 0.0
     proxy_loss_weight: float = 1.0
     dtype: str = "bf16"
+    dilation: int = 1
 
     def to_c(self) -> MsaConfig:
         return MsaConfig(self.heads_q, self.heads_kv, self.head_dim, self.proxy_dim, self.kv_block,
                          self.q_block, self.topk, self.local_window, self.softmax_scale,
                          self.proxy_scale, self.proxy_loss_weight,
-                         _lib.MSA_BF16 if self.dtype == "bf16" else _lib.MSA_F32)
+                         _lib.MSA_BF16 if self.dtype == "bf16" else _lib.MSA_F32, self.dilation)
 
     @property
     def torch_dtype(self):

@@ -13,12 +13,16 @@
  *     (ai-minor, Why Does This Matter?; keelcrux "Flash-MSA: Ein Training mit
  *     einer Million Tokens", Le fait);
  *   - sequences are varlen-packed (socker-news summary, 要約);
- *   - the block pattern has a configurable window (keelcrux, Under the hood).
+ *   - the block pattern has a configurable window and dilation (keelcrux,
+ *     Under the hood).
  * Where the pages give no formula, these readings are used: one proxy head per
  * KV group shared by the group's query heads; block score = max over the
  * (query block x KV block) tile of the raw dot product <qp, kp>; the diagonal
  * block and `local_window` blocks before it are always selected and `topk`
- * counts the diagonal; exact score ties go to the lower block index; the
+ * counts the diagonal; with a dilation delta > 1 the forced window blocks are
+ * diag - delta, ..., diag - local_window * delta (those >= 0), candidates are
+ * the blocks below diag - local_window * delta, and the other blocks inside
+ * that span are never selected; exact score ties go to the lower block index; the
  * proxy gradient is that of lam * KL(T || Q) over the selected keys, with T the
  * group-mean main attention probabilities held constant and Q the proxy
  * softmax.
@@ -54,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 
 typedef enum {
   MSA_OK = 0,
@@ -79,6 +83,7 @@ typedef struct {
   float proxy_scale;         /* 0 -> 1/sqrt(dp) */
   float proxy_loss_weight;   /* lam; 0 is a valid weight */
   int32_t dtype;             /* msa_dtype of q, k, v, qp, kp, o, dout */
+  int32_t dilation;          /* stride of the forced window blocks; 0 or 1 = contiguous */
 } msa_config;
 
 typedef struct {
@@ -115,9 +120,10 @@ msa_status msa_get_layout(const msa_config* cfg, const msa_varlen* vl, msa_layou
  * score over 128-token KV blocks).
  * block_scores: fp32 [Hkv, score_elems]; document b's nq x nk rectangle is
  * row-major at a per-document offset.  Only the candidate entries of query
- * blocks that have candidates are written (J < diag - local_window, where
- * diag = floor(I * q_block / 128), and only when diag + 1 > topk + local_window);
- * the rest are left untouched and never read.
+ * blocks that have candidates are written (J < diag - local_window * delta,
+ * where diag = floor(I * q_block / 128) and delta the dilation, and only when
+ * there are more than topk - 1 such J); the rest are left untouched and never
+ * read.
  */
 msa_status msa_proxy_scores(const msa_config* cfg, const msa_varlen* vl, const void* qp,
                             const void* kp, float* block_scores, void* workspace,
@@ -128,7 +134,8 @@ msa_status msa_proxy_scores(const msa_config* cfg, const msa_varlen* vl, const v
  * inverted index (ai-minor, News Overview / Terminology: KV chosen in block
  * units).
  * q2k_idx int32 [Hkv, NQB, sel_stride]: ascending global KV block ids, -1 padded.
- * q2k_cnt int32 [Hkv, NQB]: min(topk + local_window, diag + 1).
+ * q2k_cnt int32 [Hkv, NQB]: min(topk - 1, candidates) + forced blocks; with
+ *         delta = 1 this is min(topk + local_window, diag + 1).
  * k2q_ptr int32 [Hkv, NKB + 1]: per-group CSR offsets into row g of k2q_idx.
  * k2q_idx int32 [Hkv, k2q_capacity]: ascending query-block ids per KV block;
  *         the unused tail of each row is -1.

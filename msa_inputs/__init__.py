@@ -63,6 +63,7 @@ class Workload:
     doc_mode: str = "fixed"   # "fixed" or "loguniform"
     total_tokens: int = 0     # for doc_mode == "loguniform"
     proxy_loss_weight: float = 1.0
+    dilation: int = 1         # stride of the forced window blocks
 
     @property
     def group(self) -> int:

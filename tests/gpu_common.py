@@ -26,9 +26,9 @@ def log(*a):
 def cfgs(w: Workload, **over):
     w = replace(w, **over) if over else w
     c = msa.Config(w.heads_q, w.heads_kv, w.head_dim, w.proxy_dim, w.q_block, w.topk,
-                   w.local_window, 128, 0.0, 0.0, w.proxy_loss_weight, w.dtype)
+                   w.local_window, 128, 0.0, 0.0, w.proxy_loss_weight, w.dtype, w.dilation)
     o = om.Config(w.heads_q, w.heads_kv, w.head_dim, w.proxy_dim, w.q_block, w.topk,
-                  w.local_window, 128, None, None, w.proxy_loss_weight)
+                  w.local_window, 128, None, None, w.proxy_loss_weight, w.dilation)
     return w, c, o
 
 

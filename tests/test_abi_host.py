@@ -23,17 +23,20 @@ def test_exports_match_header():
     assert declared == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.msa_abi_version() == 1
+    assert lib.msa_abi_version() == _lib.ABI_VERSION == 2
+    assert ctypes.sizeof(_lib.MsaConfig) == 13 * 4
     assert lib.msa_status_string(0).decode() == "ok"
 
 
-@pytest.mark.parametrize("seqlens,q_block,topk,w", [((2048,), 64, 4, 0), ((3000, 0, 129, 5000), 128, 3, 2),
-                                                    ((32768,), 64, 16, 0), ((700, 64, 1), 64, 1, 0)])
-def test_layout_matches_oracle_grid(seqlens, q_block, topk, w):
+@pytest.mark.parametrize("seqlens,q_block,topk,w,dil", [((2048,), 64, 4, 0, 1), ((3000, 0, 129, 5000), 128, 3, 2, 1),
+                                                        ((32768,), 64, 16, 0, 1), ((700, 64, 1), 64, 1, 0, 1),
+                                                        ((3000, 0, 129, 5000), 128, 3, 2, 3),
+                                                        ((32768,), 64, 16, 4, 2), ((4000,), 64, 2, 1, 0)])
+def test_layout_matches_oracle_grid(seqlens, q_block, topk, w, dil):
     cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
-    cfg = msa.Config(8, 2, 64, 32, q_block, topk, w, dtype="f32")
+    cfg = msa.Config(8, 2, 64, 32, q_block, topk, w, dtype="f32", dilation=dil)
     lay = msa.msa_get_layout(cfg, msa.Varlen(torch.from_numpy(cu)))
-    ocfg = om.Config(8, 2, 64, 32, q_block, topk, w)
+    ocfg = om.Config(8, 2, 64, 32, q_block, topk, w, dilation=max(dil, 1))
     docs = om.doc_grid(cu, ocfg)
     nqb, nkb, ns = om.totals(docs)
     assert lay["total_qblocks"] == nqb and lay["total_kvblocks"] == nkb and lay["score_elems"] == ns
@@ -61,6 +64,8 @@ def _err(fn):
     (dict(kv_block=64), _lib.MSA_ERR_UNSUPPORTED),
     (dict(topk=0), _lib.MSA_ERR_INVALID_ARG),
     (dict(local_window=-1), _lib.MSA_ERR_INVALID_ARG),
+    (dict(dilation=-1), _lib.MSA_ERR_INVALID_ARG),
+    (dict(local_window=1 << 12, dilation=1 << 9), _lib.MSA_ERR_INVALID_ARG),
     (dict(heads_q=24, heads_kv=4), _lib.MSA_ERR_UNSUPPORTED),   # group of 6
     (dict(dtype="f32"), _lib.MSA_ERR_UNSUPPORTED),              # fp32 only at d = 64
 ])

@@ -22,6 +22,9 @@ SMALL = {
     "l512k-geom-window": (WORKLOADS["layer-512k-window2"], dict(topk=3), (1900, 2100, 64)),
     "l128k-geom-gqa8": (WORKLOADS["layer-128k-gqa8"], dict(topk=3), (1700,)),
     "varlen-geom": (WORKLOADS["varlen-1m-packed"], dict(topk=5), (640, 0, 1500, 77, 1200)),
+    # dilated windows: forced blocks on the window's stride
+    "l32k-geom-dilated": (WORKLOADS["layer-32k"], dict(topk=3, local_window=2, dilation=3), (2500, 1277)),
+    "l512k-geom-dilated": (WORKLOADS["layer-512k-window2"], dict(topk=3, dilation=2), (1900, 2100, 64)),
 }
 
 
@@ -48,7 +51,7 @@ def test_selection_identical_scores(name):
     check_inverse(res, ocfg)
 
 
-@pytest.mark.parametrize("name", ["l32k-geom", "l512k-geom-window", "varlen-geom"])
+@pytest.mark.parametrize("name", ["l32k-geom", "l512k-geom-window", "varlen-geom", "l32k-geom-dilated"])
 def test_selection_exact_inputs_end_to_end(name):
     """qp, kp in {-1, -1/2, 0, 1/2, 1}: every score is exact in fp32, so the GPU's
     scores and block lists equal the fp64 oracle's bit for bit."""
