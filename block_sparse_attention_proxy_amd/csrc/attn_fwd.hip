@@ -382,6 +382,115 @@ __global__ __launch_bounds__(256) void proxy_lse_kernel(const T* __restrict__ qp
   if (hi == 0 && qpos < L) lse_p[(int64_t)grp * g.T + t0 + qpos] = (mp + log2f(lt)) * LN2;
 }
 
+// Proxy log-sum-exp for 128-row query blocks: a workgroup owns one (group,
+// query block) and wave w its queries 32w .. 32w + 31, so all four waves walk
+// the same list.  The kp rows of each selected block are copied once per
+// workgroup into an LDS ring (three slots, two blocks in flight) and read as
+// A fragments by every wave; one max and one rescale per block.
+template <typename T, int DP>
+struct LseCfg {
+  typedef Tile<T, DP> TP;
+  static constexpr int NBUF = 3, AHEAD = 2;
+  static constexpr int SLOT = 128 * DP * (int)sizeof(T);          // one KV block of kp rows
+  static constexpr int ROWS_PER_COPY = 64 / TP::CPR;               // rows one wave copy covers
+  static constexpr int COPIES = 128 / (4 * ROWS_PER_COPY);         // per wave per block
+  static constexpr int LDS_BYTES = NBUF * SLOT;
+  static_assert(COPIES >= 1 && 128 % (4 * ROWS_PER_COPY) == 0, "copy split");
+};
+
+template <typename T, int DP>
+__global__ __launch_bounds__(256) void proxy_lse128_kernel(const T* __restrict__ qp,
+                                                           const T* __restrict__ kp,
+                                                           const int32_t* __restrict__ q2k_idx,
+                                                           const int32_t* __restrict__ q2k_cnt,
+                                                           float* __restrict__ lse_p, Geo g) {
+  typedef LseCfg<T, DP> C;
+  typedef typename C::TP TP;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hi = lane >> 5;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);   // the grid is exactly Hkv * nqb
+  const int grp = item / g.nqb;
+  const int QB = item % g.nqb;
+  const int b = g.qdoc[QB];
+  const int I = QB - g.qb0[b];
+  const int t0 = g.cu[b];
+  const int L = g.cu[b + 1] - t0;
+  const int kb0 = g.kb0[b];
+  const int diag = (I * 128) >> 7;
+  const int q0 = I * 128 + wave * 32;            // may lie past the document end: the wave
+  const int qpos = q0 + col;                     // still copies and waits, its result is dropped
+  const int qrow = qpos < L ? qpos : L - 1;
+  frag_t<T> QPf[DP / 16];
+  {
+    const T* sp = qp + ((int64_t)(t0 + qrow) * g.Hkv + grp) * DP + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < DP / 16; ++ks) QPf[ks] = ld8(sp + ks * 16);
+  }
+  const int64_t rowi = (int64_t)grp * g.nqb + QB;
+  const int cnt = q2k_cnt[rowi];
+  const int32_t* sel = q2k_idx + rowi * g.stride;
+  // the register loads complete before the copies, so the waits count copies only
+  wait_vmcnt<0>();
+  const uint32_t lds0 = lds_offset(smem_raw);
+  auto issue = [&](int si) __attribute__((always_inline)) {
+    const int J = sel[si < cnt ? si : cnt - 1] - kb0;    // past the end: the last block again
+    const uint32_t base = lds0 + (uint32_t)((si % C::NBUF) * C::SLOT);
+#pragma unroll
+    for (int j = 0; j < C::COPIES; ++j) {
+      const int rfirst = (wave * C::COPIES + j) * C::ROWS_PER_COPY;
+      const int r = rfirst + lane / TP::CPR, p = lane % TP::CPR;
+      const int key = J * 128 + r < L ? J * 128 + r : L - 1;
+      dma16(kp + ((int64_t)(t0 + key) * g.Hkv + grp) * DP + swz<TP::CPR>(r, p) * TP::EPC,
+            base + (uint32_t)(rfirst * DP * (int)sizeof(T)));
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < C::AHEAD; ++j) issue(j);
+  float mp = NEG_BIG, lp = 0.f;
+  for (int si = 0; si < cnt; ++si) {
+    wait_vmcnt<(C::AHEAD - 1) * C::COPIES>();   // this block's copies have landed
+    __syncthreads();                             // ... everyone's, and the slot refilled next is free
+    issue(si + C::AHEAD);
+    const T* KPs = reinterpret_cast<const T*>(smem_raw + (si % C::NBUF) * C::SLOT);
+    const int J = sel[si] - kb0;
+    const bool need_mask = J == diag;
+    // key tiles that hold a key <= the wave's last query
+    const int lim = q0 + 31 - J * 128;
+    const int ntile = lim >= 96 ? 4 : (lim < 0 ? 0 : lim / 32 + 1);
+    f32x16 Y[4];
+    float mx = NEG_BIG;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      if (kt >= ntile) break;
+      Y[kt] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < DP / 16; ++ks) mma(Y[kt], TP::row8(KPs, kt * 32 + col, ks * 16 + hi * 8), QPf[ks]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = Y[kt][i] * g.pscale_log2;
+        if (need_mask && J * 128 + kt * 32 + acc_row(i, lane) > qpos) x = -INFINITY;
+        Y[kt][i] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(mp, mx);
+    float ls = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      if (kt >= ntile) break;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ls += __builtin_amdgcn_exp2f(Y[kt][i] - mnew);
+    }
+    lp = lp * __builtin_amdgcn_exp2f(mp - mnew) + ls;
+    mp = mnew;
+  }
+  wait_vmcnt<0>();                               // copies issued past the last block
+  const float lt = lp + __shfl_xor(lp, 32, 64);
+  if (hi == 0 && qpos < L) lse_p[(int64_t)grp * g.T + t0 + qpos] = (mp + log2f(lt)) * LN2;
+}
+
 template <typename T, int D, int DP>
 static hipError_t fwd_dispatch(const Geo& g, const void* q, const void* k, const void* v,
                                const void* qp, const void* kp, const int32_t* q2k_idx,
@@ -403,8 +512,15 @@ static hipError_t fwd_dispatch(const Geo& g, const void* q, const void* k, const
                      (const T*)v, q2k_idx, q2k_cnt, (T*)o, lse, g); }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int per_wg = 4 / (g.Bq / 32);
   const int64_t nrow = (int64_t)g.Hkv * g.nqb;
+  if (g.Bq == 128) {
+    constexpr int lse_lds = LseCfg<T, DP>::LDS_BYTES;
+    { ProfScope _ps("proxy_lse", s);
+    hipLaunchKernelGGL((proxy_lse128_kernel<T, DP>), dim3((unsigned)nrow), dim3(256), lse_lds,
+                       s, (const T*)qp, (const T*)kp, q2k_idx, q2k_cnt, lse_p, g); }
+    return hipGetLastError();
+  }
+  const int per_wg = 4 / (g.Bq / 32);
   { ProfScope _ps("proxy_lse", s);
   hipLaunchKernelGGL((proxy_lse_kernel<T, DP>), dim3((unsigned)((nrow + per_wg - 1) / per_wg)), dim3(256),
                      0, s, (const T*)qp, (const T*)kp, q2k_idx, q2k_cnt, lse_p, g); }
@@ -432,6 +548,9 @@ int fwd_kernels(KernelEntry* out, int max) {
       {"proxy_lse<bf16,dp64>", (const void*)proxy_lse_kernel<bf16, 64>, 256, 0},
       {"proxy_lse<bf16,dp32>", (const void*)proxy_lse_kernel<bf16, 32>, 256, 0},
       {"proxy_lse<f32,dp32>", (const void*)proxy_lse_kernel<float, 32>, 256, 0},
+      {"proxy_lse128<bf16,dp64>", (const void*)proxy_lse128_kernel<bf16, 64>, 256, LseCfg<bf16, 64>::LDS_BYTES},
+      {"proxy_lse128<bf16,dp32>", (const void*)proxy_lse128_kernel<bf16, 32>, 256, LseCfg<bf16, 32>::LDS_BYTES},
+      {"proxy_lse128<f32,dp32>", (const void*)proxy_lse128_kernel<float, 32>, 256, LseCfg<float, 32>::LDS_BYTES},
   };
   int n = (int)(sizeof(all) / sizeof(all[0]));
   for (int i = 0; i < n && i < max; ++i) out[i] = all[i];
