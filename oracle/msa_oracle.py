@@ -33,6 +33,9 @@ What the pages fix:
 Readings (the pages give no formulas):
   R1  One proxy head per KV group (Hp = Hkv); its block choice is shared by the
       G query heads of the group.  Query head h uses group h // G.
+  R1s The shared-proxy variant (Hp = 1, proxy_heads = 1): one proxy head whose
+      block choice every query head uses; in R8, T is then the mean of the main
+      probabilities over all Hq heads (the heads that share the choice).
   R2  Proxy block score S[g, I, J] = max over valid query rows t of block I and
       keys u of block J of the raw dot product <qp[t, g], kp[u, g]> (unscaled:
       a positive scale does not change a ranking).
@@ -88,6 +91,19 @@ class Config:
     proxy_scale: Optional[float] = None
     proxy_loss_weight: float = 1.0
     dilation: int = 1
+    proxy_heads: int = 0      # 0: one per KV group (R1); 1: one shared proxy head (R1s)
+
+    @property
+    def Hp(self) -> int:
+        return 1 if self.proxy_heads == 1 else self.heads_kv
+
+    def proxy_of(self, g: int) -> int:
+        """Proxy head whose choice KV group g uses."""
+        return 0 if self.proxy_heads == 1 else g
+
+    def groups_of(self, p: int) -> List[int]:
+        """KV groups that use proxy head p."""
+        return list(range(self.heads_kv)) if self.proxy_heads == 1 else [p]
 
     @property
     def G(self) -> int:
@@ -203,8 +219,8 @@ def proxy_block_scores(qp, kp, cu_seqlens, cfg: Config) -> np.ndarray:
     document); entries that are not candidates are -inf."""
     docs = doc_grid(cu_seqlens, cfg)
     _, _, ns = totals(docs)
-    S = np.full((cfg.heads_kv, ns), -np.inf)
-    for g in range(cfg.heads_kv):
+    S = np.full((cfg.Hp, ns), -np.inf)
+    for g in range(cfg.Hp):
         for doc in docs:
             for I in range(doc.nq):
                 r = proxy_row_scores(qp, kp, doc, g, I, cfg)
@@ -239,9 +255,9 @@ def select_blocks(scores: np.ndarray, cu_seqlens, cfg: Config):
     q2k_cnt [Hp, NQB]."""
     docs = doc_grid(cu_seqlens, cfg)
     nqb, _, _ = totals(docs)
-    idx = np.full((cfg.heads_kv, nqb, cfg.sel_stride), -1, dtype=np.int32)
-    cnt = np.zeros((cfg.heads_kv, nqb), dtype=np.int32)
-    for g in range(cfg.heads_kv):
+    idx = np.full((cfg.Hp, nqb, cfg.sel_stride), -1, dtype=np.int32)
+    cnt = np.zeros((cfg.Hp, nqb), dtype=np.int32)
+    for g in range(cfg.Hp):
         for doc in docs:
             for I in range(doc.nq):
                 nc = candidate_count(I, cfg)
@@ -313,8 +329,8 @@ def qblock_forward(q, k, v, qp, kp, doc: Doc, g: int, I: int, sel_global, cfg: C
         out["P"].append(P)
         out["O"].append(P @ Vg)
         out["LSE"].append(lse)
-    Qp = qp[rows, g, :].astype(np.float64)
-    Kp = kp[keys, g, :].astype(np.float64)
+    Qp = qp[rows, cfg.proxy_of(g), :].astype(np.float64)
+    Kp = kp[keys, cfg.proxy_of(g), :].astype(np.float64)
     y = np.where(causal, cfg.pscale * (Qp @ Kp.T), -np.inf)
     lse_p, Qprob = _softmax_rows(y)
     out.update(y=y, Q=Qprob, LSE_p=lse_p)
@@ -327,7 +343,8 @@ def qblock_backward(fw, q, k, v, qp, kp, dO, g: int, cfg: Config, O_for_D=None):
     Main (R7): D = <dO, O>, dP = dO v^T, dS = P (dP - D), dQ = s dS k,
     dK = s dS^T q, dV = P^T dO (summed over the group's heads).
     Proxy (R8): T = mean over the group's heads of P; dY = lam (Q - T);
-    dqp = s_p dY kp; dkp = s_p dY^T qp.  Fused with the main backward in the
+    dqp = s_p dY kp; dkp = s_p dY^T qp (the per-group reading R1; with a
+    shared proxy head the layer driver forms T over all heads instead).  Fused with the main backward in the
     sense of the pages [AIM Why Does This Matter?]: both use the same P."""
     rows, keys = fw["rows"], fw["keys"]
     Kg = k[keys, g, :].astype(np.float64)
@@ -345,14 +362,22 @@ def qblock_backward(fw, q, k, v, qp, kp, dO, g: int, cfg: Config, O_for_D=None):
         res["dQ"].append(cfg.scale * (dS @ Kg))
         res["dK"] += cfg.scale * (dS.T @ Qh)
         res["dV"] += P.T @ dOh
-    T = sum(fw["P"]) / cfg.G
-    dY = cfg.proxy_loss_weight * (fw["Q"] - T)
-    Qp = qp[rows, g, :].astype(np.float64)
-    Kp = kp[keys, g, :].astype(np.float64)
-    res["dqp"] = cfg.pscale * (dY @ Kp)
-    res["dkp"] = cfg.pscale * (dY.T @ Qp)
-    res["T"] = T
+    res.update(proxy_backward([fw], qp, kp, cfg.proxy_of(g), cfg))
     return res
+
+
+def proxy_backward(fws, qp, kp, p: int, cfg: Config):
+    """Proxy gradient of proxy head p for one query block (R8): T = mean of the
+    main probabilities over every head that uses p's choice (the forward
+    quantities of those heads' groups are in ``fws``, sharing rows and keys);
+    dY = lam (Q - T); dqp = s_p dY kp; dkp = s_p dY^T qp."""
+    rows, keys = fws[0]["rows"], fws[0]["keys"]
+    P = [Ph for fw in fws for Ph in fw["P"]]
+    T = sum(P) / len(P)
+    dY = cfg.proxy_loss_weight * (fws[0]["Q"] - T)
+    Qp = qp[rows, p, :].astype(np.float64)
+    Kp = kp[keys, p, :].astype(np.float64)
+    return {"dqp": cfg.pscale * (dY @ Kp), "dkp": cfg.pscale * (dY.T @ Qp), "T": T}
 
 
 # --------------------------------------------------------------------------
@@ -368,16 +393,16 @@ def forward(q, k, v, qp, kp, cu_seqlens, q2k_idx, q2k_cnt, cfg: Config):
     T = q.shape[0]
     O = np.zeros((T, cfg.heads_q, cfg.head_dim))
     LSE = np.zeros((cfg.heads_q, T))
-    LSEp = np.zeros((cfg.heads_kv, T))
+    LSEp = np.zeros((cfg.Hp, T))
     for doc in doc_grid(cu_seqlens, cfg):
         for g in range(cfg.heads_kv):
             for I in range(doc.nq):
                 fw = qblock_forward(q, k, v, qp, kp, doc, g, I,
-                                    _sel_of(q2k_idx, q2k_cnt, g, doc.qb0 + I), cfg)
+                                    _sel_of(q2k_idx, q2k_cnt, cfg.proxy_of(g), doc.qb0 + I), cfg)
                 for j, h in enumerate(range(g * cfg.G, (g + 1) * cfg.G)):
                     O[fw["rows"], h, :] = fw["O"][j]
                     LSE[h, fw["rows"]] = fw["LSE"][j]
-                LSEp[g, fw["rows"]] = fw["LSE_p"]
+                LSEp[cfg.proxy_of(g), fw["rows"]] = fw["LSE_p"]
     return O, LSE, LSEp
 
 
@@ -388,13 +413,15 @@ def backward(q, k, v, qp, kp, dO, cu_seqlens, q2k_idx, q2k_cnt, cfg: Config, O_f
     dq = np.zeros((T, cfg.heads_q, cfg.head_dim))
     dk = np.zeros((T, cfg.heads_kv, cfg.head_dim))
     dv = np.zeros((T, cfg.heads_kv, cfg.head_dim))
-    dqp = np.zeros((T, cfg.heads_kv, cfg.proxy_dim))
-    dkp = np.zeros((T, cfg.heads_kv, cfg.proxy_dim))
+    dqp = np.zeros((T, cfg.Hp, cfg.proxy_dim))
+    dkp = np.zeros((T, cfg.Hp, cfg.proxy_dim))
     for doc in doc_grid(cu_seqlens, cfg):
-        for g in range(cfg.heads_kv):
-            for I in range(doc.nq):
+        for I in range(doc.nq):
+            fws = {}
+            for g in range(cfg.heads_kv):
                 fw = qblock_forward(q, k, v, qp, kp, doc, g, I,
-                                    _sel_of(q2k_idx, q2k_cnt, g, doc.qb0 + I), cfg)
+                                    _sel_of(q2k_idx, q2k_cnt, cfg.proxy_of(g), doc.qb0 + I), cfg)
+                fws[g] = fw
                 od = None
                 if O_for_D is not None:
                     od = [O_for_D[fw["rows"], h, :].astype(np.float64)
@@ -405,26 +432,34 @@ def backward(q, k, v, qp, kp, dO, cu_seqlens, q2k_idx, q2k_cnt, cfg: Config, O_f
                     dq[rows, h, :] = bw["dQ"][j]
                 dk[keys, g, :] += bw["dK"]          # keys are distinct within a block
                 dv[keys, g, :] += bw["dV"]
-                dqp[rows, g, :] = bw["dqp"]
-                dkp[keys, g, :] += bw["dkp"]
+            for p in range(cfg.Hp):
+                pb = proxy_backward([fws[g] for g in cfg.groups_of(p)], qp, kp, p, cfg)
+                rows, keys = fws[cfg.groups_of(p)[0]]["rows"], fws[cfg.groups_of(p)[0]]["keys"]
+                dqp[rows, p, :] = pb["dqp"]
+                dkp[keys, p, :] += pb["dkp"]
     return dq, dk, dv, dqp, dkp
 
 
 def losses(q, k, v, qp, kp, dO, cu_seqlens, q2k_idx, q2k_cnt, cfg: Config, T_fixed=None):
     """Scalar objectives whose gradients the backward returns (for finite
     differences).  L_main = sum <dO, O>.  L_aux = lam sum_{g,i} sum_u
-    T (ln T - ln Q) with T held fixed (0 ln 0 = 0).  ``T_fixed`` maps
-    (doc index, g, I) to the T matrix to hold; by default T comes from the
-    given q, k."""
+    T (ln T - ln Q) with T held fixed (0 ln 0 = 0), one term per proxy head.
+    ``T_fixed`` maps (doc index, proxy head, I) to the T matrix to hold; by
+    default T comes from the given q, k."""
     Lm, La = 0.0, 0.0
     for bi, doc in enumerate(doc_grid(cu_seqlens, cfg)):
-        for g in range(cfg.heads_kv):
-            for I in range(doc.nq):
+        for I in range(doc.nq):
+            fws = {}
+            for g in range(cfg.heads_kv):
                 fw = qblock_forward(q, k, v, qp, kp, doc, g, I,
-                                    _sel_of(q2k_idx, q2k_cnt, g, doc.qb0 + I), cfg)
+                                    _sel_of(q2k_idx, q2k_cnt, cfg.proxy_of(g), doc.qb0 + I), cfg)
+                fws[g] = fw
                 for j, h in enumerate(range(g * cfg.G, (g + 1) * cfg.G)):
                     Lm += float((dO[fw["rows"], h, :].astype(np.float64) * fw["O"][j]).sum())
-                T = sum(fw["P"]) / cfg.G if T_fixed is None else T_fixed[(bi, g, I)]
+            for p in range(cfg.Hp):
+                P = [Ph for g in cfg.groups_of(p) for Ph in fws[g]["P"]]
+                T = sum(P) / len(P) if T_fixed is None else T_fixed[(bi, p, I)]
+                fw = fws[cfg.groups_of(p)[0]]
                 lnQ = np.where(fw["mask"], fw["y"] - fw["LSE_p"][:, None], 0.0)
                 lnT = np.log(np.where(T > 0, T, 1.0))
                 La += cfg.proxy_loss_weight * float((T * (lnT - lnQ)).sum())
@@ -432,14 +467,17 @@ def losses(q, k, v, qp, kp, dO, cu_seqlens, q2k_idx, q2k_cnt, cfg: Config, T_fix
 
 
 def group_mean_probs(q, k, v, qp, kp, cu_seqlens, q2k_idx, q2k_cnt, cfg: Config):
-    """T for every (doc index, g, I), for holding it fixed in L_aux."""
+    """T for every (doc index, proxy head, I), for holding it fixed in L_aux."""
     out = {}
     for bi, doc in enumerate(doc_grid(cu_seqlens, cfg)):
-        for g in range(cfg.heads_kv):
-            for I in range(doc.nq):
-                fw = qblock_forward(q, k, v, qp, kp, doc, g, I,
-                                    _sel_of(q2k_idx, q2k_cnt, g, doc.qb0 + I), cfg)
-                out[(bi, g, I)] = sum(fw["P"]) / cfg.G
+        for I in range(doc.nq):
+            for p in range(cfg.Hp):
+                P = []
+                for g in cfg.groups_of(p):
+                    fw = qblock_forward(q, k, v, qp, kp, doc, g, I,
+                                        _sel_of(q2k_idx, q2k_cnt, p, doc.qb0 + I), cfg)
+                    P += fw["P"]
+                out[(bi, p, I)] = sum(P) / len(P)
     return out
 
 
@@ -478,6 +516,7 @@ def sampled_query_side(q, k, v, qp, kp, dO, cu_seqlens, q2k_idx, q2k_cnt, cfg: C
                        samples: List[Tuple[int, int]], O_for_D=None):
     """For sampled (g, global query block) pairs: O, LSE, LSE_p, dQ and dqp of
     that block's rows, computed from the definition."""
+    assert cfg.proxy_heads != 1, "sampled evaluation covers one proxy head per group"
     docs = doc_grid(cu_seqlens, cfg)
     out = []
     for g, QB in samples:
@@ -499,6 +538,7 @@ def sampled_key_side(q, k, v, qp, kp, dO, cu_seqlens, q2k_idx, q2k_cnt, cfg: Con
                      samples: List[Tuple[int, int]], O_for_D=None):
     """For sampled (g, global KV block) pairs: dK, dV and dkp of that block's
     keys, summed over every query block whose selection holds it."""
+    assert cfg.proxy_heads != 1, "sampled evaluation covers one proxy head per group"
     docs = doc_grid(cu_seqlens, cfg)
     out = []
     for g, KB in samples:

@@ -290,3 +290,85 @@ def test_sampled_matches_full():
         np.testing.assert_allclose(r["dK"], full["dk"][r["keys"], r["g"]], atol=1e-12)
         np.testing.assert_allclose(r["dV"], full["dv"][r["keys"], r["g"]], atol=1e-12)
         np.testing.assert_allclose(r["dkp"], full["dkp"][r["keys"], r["g"]], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# the shared proxy head (one proxy head for all KV groups)
+# ---------------------------------------------------------------------------
+
+def _shared_setup(seed, heads_q=4, heads_kv=2):
+    rng = np.random.default_rng(seed)
+    cfg = _cfg(heads_q=heads_q, heads_kv=heads_kv, topk=2, q_block=64, local_window=1, head_dim=8,
+               proxy_dim=4, proxy_heads=1)
+    seqlens = (450, 300)
+    T = sum(seqlens)
+    q, k, v, _, _, dO = _inputs(rng, T, cfg, scale=0.7)
+    qp = 0.7 * rng.standard_normal((T, 1, cfg.proxy_dim))
+    kp = 0.7 * rng.standard_normal((T, 1, cfg.proxy_dim))
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    idx, cnt = _select(qp, kp, cu, cfg)
+    return rng, cfg, cu, idx, cnt, [q, k, v, qp, kp, dO]
+
+
+def test_shared_proxy_with_one_group_is_the_per_group_reading():
+    """With one KV group the shared head and the per-group head are the same."""
+    _, cfg, cu, idx, cnt, X = _shared_setup(31, heads_q=3, heads_kv=1)
+    per = om.Config(**{**cfg.__dict__, "proxy_heads": 0})
+    a = om.run_all(*X, cu, cfg)
+    b = om.run_all(*X, cu, per)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_shared_proxy_is_the_mean_of_replicated_groups():
+    """T over all Hq heads is the mean of the groups' means, and the proxy
+    gradients are linear in T: the shared head's dqp, dkp equal the average
+    over groups of the per-group reading run with qp, kp and the block lists
+    copied to every group; LSE_p and every main output are unchanged."""
+    _, cfg, cu, idx, cnt, X = _shared_setup(32)
+    q, k, v, qp, kp, dO = X
+    Hkv = cfg.heads_kv
+    per = om.Config(**{**cfg.__dict__, "proxy_heads": 0})
+    rep = [np.repeat(qp, Hkv, axis=1), np.repeat(kp, Hkv, axis=1)]
+    idx_r, cnt_r = np.repeat(idx, Hkv, axis=0), np.repeat(cnt, Hkv, axis=0)
+    O, LSE, LSEp = om.forward(q, k, v, qp, kp, cu, idx, cnt, cfg)
+    O2, LSE2, LSEp2 = om.forward(q, k, v, *rep, cu, idx_r, cnt_r, per)
+    assert np.array_equal(O, O2) and np.array_equal(LSE, LSE2)
+    for g in range(Hkv):
+        assert np.array_equal(LSEp[0], LSEp2[g])
+    g1 = om.backward(q, k, v, qp, kp, dO, cu, idx, cnt, cfg)
+    g2 = om.backward(q, k, v, *rep, dO, cu, idx_r, cnt_r, per)
+    for a, b in zip(g1[:3], g2[:3]):
+        assert np.array_equal(a, b)
+    np.testing.assert_allclose(g1[3][:, 0], g2[3].mean(axis=1), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(g1[4][:, 0], g2[4].mean(axis=1), rtol=0, atol=1e-13)
+    # and it is not any single group's reading
+    assert np.abs(g1[3][:, 0] - g2[3][:, 0]).max() > 1e-3
+
+
+def test_shared_proxy_finite_differences():
+    rng, cfg, cu, idx, cnt, X = _shared_setup(33)
+    _, _, _, dqp, dkp = om.backward(*X, cu, idx, cnt, cfg)
+    assert dqp.shape[1] == 1 and dkp.shape[1] == 1
+    Tfix = om.group_mean_probs(*X[:5], cu, idx, cnt, cfg)
+    h = 1e-5
+    for which, G in ((3, dqp), (4, dkp)):
+        for _ in range(6):
+            pos = tuple(int(rng.integers(0, s)) for s in X[which].shape)
+            plus = [x.copy() for x in X]
+            minus = [x.copy() for x in X]
+            plus[which][pos] += h
+            minus[which][pos] -= h
+            fd = (om.losses(*plus, cu, idx, cnt, cfg, T_fixed=Tfix)[1]
+                  - om.losses(*minus, cu, idx, cnt, cfg, T_fixed=Tfix)[1]) / (2 * h)
+            assert abs(fd - G[pos]) < 1e-6 * max(1.0, abs(fd)), (which, pos, fd, G[pos])
+
+
+def test_shared_proxy_invariants():
+    """sum_u dkp = 0 per document (rows of dY sum to zero); T is a distribution."""
+    _, cfg, cu, idx, cnt, X = _shared_setup(34)
+    _, _, _, _, dkp = om.backward(*X, cu, idx, cnt, cfg)
+    for b in range(len(cu) - 1):
+        np.testing.assert_allclose(dkp[int(cu[b]):int(cu[b + 1]), 0].sum(0), 0, atol=1e-10)
+    for T in om.group_mean_probs(*X[:5], cu, idx, cnt, cfg).values():
+        np.testing.assert_allclose(T.sum(1), 1.0, atol=1e-12)
