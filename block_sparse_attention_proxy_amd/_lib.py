@@ -17,7 +17,7 @@ MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_HIP, MSA_ERR_WORKSPACE
 MSA_BF16, MSA_F32 = 0, 1
 
 # Every symbol include/msa.h declares.
-ABI_VERSION = 2        # include/msa.h MSA_ABI_VERSION; msa_config layout below
+ABI_VERSION = 3        # include/msa.h MSA_ABI_VERSION; msa_config / msa_layout below
 EXPORTS = ("msa_abi_version", "msa_status_string", "msa_last_error", "msa_get_layout",
            "msa_proxy_scores", "msa_select_blocks", "msa_fwd", "msa_bwd", "msa_kernel_count",
            "msa_kernel_info", "msa_profile_enable", "msa_profile_collect", "msa_profile_entry")
@@ -28,7 +28,7 @@ class MsaConfig(ctypes.Structure):
                 ("proxy_dim", c_int32), ("kv_block", c_int32), ("q_block", c_int32),
                 ("topk", c_int32), ("local_window", c_int32), ("softmax_scale", c_float),
                 ("proxy_scale", c_float), ("proxy_loss_weight", c_float), ("dtype", c_int32),
-                ("dilation", c_int32)]
+                ("dilation", c_int32), ("proxy_heads", c_int32)]
 
 
 class MsaVarlen(ctypes.Structure):
@@ -39,7 +39,7 @@ class MsaVarlen(ctypes.Structure):
 class MsaLayout(ctypes.Structure):
     _fields_ = [("total_qblocks", c_int64), ("total_kvblocks", c_int64), ("score_elems", c_int64),
                 ("sel_stride", c_int64), ("k2q_capacity", c_int64), ("scored_pairs", c_int64),
-                ("max_qblocks_doc", c_int64), ("workspace_bytes", c_int64)]
+                ("max_qblocks_doc", c_int64), ("workspace_bytes", c_int64), ("proxy_heads", c_int64)]
 
     def as_dict(self):
         return {name: int(getattr(self, name)) for name, _ in self._fields_}

@@ -48,10 +48,12 @@ def msa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qp: torch.T
                   local_window: int = 0, softmax_scale: Optional[float] = None,
                   proxy_scale: Optional[float] = None, proxy_loss_weight: float = 1.0,
                   cu_seqlens_host: Optional[Sequence[int]] = None, dense: bool = False,
-                  dilation: int = 1):
+                  dilation: int = 1, proxy_heads: int = 0):
     """Block-sparse GQA attention with proxy-head block selection.
 
-    q [T, Hq, d]; k, v [T, Hkv, d]; qp, kp [T, Hkv, dp]; cu_seqlens int32 [B+1].
+    q [T, Hq, d]; k, v [T, Hkv, d]; qp, kp [T, Hp, dp]; cu_seqlens int32 [B+1].
+    Hp = Hkv (one proxy head per KV group, ``proxy_heads=0``) or 1 (one proxy
+    head shared by every group, ``proxy_heads=1``).
     ``dense=True`` selects every causal block (top-k = all blocks; window and
     dilation are then moot).  ``dilation`` spaces the forced window blocks (1 = contiguous window).
     """
@@ -64,5 +66,5 @@ def msa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, qp: torch.T
         local_window, dilation = 0, 1           # every block up to the diagonal
     cfg = Config(Hq, Hkv, d, dp, q_block, topk, local_window, 128, softmax_scale or 0.0,
                  proxy_scale or 0.0, proxy_loss_weight,
-                 "bf16" if q.dtype == torch.bfloat16 else "f32", dilation)
+                 "bf16" if q.dtype == torch.bfloat16 else "f32", dilation, proxy_heads)
     return _MSAFunction.apply(q, k, v, qp, kp, cfg, vl)

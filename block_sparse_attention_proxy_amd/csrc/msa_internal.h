@@ -66,6 +66,12 @@ struct Work {
 };
 
 hipError_t launch_meta(const Geo& g, hipStream_t s);
+// shared proxy head: row broadcast (dst[r][c] = src[r], rows of row_bytes, a
+// multiple of 4) and the in-order average over copies of fp32 rows
+hipError_t launch_bcast(const void* src, void* dst, int64_t rows, int copies, int64_t row_bytes,
+                        hipStream_t s);
+hipError_t launch_group_mean(const float* src, float* dst, int64_t rows, int copies, int64_t words,
+                             hipStream_t s);
 hipError_t launch_proxy_scores(const Geo& g, int is_bf16, const void* qp, const void* kp,
                                float* scores, hipStream_t s);
 hipError_t launch_select(const Geo& g, const float* scores, int32_t* q2k_idx, int32_t* q2k_cnt,
@@ -89,6 +95,7 @@ struct KernelEntry {
   int dyn_lds;
 };
 int select_kernels(KernelEntry* out, int max);
+int share_kernels(KernelEntry* out, int max);
 int fwd_kernels(KernelEntry* out, int max);
 int bwd_kernels(KernelEntry* out, int max);
 

@@ -33,12 +33,14 @@ class Config:
     proxy_loss_weight: float = 1.0
     dtype: str = "bf16"
     dilation: int = 1
+    proxy_heads: int = 0       # 0 = one proxy head per KV group; 1 = one shared proxy head
 
     def to_c(self) -> MsaConfig:
         return MsaConfig(self.heads_q, self.heads_kv, self.head_dim, self.proxy_dim, self.kv_block,
                          self.q_block, self.topk, self.local_window, self.softmax_scale,
                          self.proxy_scale, self.proxy_loss_weight,
-                         _lib.MSA_BF16 if self.dtype == "bf16" else _lib.MSA_F32, self.dilation)
+                         _lib.MSA_BF16 if self.dtype == "bf16" else _lib.MSA_F32, self.dilation,
+                         self.proxy_heads)
 
     @property
     def torch_dtype(self):
@@ -94,7 +96,7 @@ def msa_get_layout(cfg: Config, vl: Varlen) -> dict:
 def msa_proxy_scores(cfg: Config, vl: Varlen, qp, kp, block_scores, workspace, stream=None):
     lib = load()
     lay = msa_get_layout(cfg, vl)
-    T, Hp, dp = vl.total, cfg.heads_kv, cfg.proxy_dim
+    T, Hp, dp = vl.total, lay["proxy_heads"], cfg.proxy_dim
     dt = cfg.torch_dtype
     a = [_ptr(qp, "qp", dt, (T, Hp, dp)), _ptr(kp, "kp", dt, (T, Hp, dp)),
          _ptr(block_scores, "block_scores", torch.float32, (Hp, lay["score_elems"])),
@@ -108,7 +110,7 @@ def msa_select_blocks(cfg: Config, vl: Varlen, block_scores, q2k_idx, q2k_cnt, k
                       workspace, stream=None):
     lib = load()
     lay = msa_get_layout(cfg, vl)
-    Hp = cfg.heads_kv
+    Hp = lay["proxy_heads"]
     i32 = torch.int32
     a = [_ptr(block_scores, "block_scores", torch.float32, (Hp, lay["score_elems"])),
          _ptr(q2k_idx, "q2k_idx", i32, (Hp, lay["total_qblocks"], lay["sel_stride"])),
@@ -126,13 +128,14 @@ def msa_fwd(cfg: Config, vl: Varlen, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, 
     lib = load()
     lay = msa_get_layout(cfg, vl)
     T, Hq, Hkv, d, dp = vl.total, cfg.heads_q, cfg.heads_kv, cfg.head_dim, cfg.proxy_dim
+    Hp = lay["proxy_heads"]
     dt, i32, f32 = cfg.torch_dtype, torch.int32, torch.float32
     a = [_ptr(q, "q", dt, (T, Hq, d)), _ptr(k, "k", dt, (T, Hkv, d)), _ptr(v, "v", dt, (T, Hkv, d)),
-         _ptr(qp, "qp", dt, (T, Hkv, dp)), _ptr(kp, "kp", dt, (T, Hkv, dp)),
-         _ptr(q2k_idx, "q2k_idx", i32, (Hkv, lay["total_qblocks"], lay["sel_stride"])),
-         _ptr(q2k_cnt, "q2k_cnt", i32, (Hkv, lay["total_qblocks"])),
+         _ptr(qp, "qp", dt, (T, Hp, dp)), _ptr(kp, "kp", dt, (T, Hp, dp)),
+         _ptr(q2k_idx, "q2k_idx", i32, (Hp, lay["total_qblocks"], lay["sel_stride"])),
+         _ptr(q2k_cnt, "q2k_cnt", i32, (Hp, lay["total_qblocks"])),
          _ptr(o, "o", dt, (T, Hq, d)), _ptr(lse, "lse", f32, (Hq, T)),
-         _ptr(lse_p, "lse_p", f32, (Hkv, T)), _ptr(workspace, "workspace", torch.uint8)]
+         _ptr(lse_p, "lse_p", f32, (Hp, T)), _ptr(workspace, "workspace", torch.uint8)]
     c, vv = cfg.to_c(), vl.to_c()
     check(lib.msa_fwd(ctypes.byref(c), ctypes.byref(vv), *a, workspace.numel(), _stream(stream)))
 
@@ -142,18 +145,19 @@ def msa_bwd(cfg: Config, vl: Varlen, q, k, v, qp, kp, o, lse, lse_p, dout, q2k_i
     lib = load()
     lay = msa_get_layout(cfg, vl)
     T, Hq, Hkv, d, dp = vl.total, cfg.heads_q, cfg.heads_kv, cfg.head_dim, cfg.proxy_dim
+    Hp = lay["proxy_heads"]
     dt, i32, f32 = cfg.torch_dtype, torch.int32, torch.float32
     a = [_ptr(q, "q", dt, (T, Hq, d)), _ptr(k, "k", dt, (T, Hkv, d)), _ptr(v, "v", dt, (T, Hkv, d)),
-         _ptr(qp, "qp", dt, (T, Hkv, dp)), _ptr(kp, "kp", dt, (T, Hkv, dp)),
+         _ptr(qp, "qp", dt, (T, Hp, dp)), _ptr(kp, "kp", dt, (T, Hp, dp)),
          _ptr(o, "o", dt, (T, Hq, d)), _ptr(lse, "lse", f32, (Hq, T)),
-         _ptr(lse_p, "lse_p", f32, (Hkv, T)), _ptr(dout, "dout", dt, (T, Hq, d)),
-         _ptr(q2k_idx, "q2k_idx", i32, (Hkv, lay["total_qblocks"], lay["sel_stride"])),
-         _ptr(q2k_cnt, "q2k_cnt", i32, (Hkv, lay["total_qblocks"])),
-         _ptr(k2q_ptr, "k2q_ptr", i32, (Hkv, lay["total_kvblocks"] + 1)),
-         _ptr(k2q_idx, "k2q_idx", i32, (Hkv, lay["k2q_capacity"])),
+         _ptr(lse_p, "lse_p", f32, (Hp, T)), _ptr(dout, "dout", dt, (T, Hq, d)),
+         _ptr(q2k_idx, "q2k_idx", i32, (Hp, lay["total_qblocks"], lay["sel_stride"])),
+         _ptr(q2k_cnt, "q2k_cnt", i32, (Hp, lay["total_qblocks"])),
+         _ptr(k2q_ptr, "k2q_ptr", i32, (Hp, lay["total_kvblocks"] + 1)),
+         _ptr(k2q_idx, "k2q_idx", i32, (Hp, lay["k2q_capacity"])),
          _ptr(dq, "dq", f32, (T, Hq, d)), _ptr(dk, "dk", f32, (T, Hkv, d)),
-         _ptr(dv, "dv", f32, (T, Hkv, d)), _ptr(dqp, "dqp", f32, (T, Hkv, dp)),
-         _ptr(dkp, "dkp", f32, (T, Hkv, dp)), _ptr(workspace, "workspace", torch.uint8)]
+         _ptr(dv, "dv", f32, (T, Hkv, d)), _ptr(dqp, "dqp", f32, (T, Hp, dp)),
+         _ptr(dkp, "dkp", f32, (T, Hp, dp)), _ptr(workspace, "workspace", torch.uint8)]
     c, vv = cfg.to_c(), vl.to_c()
     check(lib.msa_bwd(ctypes.byref(c), ctypes.byref(vv), *a, workspace.numel(), _stream(stream)))
 
@@ -197,34 +201,35 @@ class Buffers:
         lay = msa_get_layout(cfg, vl)
         self.layout = lay
         T, Hq, Hkv, d, dp = vl.total, cfg.heads_q, cfg.heads_kv, cfg.head_dim, cfg.proxy_dim
+        Hp = lay["proxy_heads"]
         i32, f32 = torch.int32, torch.float32
         z = dict(device=device)
         self.workspace = torch.empty(max(lay["workspace_bytes"], 16), dtype=torch.uint8, **z)
-        self.scores = torch.empty((Hkv, max(lay["score_elems"], 1)), dtype=f32, **z)[:, :lay["score_elems"]]
+        self.scores = torch.empty((Hp, max(lay["score_elems"], 1)), dtype=f32, **z)[:, :lay["score_elems"]]
         if lay["score_elems"] == 0:
-            self.scores = torch.empty((Hkv, 0), dtype=f32, **z)
-        self.q2k_idx = torch.empty((Hkv, lay["total_qblocks"], lay["sel_stride"]), dtype=i32, **z)
-        self.q2k_cnt = torch.empty((Hkv, lay["total_qblocks"]), dtype=i32, **z)
-        self.k2q_ptr = torch.empty((Hkv, lay["total_kvblocks"] + 1), dtype=i32, **z)
-        self.k2q_idx = torch.empty((Hkv, lay["k2q_capacity"]), dtype=i32, **z)
+            self.scores = torch.empty((Hp, 0), dtype=f32, **z)
+        self.q2k_idx = torch.empty((Hp, lay["total_qblocks"], lay["sel_stride"]), dtype=i32, **z)
+        self.q2k_cnt = torch.empty((Hp, lay["total_qblocks"]), dtype=i32, **z)
+        self.k2q_ptr = torch.empty((Hp, lay["total_kvblocks"] + 1), dtype=i32, **z)
+        self.k2q_idx = torch.empty((Hp, lay["k2q_capacity"]), dtype=i32, **z)
         self.o = torch.empty((T, Hq, d), dtype=cfg.torch_dtype, **z)
         self.lse = torch.empty((Hq, T), dtype=f32, **z)
-        self.lse_p = torch.empty((Hkv, T), dtype=f32, **z)
-        self._shape = (T, Hq, Hkv, d, dp, device)
+        self.lse_p = torch.empty((Hp, T), dtype=f32, **z)
+        self._shape = (T, Hq, Hkv, Hp, d, dp, device)
         if need_bwd:
             self.alloc_backward()
 
     def alloc_backward(self):
         """The gradient outputs (fp32) and, if released, the workspace."""
-        T, Hq, Hkv, d, dp, device = self._shape
+        T, Hq, Hkv, Hp, d, dp, device = self._shape
         f32, z = torch.float32, dict(device=device)
         if getattr(self, "workspace", None) is None:
             self.workspace = torch.empty(max(self.layout["workspace_bytes"], 16), dtype=torch.uint8, **z)
         self.dq = torch.empty((T, Hq, d), dtype=f32, **z)
         self.dk = torch.empty((T, Hkv, d), dtype=f32, **z)
         self.dv = torch.empty((T, Hkv, d), dtype=f32, **z)
-        self.dqp = torch.empty((T, Hkv, dp), dtype=f32, **z)
-        self.dkp = torch.empty((T, Hkv, dp), dtype=f32, **z)
+        self.dqp = torch.empty((T, Hp, dp), dtype=f32, **z)
+        self.dkp = torch.empty((T, Hp, dp), dtype=f32, **z)
 
     def release_transients(self):
         """Drop what the backward does not read: the block scores and the

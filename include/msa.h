@@ -29,8 +29,13 @@
  *
  * Conventions for every entry point
  *   - Tokens-major packed layouts: q, o, dout [T, Hq, d]; k, v [T, Hkv, d];
- *     qp, kp [T, Hkv, dp].  Gradients are fp32 in the same layouts.
- *     lse [Hq, T] and lse_p [Hkv, T] are fp32 natural logarithms.
+ *     qp, kp [T, Hp, dp].  Gradients are fp32 in the same layouts.
+ *     lse [Hq, T] and lse_p [Hp, T] are fp32 natural logarithms.  Hp, the
+ *     number of proxy heads, is Hkv (one per KV group) or 1 (one proxy head
+ *     shared by every group: its block choice serves every query head, and the
+ *     proxy gradient's target is the mean main attention over all query heads);
+ *     every per-proxy-head tensor below (block scores, block lists, lse_p) has
+ *     Hp in place of Hkv.
  *   - cu_seqlens: int32 [batch + 1], cu_seqlens[0] = 0, non-decreasing,
  *     cu_seqlens[batch] = total_tokens.  Blocks start at each document start;
  *     selection never crosses a document.  Zero-length documents are allowed.
@@ -58,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 2
+#define MSA_ABI_VERSION 3
 
 typedef enum {
   MSA_OK = 0,
@@ -72,7 +77,7 @@ typedef enum { MSA_BF16 = 0, MSA_F32 = 1 } msa_dtype;
 
 typedef struct {
   int32_t heads_q;           /* Hq, a multiple of heads_kv */
-  int32_t heads_kv;          /* Hkv; also the number of proxy heads */
+  int32_t heads_kv;          /* Hkv */
   int32_t head_dim;          /* d:  128 (bf16) or 64 (bf16, fp32) */
   int32_t proxy_dim;         /* dp: 64 with d = 128, 32 with d = 64 */
   int32_t kv_block;          /* must be 128 */
@@ -84,6 +89,8 @@ typedef struct {
   float proxy_loss_weight;   /* lam; 0 is a valid weight */
   int32_t dtype;             /* msa_dtype of q, k, v, qp, kp, o, dout */
   int32_t dilation;          /* stride of the forced window blocks; 0 or 1 = contiguous */
+  int32_t proxy_heads;       /* Hp: 0 or heads_kv = one proxy head per KV group; 1 = one
+                                proxy head shared by every group */
 } msa_config;
 
 typedef struct {
@@ -102,6 +109,7 @@ typedef struct {
   int64_t scored_pairs;      /* per proxy head: (query, key) pairs the scoring contracts */
   int64_t max_qblocks_doc;   /* largest per-document query-block count */
   int64_t workspace_bytes;   /* one workspace serves every entry point */
+  int64_t proxy_heads;       /* Hp, the leading size of every per-proxy-head tensor */
 } msa_layout;
 
 int32_t msa_abi_version(void);
@@ -118,7 +126,7 @@ msa_status msa_get_layout(const msa_config* cfg, const msa_varlen* vl, msa_layou
 /*
  * Proxy block scores (ai-minor, News Overview: the maximum of the proxy
  * score over 128-token KV blocks).
- * block_scores: fp32 [Hkv, score_elems]; document b's nq x nk rectangle is
+ * block_scores: fp32 [Hp, score_elems]; document b's nq x nk rectangle is
  * row-major at a per-document offset.  Only the candidate entries of query
  * blocks that have candidates are written (J < diag - local_window * delta,
  * where diag = floor(I * q_block / 128) and delta the dilation, and only when
@@ -133,11 +141,11 @@ msa_status msa_proxy_scores(const msa_config* cfg, const msa_varlen* vl, const v
  * Top-k block selection per (proxy head, query block) and the KV-major
  * inverted index (ai-minor, News Overview / Terminology: KV chosen in block
  * units).
- * q2k_idx int32 [Hkv, NQB, sel_stride]: ascending global KV block ids, -1 padded.
- * q2k_cnt int32 [Hkv, NQB]: min(topk - 1, candidates) + forced blocks; with
+ * q2k_idx int32 [Hp, NQB, sel_stride]: ascending global KV block ids, -1 padded.
+ * q2k_cnt int32 [Hp, NQB]: min(topk - 1, candidates) + forced blocks; with
  *         delta = 1 this is min(topk + local_window, diag + 1).
- * k2q_ptr int32 [Hkv, NKB + 1]: per-group CSR offsets into row g of k2q_idx.
- * k2q_idx int32 [Hkv, k2q_capacity]: ascending query-block ids per KV block;
+ * k2q_ptr int32 [Hp, NKB + 1]: per-proxy-head CSR offsets into row p of k2q_idx.
+ * k2q_idx int32 [Hp, k2q_capacity]: ascending query-block ids per KV block;
  *         the unused tail of each row is -1.
  */
 msa_status msa_select_blocks(const msa_config* cfg, const msa_varlen* vl, const float* block_scores,
@@ -148,7 +156,7 @@ msa_status msa_select_blocks(const msa_config* cfg, const msa_varlen* vl, const 
 /*
  * Sparse GQA forward over the selected blocks (socker-news summary 要約;
  * ai-minor News Overview).  o has the input dtype; lse [Hq, T] and
- * lse_p [Hkv, T] (proxy softmax over the same selected keys) are fp32.
+ * lse_p [Hp, T] (proxy softmax over the same selected keys) are fp32.
  */
 msa_status msa_fwd(const msa_config* cfg, const msa_varlen* vl, const void* q, const void* k,
                    const void* v, const void* qp, const void* kp, const int32_t* q2k_idx,
@@ -159,7 +167,7 @@ msa_status msa_fwd(const msa_config* cfg, const msa_varlen* vl, const void* q, c
  * Fused backward of the main attention and the proxy head (ai-minor, Why
  * Does This Matter?: fused backward).  Takes the forward's o, lse, lse_p and
  * block lists plus the upstream gradient dout; writes fp32 dq [T, Hq, d],
- * dk, dv [T, Hkv, d], dqp, dkp [T, Hkv, dp].
+ * dk, dv [T, Hkv, d], dqp, dkp [T, Hp, dp].
  */
 msa_status msa_bwd(const msa_config* cfg, const msa_varlen* vl, const void* q, const void* k,
                    const void* v, const void* qp, const void* kp, const void* o, const float* lse,

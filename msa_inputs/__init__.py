@@ -64,6 +64,7 @@ class Workload:
     total_tokens: int = 0     # for doc_mode == "loguniform"
     proxy_loss_weight: float = 1.0
     dilation: int = 1         # stride of the forced window blocks
+    proxy_heads: int = 0      # 0: one proxy head per KV group; 1: one shared proxy head
 
     @property
     def group(self) -> int:
@@ -193,6 +194,8 @@ def make_case(w: Workload, seed: int = 0, seqlens: Optional[List[int]] = None,
     else:
         arrs = [np.ascontiguousarray(a, dtype=np.float32) for a in arrs]
     q, k, v, qp, kp, dO = arrs
+    if w.proxy_heads == 1:            # one shared proxy head: the first group's projection
+        qp, kp = np.ascontiguousarray(qp[:, :1]), np.ascontiguousarray(kp[:, :1])
     return Case(w, seed, list(seqlens), cu_seqlens_of(seqlens), q, k, v, qp, kp, dO)
 
 
@@ -239,6 +242,9 @@ def make_case_torch(w: Workload, seed: int = 0, device="cuda", seqlens: Optional
         qp = normal((T, Hkv, dp), 0.5); qp.add_(add_prox_blk[tok_blk]); out["qp"] = qp.to(dt); del qp
         kp = normal((T, Hkv, dp), 0.5); kp.add_(add_prox_blk[tok_blk]); out["kp"] = kp.to(dt); del kp
         out["dO"] = normal((T, Hq, d), 0.5).to(dt)
+    if w.proxy_heads == 1:            # one shared proxy head: the first group's projection
+        out["qp"] = out["qp"][:, :1].contiguous()
+        out["kp"] = out["kp"][:, :1].contiguous()
     out["cu_seqlens"] = torch.from_numpy(cu_seqlens_of(seqlens)).to(device)
     out["seqlens"] = list(seqlens)
     return out

@@ -26,9 +26,10 @@ def log(*a):
 def cfgs(w: Workload, **over):
     w = replace(w, **over) if over else w
     c = msa.Config(w.heads_q, w.heads_kv, w.head_dim, w.proxy_dim, w.q_block, w.topk,
-                   w.local_window, 128, 0.0, 0.0, w.proxy_loss_weight, w.dtype, w.dilation)
+                   w.local_window, 128, 0.0, 0.0, w.proxy_loss_weight, w.dtype, w.dilation,
+                   w.proxy_heads)
     o = om.Config(w.heads_q, w.heads_kv, w.head_dim, w.proxy_dim, w.q_block, w.topk,
-                  w.local_window, 128, None, None, w.proxy_loss_weight, w.dilation)
+                  w.local_window, 128, None, None, w.proxy_loss_weight, w.dilation, w.proxy_heads)
     return w, c, o
 
 

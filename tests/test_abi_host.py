@@ -23,8 +23,9 @@ def test_exports_match_header():
     assert declared == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.msa_abi_version() == _lib.ABI_VERSION == 2
-    assert ctypes.sizeof(_lib.MsaConfig) == 13 * 4
+    assert lib.msa_abi_version() == _lib.ABI_VERSION == 3
+    assert ctypes.sizeof(_lib.MsaConfig) == 14 * 4
+    assert ctypes.sizeof(_lib.MsaLayout) == 9 * 8
     assert lib.msa_status_string(0).decode() == "ok"
 
 
@@ -65,6 +66,7 @@ def _err(fn):
     (dict(topk=0), _lib.MSA_ERR_INVALID_ARG),
     (dict(local_window=-1), _lib.MSA_ERR_INVALID_ARG),
     (dict(dilation=-1), _lib.MSA_ERR_INVALID_ARG),
+    (dict(proxy_heads=2), _lib.MSA_ERR_INVALID_ARG),            # neither 1 nor heads_kv
     (dict(local_window=1 << 12, dilation=1 << 9), _lib.MSA_ERR_INVALID_ARG),
     (dict(heads_q=24, heads_kv=4), _lib.MSA_ERR_UNSUPPORTED),   # group of 6
     (dict(dtype="f32"), _lib.MSA_ERR_UNSUPPORTED),              # fp32 only at d = 64
@@ -140,3 +142,21 @@ def test_buffer_lifetimes_and_saved_bytes():
     assert buf.workspace.numel() >= lay["workspace_bytes"]
     assert tuple(buf.dq.shape) == (T, Hq, d) and tuple(buf.dkp.shape) == (T, Hkv, dp)
     assert buf.dq.dtype == torch.float32
+
+
+@pytest.mark.parametrize("proxy_heads,Hp", [(0, 8), (8, 8), (1, 1)])
+def test_layout_proxy_heads(proxy_heads, Hp):
+    """Hp leads every per-proxy-head tensor; the shared head adds workspace for
+    the per-group copies the forward and backward run on."""
+    cu = torch.tensor([0, 3000, 4100], dtype=torch.int32)
+    base = msa.msa_get_layout(msa.Config(32, 8, 128, 64, 128, 8), msa.Varlen(cu))
+    lay = msa.msa_get_layout(msa.Config(32, 8, 128, 64, 128, 8, proxy_heads=proxy_heads), msa.Varlen(cu))
+    assert lay["proxy_heads"] == Hp
+    assert {k: v for k, v in lay.items() if k not in ("workspace_bytes", "proxy_heads")} == \
+           {k: v for k, v in base.items() if k not in ("workspace_bytes", "proxy_heads")}
+    T = 4100
+    copies = 2 * 2 * T * 8 * 64 + 4 * 8 * T + 2 * 4 * T * 8 * 64    # qp, kp; lse_p; dqp, dkp
+    if Hp == 1:
+        assert lay["workspace_bytes"] >= base["workspace_bytes"] + copies
+    else:
+        assert lay["workspace_bytes"] == base["workspace_bytes"]

@@ -15,6 +15,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _autograd_run(case, w, dense=False):
+    # (the workload's dilation and proxy-head count are passed through)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     leaves = {n: torch.from_numpy(getattr(case, n)).to(dt).cuda().requires_grad_(True)
               for n in ("q", "k", "v", "qp", "kp")}
@@ -22,7 +23,8 @@ def _autograd_run(case, w, dense=False):
     o = msa.msa_attention(*(leaves[n] for n in ("q", "k", "v", "qp", "kp")), cu, topk=w.topk,
                           q_block=w.q_block, local_window=w.local_window,
                           proxy_loss_weight=w.proxy_loss_weight,
-                          cu_seqlens_host=[int(c) for c in case.cu_seqlens], dense=dense)
+                          cu_seqlens_host=[int(c) for c in case.cu_seqlens], dense=dense,
+                          dilation=w.dilation, proxy_heads=w.proxy_heads)
     o.backward(torch.from_numpy(case.dO).to(dt).cuda())
     torch.cuda.synchronize()
     out = {"o": o.detach().float().cpu().numpy()}
@@ -31,12 +33,13 @@ def _autograd_run(case, w, dense=False):
     return out
 
 
-@pytest.mark.parametrize("name,seqlens", [("tiny-2k-fp32", (2048,)), ("layer-32k", (1500, 0, 700))])
-def test_autograd_equals_c_abi_path(name, seqlens):
+@pytest.mark.parametrize("name,seqlens,shared", [("tiny-2k-fp32", (2048,), 0), ("layer-32k", (1500, 0, 700), 0),
+                                                 ("tiny-2k-fp32", (2048,), 1)])
+def test_autograd_equals_c_abi_path(name, seqlens, shared):
     """Same kernels, same inputs: the autograd wrapper's O is the C-ABI path's
     O bit for bit, and its gradients are the fp32 gradients (bf16 inputs get
     them rounded to bf16)."""
-    w, cfg, ocfg = cfgs(WORKLOADS[name], topk=4)
+    w, cfg, ocfg = cfgs(WORKLOADS[name], topk=4, proxy_heads=shared)
     case = small_case(w, seqlens, seed=7)
     ref = run_gpu(case, cfg, backward=True, scores=False)
     got = _autograd_run(case, w)

@@ -25,6 +25,9 @@ SMALL = {
     # dilated windows: forced blocks on the window's stride
     "l32k-geom-dilated": (WORKLOADS["layer-32k"], dict(topk=3, local_window=2, dilation=3), (2500, 1277)),
     "l512k-geom-dilated": (WORKLOADS["layer-512k-window2"], dict(topk=3, dilation=2), (1900, 2100, 64)),
+    # one proxy head shared by every KV group
+    "l32k-geom-shared": (WORKLOADS["layer-32k"], dict(topk=4, proxy_heads=1), (2500, 1277)),
+    "l128k-geom-gqa8-shared": (WORKLOADS["layer-128k-gqa8"], dict(topk=3, proxy_heads=1), (1700, 300)),
 }
 
 
