@@ -55,7 +55,11 @@ def selected_pairs(seqlens, q_block, topk, window, dilation=1):
 
 
 def flop_model(w, seqlens, scored_pairs):
-    d, dp, Hq, Hp = w.head_dim, w.proxy_dim, w.heads_q, w.heads_kv
+    """Counted FLOPs use the proxy-head count Hp (Hkv, or 1 for the shared
+    head); the per-kernel figures use what the kernels run (the attention
+    kernels work per KV group either way; scoring runs once per proxy head)."""
+    d, dp, Hq, Hkv = w.head_dim, w.proxy_dim, w.heads_q, w.heads_kv
+    Hp = 1 if getattr(w, "proxy_heads", 0) == 1 else Hkv
     n = selected_pairs(seqlens, w.q_block, w.topk, w.local_window, w.dilation)
     f = {
         "pairs_per_group": n,
@@ -66,13 +70,13 @@ def flop_model(w, seqlens, scored_pairs):
         # passes (14 d per head), the query-major pass also forms P kp per
         # head for the group-mean term, and each pass recomputes Y and applies
         # one proxy product per group
-        "bwd_executed": 14 * d * Hq * n + 2 * dp * Hq * n + 8 * dp * Hp * n,
+        "bwd_executed": 14 * d * Hq * n + 2 * dp * Hq * n + 8 * dp * Hkv * n,
         # per-kernel algorithmic work
         "k:proxy_scores": 2 * dp * Hp * scored_pairs,
         "k:fwd": 4 * d * Hq * n,
-        "k:proxy_lse": 2 * dp * Hp * n,
-        "k:bwd_dq": 6 * d * Hq * n + 4 * dp * Hp * n,
-        "k:bwd_dkdv": 8 * d * Hq * n + 4 * dp * Hp * n,
+        "k:proxy_lse": 2 * dp * Hkv * n,
+        "k:bwd_dq": 6 * d * Hq * n + 4 * dp * Hkv * n,
+        "k:bwd_dkdv": 8 * d * Hq * n + 4 * dp * Hkv * n,
     }
     return f
 
@@ -179,7 +183,7 @@ def dense_compare(a, w, seqlens, x, msa, torch):
             return msa.msa_attention(*(leaves[n] for n in names), x["cu_seqlens"], topk=w.topk,
                                      q_block=w.q_block, local_window=w.local_window,
                                      proxy_loss_weight=w.proxy_loss_weight, cu_seqlens_host=host,
-                                     dense=dense, dilation=w.dilation)
+                                     dense=dense, dilation=w.dilation, proxy_heads=w.proxy_heads)
 
         for _ in range(max(a.warmup, 1)):
             o = forward()
@@ -261,6 +265,10 @@ def main(argv=None):
                          "selection, forward); dense-compare: the same workload once sparse and once "
                          "with every causal block selected, through the autograd API, with the "
                          "memory kept between forward and backward")
+    ap.add_argument("--proxy-heads", type=int, default=None, choices=(0, 1),
+                    help="override the workload's proxy heads (0: one per KV group, 1: one shared head)")
+    ap.add_argument("--dilation", type=int, default=None, help="override the window dilation")
+    ap.add_argument("--local-window", type=int, default=None, help="override the local window")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB, 4 times (the "
                          "known-size reference for scaling HBM byte counters), then exit")
@@ -280,13 +288,18 @@ def main(argv=None):
     from msa_inputs import WORKLOADS, make_case_torch, seqlens_of
 
     w = WORKLOADS[a.workload]
+    over = {k: v for k, v in (("proxy_heads", a.proxy_heads), ("dilation", a.dilation),
+                              ("local_window", a.local_window)) if v is not None}
+    if over:
+        from dataclasses import replace
+        w = replace(w, **over)
     seqlens = seqlens_of(w, a.seed)
     t_gen = time.perf_counter()
     x = make_case_torch(w, a.seed, device="cuda", seqlens=seqlens)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
     cfg = msa.Config(w.heads_q, w.heads_kv, w.head_dim, w.proxy_dim, w.q_block, w.topk, w.local_window,
-                     128, 0.0, 0.0, w.proxy_loss_weight, w.dtype, w.dilation)
+                     128, 0.0, 0.0, w.proxy_loss_weight, w.dtype, w.dilation, w.proxy_heads)
     vl = msa.Varlen(x["cu_seqlens"], x["cu_seqlens"].cpu().numpy())
     buf = msa.Buffers(cfg, vl, device="cuda", need_bwd=True)
     lay = buf.layout
@@ -361,7 +374,7 @@ def main(argv=None):
             pool = I * w.q_block // 128 - w.local_window * w.dilation
             if pool > w.topk - 1:
                 n_cand_entries += pool
-    sel_bytes = w.heads_kv * (4 * n_cand_entries + 4 * lay["total_qblocks"] * (lay["sel_stride"] + 1))
+    sel_bytes = lay["proxy_heads"] * (4 * n_cand_entries + 4 * lay["total_qblocks"] * (lay["sel_stride"] + 1))
     selection = None
     if "select" in per_kernel:
         gbps = sel_bytes / (per_kernel["select"]["avg_ms"] * 1e-3) / 1e9
@@ -388,7 +401,8 @@ def main(argv=None):
         "config": {"workload": w.name, "total_tokens": int(sum(seqlens)), "docs": len(seqlens),
                    "heads_q": w.heads_q, "heads_kv": w.heads_kv, "head_dim": w.head_dim,
                    "proxy_dim": w.proxy_dim, "kv_block": 128, "q_block": w.q_block, "topk": w.topk,
-                   "local_window": w.local_window, "dilation": w.dilation, "seed": a.seed,
+                   "local_window": w.local_window, "dilation": w.dilation,
+                   "proxy_heads": lay["proxy_heads"], "seed": a.seed,
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
