@@ -59,6 +59,9 @@ struct FwdCfg {
   static constexpr int NK = KC * CPR / 256;              // chunks per thread per tensor
 };
 
+template <typename U>
+struct TypeTag { using type = U; };
+
 template <typename T, int D, int DP, int QT>
 __global__ __launch_bounds__(256) void fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -210,6 +213,130 @@ __global__ __launch_bounds__(256) void fwd_kernel(
     for (int qt = 0; qt < QT; ++qt) mtrue[qt] = fmaxf(mtrue[qt], mx[qt]);
   };
 
+  // The accumulation of one 64-key stage (bf16, d = 128) as a fixed sequence
+  // of MFMAs, each pair (the two query tiles) sharing one operand read from
+  // LDS: S of key tile 0 (K rows), S of tile 1, then P V of tile 0 (V^T
+  // fragments), then of tile 1.  Every operand is read LOOK pairs ahead of
+  // its use; tile 0's exponentials run between tile 1's S products and tile
+  // 1's between tile 0's P V products; scheduling fences keep that order.
+  constexpr bool FAST = sizeof(T) == 2 && D == 128 && QT == 2;
+  uint32_t oRow[D / 16], oColV[D / 32][2];
+  if constexpr (FAST) {
+    const int s16 = lane & 15, g4 = lane >> 4;
+    const int tr_r = hi * 4 + (s16 >> 2), tr_c = 16 * (g4 & 1) + 4 * (s16 & 3);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) oRow[ks] = TK::off(col, ks * 16 + hi * 8) * (int)sizeof(T);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      oColV[dt][0] = (C::KS + TK::off(tr_r, dt * 32 + tr_c)) * (int)sizeof(T);
+      oColV[dt][1] = (C::KS + TK::off(tr_r + 8, dt * 32 + tr_c)) * (int)sizeof(T);
+    }
+  }
+  // (the element type comes in as a tag so that the body is type-checked only
+  // where it is used, with bf16)
+  auto stage_fast = [&](int buf, int kpos0, auto masked_c, auto tag) __attribute__((always_inline)) {
+    using TT = typename decltype(tag)::type;
+    constexpr bool MASKED = decltype(masked_c)::value;
+    constexpr int NA = D / 16;                      // S operands per key tile
+    constexpr int NB = 2 * (D / 32);                // P V operands per key tile
+    constexpr int NO = 2 * NA + 2 * NB;
+    constexpr int LOOK = 4;
+    const uint32_t sb = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(lds_offset(smem_raw) + buf * C::STAGE * (int)sizeof(T)));
+    uint32_t aRow[D / 16], aCol[D / 32][2];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) aRow[ks] = lds_base_add(sb, oRow[ks]);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      aCol[dt][0] = lds_base_add(sb, oColV[dt][0]);
+      aCol[dt][1] = lds_base_add(sb, oColV[dt][1]);
+    }
+    f32x16 S[2][QT];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) S[kt][qt] = zero16();
+    frag_t<TT> Pf[2][2][QT];
+    frag_t<TT> opnd[NO];
+    float ls[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) ls[qt] = 0.f;
+    int lim[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) lim[qt] = qbase + qt * 32 + col - kpos0;
+    auto operand = [&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < 2 * NA) {
+        constexpr int kt = m / NA, ks = m % NA;
+        opnd[m] = lds_ld8<kt * 32 * D * 2>(aRow[ks]);
+      } else {
+        constexpr int r = m - 2 * NA, kt = r / NB, dt = (r % NB) / 2, kk = (r % NB) % 2;
+        opnd[m] = tr_pair_at<(kt * 32 + kk * 16) * D * 2>(aCol[dt][0], aCol[dt][1]);
+      }
+    };
+    auto product = [&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < 2 * NA) {
+        constexpr int kt = m / NA, ks = m % NA;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) mma(S[kt][qt], opnd[m], Qf[qt][ks]);
+      } else {
+        constexpr int r = m - 2 * NA, kt = r / NB, dt = (r % NB) / 2, kk = (r % NB) % 2;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) mma(O[dt][qt], opnd[m], Pf[kt][kk][qt]);
+      }
+    };
+    // softmax element e (of 2 x 16) of key tile kt
+    auto soft = [&](int kt, int e) __attribute__((always_inline)) {
+      const int qt = e >> 4, i = e & 15;
+      float p = __builtin_amdgcn_exp2f(fmaf(S[kt][qt][i], g.scale_log2, -mref[qt]));
+      if (MASKED) p = acc_row(i, lane) <= lim[qt] - kt * 32 ? p : 0.f;
+      S[kt][qt][i] = p;
+      ls[qt] += p;
+    };
+    auto pack = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) Pf[kt][kk][qt] = acc_frag<TT>(S[kt][qt], kk);
+    };
+    static_for<LOOK>([&](auto mc) __attribute__((always_inline)) { operand(mc); });
+    static_for<NO>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      product(mc);
+      if constexpr (m + LOOK < NO) operand(std::integral_constant<int, m + LOOK>());
+      if constexpr (m >= NA && m < 2 * NA) {
+        constexpr int e0 = (m - NA) * 2 * 16 / NA, e1 = (m - NA + 1) * 2 * 16 / NA;
+#pragma unroll
+        for (int e = e0; e < e1; ++e) soft(0, e);
+        if constexpr (m == 2 * NA - 1) pack(0);
+      } else if constexpr (m >= 2 * NA && m < 2 * NA + NB) {
+        constexpr int e0 = (m - 2 * NA) * 2 * 16 / NB, e1 = (m - 2 * NA + 1) * 2 * 16 / NB;
+#pragma unroll
+        for (int e = e0; e < e1; ++e) soft(1, e);
+        if constexpr (m == 2 * NA + NB - 1) pack(1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) l[qt] += ls[qt];
+  };
+  auto pass_fast = [&](auto tag) __attribute__((always_inline)) {   // built only where called
+    int s = 0;
+    for (; s < nst_plain; ++s) {
+      load_stage(s + 1 < nst ? s + 1 : s);
+      if (active) stage_fast(s & 1, (sel[s >> 1] - kb0) * 128 + (s & 1) * C::KC, std::false_type(), tag);
+      store_stage((s & 1) ^ 1);
+      __syncthreads();
+    }
+    for (; s < nst; ++s) {
+      load_stage(s + 1 < nst ? s + 1 : s);
+      if (active) stage_fast(s & 1, diag * 128 + (s & 1) * C::KC, std::true_type(), tag);
+      store_stage((s & 1) ^ 1);
+      __syncthreads();
+    }
+  };
+
   // One pass over every stage; stage 0 must already sit in buffer 0.  The
   // stage after the last re-reads the last one (valid memory) into the unused
   // buffer, so each loop body is straight-line.
@@ -263,7 +390,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(
     scores(smem, 0, (sel[0] - kb0) * 128, sel[0] - kb0 == diag, S);
     row_max(S, mref);
   }
-  pass(accumulate);
+  if constexpr (FAST) pass_fast(TypeTag<T>());
+  else pass(accumulate);
 
   // fallback when a later score exceeded the reference by too much (never for
   // ordinary inputs): find the true row maxima, then accumulate again
