@@ -54,7 +54,8 @@ struct FwdCfg {
   typedef Tile<T, D> TK;                                 // K and V rows, swizzled
   static constexpr int KS = KC * D;
   static constexpr int STAGE = 2 * KS;
-  static constexpr int LDS_BYTES = 2 * STAGE * (int)sizeof(T);
+  static constexpr int NBUF = 3;                         // LDS ring (two stages in flight)
+  static constexpr int LDS_BYTES = NBUF * STAGE * (int)sizeof(T);
   static constexpr int EPC = TK::EPC, CPR = TK::CPR;
   static constexpr int NK = KC * CPR / 256;              // chunks per thread per tensor
 };
@@ -321,20 +322,53 @@ __global__ __launch_bounds__(256) void fwd_kernel(
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) l[qt] += ls[qt];
   };
-  auto pass_fast = [&](auto tag) __attribute__((always_inline)) {   // built only where called
+  // The main pass with a DMA ring: stage s (64 keys of K and V) is copied
+  // into slot s % 3 two stages ahead; every thread issues C::NK copies per
+  // tensor per stage (past the last stage it re-copies the last one), which
+  // the vmcnt waits count.  Keys past the document end (the last block only)
+  // are clamped to its last key: they lie above every query of the block, so
+  // the causal mask drops them.  The reference maxima come from stage 0.
+  auto pass_ring = [&](auto tag) __attribute__((always_inline)) {   // built only where called
+    const uint32_t lds0 = lds_offset(smem_raw);
+    auto issue = [&](int st) __attribute__((always_inline)) {
+      const int sc = st < nst ? st : nst - 1;
+      const int key0 = (sel[sc >> 1] - kb0) * 128 + (sc & 1) * C::KC;
+      const uint32_t base = lds0 + (uint32_t)((st % C::NBUF) * C::STAGE * (int)sizeof(T));
+#pragma unroll
+      for (int i = 0; i < C::NK; ++i) {
+        const int c = i * 256 + tid, r = c / C::CPR, p = c % C::CPR;
+        const int key = key0 + r < L ? key0 + r : L - 1;
+        const int64_t off = ((int64_t)(t0 + key) * g.Hkv + grp) * D + swz<C::CPR>(r, p) * C::EPC;
+        const uint32_t dst = base + (uint32_t)((i * 256 + wave * 64) * 16);
+        dma16(k + off, dst);
+        dma16(v + off, dst + (uint32_t)(C::KS * (int)sizeof(T)));
+      }
+    };
+    wait_vmcnt<0>();                               // the Q fragments: the waits below count copies only
+    issue(0);
+    issue(1);
+    wait_vmcnt<2 * C::NK>();
+    __syncthreads();
+    if (active) {
+      f32x16 S0[QT];
+      scores(smem, 0, (sel[0] - kb0) * 128, sel[0] - kb0 == diag, S0);
+      row_max(S0, mref);
+    }
     int s = 0;
     for (; s < nst_plain; ++s) {
-      load_stage(s + 1 < nst ? s + 1 : s);
-      if (active) stage_fast(s & 1, (sel[s >> 1] - kb0) * 128 + (s & 1) * C::KC, std::false_type(), tag);
-      store_stage((s & 1) ^ 1);
-      __syncthreads();
+      wait_vmcnt<2 * C::NK>();                     // stage s has landed
+      __syncthreads();                             // everyone's, and slot (s + 2) % 3 is free
+      issue(s + 2);
+      if (active) stage_fast(s % C::NBUF, (sel[s >> 1] - kb0) * 128 + (s & 1) * C::KC, std::false_type(), tag);
     }
     for (; s < nst; ++s) {
-      load_stage(s + 1 < nst ? s + 1 : s);
-      if (active) stage_fast(s & 1, diag * 128 + (s & 1) * C::KC, std::true_type(), tag);
-      store_stage((s & 1) ^ 1);
+      wait_vmcnt<2 * C::NK>();
       __syncthreads();
+      issue(s + 2);
+      if (active) stage_fast(s % C::NBUF, diag * 128 + (s & 1) * C::KC, std::true_type(), tag);
     }
+    wait_vmcnt<0>();
+    __syncthreads();
   };
 
   // One pass over every stage; stage 0 must already sit in buffer 0.  The
@@ -382,16 +416,19 @@ __global__ __launch_bounds__(256) void fwd_kernel(
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) { l[qt] = 0.f; mref[qt] = NEG_BIG; mtrue[qt] = NEG_BIG; }
 
-  restage0();
   // reference maximum: the first 32 keys of the list (never all masked for a
   // valid query: the list's lowest block starts at or before the query block)
-  if (active) {
-    f32x16 S[QT];
-    scores(smem, 0, (sel[0] - kb0) * 128, sel[0] - kb0 == diag, S);
-    row_max(S, mref);
+  if constexpr (FAST) {
+    pass_ring(TypeTag<T>());
+  } else {
+    restage0();
+    if (active) {
+      f32x16 S[QT];
+      scores(smem, 0, (sel[0] - kb0) * 128, sel[0] - kb0 == diag, S);
+      row_max(S, mref);
+    }
+    pass(accumulate);
   }
-  if constexpr (FAST) pass_fast(TypeTag<T>());
-  else pass(accumulate);
 
   // fallback when a later score exceeded the reference by too much (never for
   // ordinary inputs): find the true row maxima, then accumulate again
