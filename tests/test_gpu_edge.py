@@ -1,0 +1,32 @@
+"""GPU parity on the method's degenerate cases, through the C ABI against the
+oracle: top-k of 1 (only the forced blocks), documents of one token and
+shorter than a query block, a window wider than most documents, a dilated
+window whose stride skips whole documents' worth of blocks, the shared proxy
+head in fp32, and a batch whose every document but one is empty."""
+import pytest
+
+from msa_inputs import WORKLOADS
+from tests.gpu_common import cfgs, check_inverse, full_compare, log, run_gpu, small_case
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "topk1": (WORKLOADS["layer-32k"], dict(topk=1), (1300, 700)),
+    "topk1-window": (WORKLOADS["layer-512k-window2"], dict(topk=1), (1500, 90)),
+    "tiny-docs": (WORKLOADS["layer-32k"], dict(topk=2), (1, 63, 64, 65, 127, 128, 129, 1)),
+    "wide-window": (WORKLOADS["layer-512k-window2"], dict(topk=2, local_window=6), (2000, 300, 900)),
+    "dilated-wide": (WORKLOADS["layer-32k"], dict(topk=3, local_window=3, dilation=5), (3000, 640)),
+    "shared-fp32": (WORKLOADS["tiny-2k-fp32"], dict(topk=3, proxy_heads=1, local_window=1), (1500, 600)),
+    "one-nonempty": (WORKLOADS["layer-32k"], dict(topk=3), (0, 0, 1900, 0)),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_edge_parity(name):
+    w0, over, seqlens = CASES[name]
+    w, cfg, ocfg = cfgs(w0, **over)
+    case = small_case(w, seqlens, seed=11)
+    log(f"[{name}] T={sum(seqlens)} docs={seqlens}")
+    res = run_gpu(case, cfg, backward=True)
+    check_inverse(res, ocfg)
+    full_compare(case, res, ocfg, tag=name)
