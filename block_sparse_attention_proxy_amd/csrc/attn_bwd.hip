@@ -56,7 +56,7 @@ struct DqCfg {
   static constexpr int COPIES = 2 * NKCOPY + NPCOPY;
   static_assert(NKCOPY >= 1 && NPCOPY >= 1, "copy split");
   static_assert(KC % (4 * KROWS_PER_COPY) == 0 && KC % (4 * PROWS_PER_COPY) == 0, "copy split");
-  static_assert(4 * DP * 32 * 4 <= LDS_BYTES, "reduction scratch");
+  static_assert(4 * DP * 33 * 4 <= LDS_BYTES, "reduction scratch");
 };
 
 template <typename T, int D, int DP>
@@ -359,13 +359,16 @@ __global__ __launch_bounds__(256) void dq_kernel(
         *reinterpret_cast<f32x4*>(dst + dt * 32 + acc_row(i4 * 4, lane)) = r;
       }
   }
-  // proxy term: sum over the heads of this workgroup that share a chunk
-  float* red = reinterpret_cast<float*>(smem_raw);          // [4][DP][32]
+  // proxy term: sum over the heads of this workgroup that share a chunk.
+  // Rows of 33 floats: the reads below walk the proxy dimension across lanes,
+  // and a stride of 33 words puts every lane in its own bank.
+  constexpr int RS = 33;
+  float* red = reinterpret_cast<float*>(smem_raw);          // [4][DP][RS]
   if (active) {
 #pragma unroll
     for (int dt = 0; dt < DP / 32; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) red[(wave * DP + dt * 32 + acc_row(i, lane)) * 32 + col] = Cd[dt][i];
+      for (int i = 0; i < 16; ++i) red[(wave * DP + dt * 32 + acc_row(i, lane)) * RS + col] = Cd[dt][i];
   }
   __syncthreads();
   const int u_lo = wgi * 4;
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
     float acc = 0.f;
     for (int w = 0; w < 4; ++w) {
       const int uw = u_lo + w;
-      if (uw < NU && uw / g.G == c) acc += red[(w * DP + dpi) * 32 + qq];
+      if (uw < NU && uw / g.G == c) acc += red[(w * DP + dpi) * RS + qq];
     }
     const int pos = I * g.Bq + c * 32 + qq;
     if (pos < L) {
