@@ -866,7 +866,12 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t nk = (int64_t)g.Hkv * g.nkb;
-  if (nk > 0) {
+  if (nk > 0 && std::is_same<T, bf16>::value && D == 128 && DP == 64 && dkdv128_supported(g)) {
+    { ProfScope _ps("bwd_dkdv", s);
+    e = launch_dkdv128(g, q, k, v, qp, kp, w.lse2, w.lsep2, dout, w.delta, k2q_ptr, k2q_idx, dk, dv,
+                       dkp, s); }
+    if (e != hipSuccess) return e;
+  } else if (nk > 0) {
     { ProfScope _ps("bwd_dkdv", s);
 #define MSA_LAUNCH_DKDV(GG)                                                                          \
     hipLaunchKernelGGL((dkdv_kernel<T, D, DP, GG>), dim3((unsigned)nk), dim3(256), CK::LDS_BYTES, s, \

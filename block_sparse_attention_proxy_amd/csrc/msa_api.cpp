@@ -508,6 +508,7 @@ static std::vector<msa::KernelEntry> all_kernels() {
   n += msa::select_kernels(v.data() + n, 64 - n);
   n += msa::fwd_kernels(v.data() + n, 64 - n);
   n += msa::bwd_kernels(v.data() + n, 64 - n);
+  n += msa::bwd_kv_kernels(v.data() + n, 64 - n);
   n += msa::share_kernels(v.data() + n, 64 - n);
   v.resize(n);
   return v;

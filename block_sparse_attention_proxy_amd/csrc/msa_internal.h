@@ -86,6 +86,14 @@ hipError_t launch_bwd(const Geo& g, int is_bf16, const void* q, const void* k, c
                       float* dq, float* dk, float* dv, float* dqp, float* dkp, const Work& w,
                       hipStream_t s);
 
+// KV-major backward for bf16, d = 128, dp = 64 and 4 or 8 heads per group
+// (the software-pipelined kernel); other shapes use the generic kernel.
+bool dkdv128_supported(const Geo& g);
+hipError_t launch_dkdv128(const Geo& g, const void* q, const void* k, const void* v,
+                          const void* qp, const void* kp, const float* lse2, const float* lsep2,
+                          const void* dout, const float* delta, const int32_t* k2q_ptr,
+                          const int32_t* k2q_idx, float* dk, float* dv, float* dkp, hipStream_t s);
+
 // Kernel registry for the resource report: each translation unit lists the
 // kernels it instantiates, with the block size and dynamic LDS of its launch.
 struct KernelEntry {
@@ -98,5 +106,6 @@ int select_kernels(KernelEntry* out, int max);
 int share_kernels(KernelEntry* out, int max);
 int fwd_kernels(KernelEntry* out, int max);
 int bwd_kernels(KernelEntry* out, int max);
+int bwd_kv_kernels(KernelEntry* out, int max);
 
 }  // namespace msa
