@@ -479,7 +479,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(
 // of a (group, query block); kp tiles are read as A fragments straight from
 // global memory (the waves of a workgroup walk the same blocks).
 template <typename T, int DP>
-__global__ __launch_bounds__(256) void proxy_lse_kernel(const T* __restrict__ qp,
+__global__ __launch_bounds__(256, 4) void proxy_lse_kernel(const T* __restrict__ qp,
                                                         const T* __restrict__ kp,
                                                         const int32_t* __restrict__ q2k_idx,
                                                         const int32_t* __restrict__ q2k_cnt,
@@ -564,7 +564,7 @@ struct LseCfg {
 };
 
 template <typename T, int DP>
-__global__ __launch_bounds__(256) void proxy_lse128_kernel(const T* __restrict__ qp,
+__global__ __launch_bounds__(256, 3) void proxy_lse128_kernel(const T* __restrict__ qp,
                                                            const T* __restrict__ kp,
                                                            const int32_t* __restrict__ q2k_idx,
                                                            const int32_t* __restrict__ q2k_cnt,

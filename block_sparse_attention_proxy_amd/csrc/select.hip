@@ -148,8 +148,24 @@ hipError_t launch_meta(const Geo& g, hipStream_t s) {
 // Each KV block gives four 32x32 row tiles x four 32-key tiles; the maxima are
 // folded per lane, reduced over the wave, and written 64 blocks at a time.
 
+// Maximum over the 64 lanes, uniform result: row shifts within rows of 16
+// lanes (DPP, no LDS round trips), then the four row maxima by readlane.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  const int ninf = (int)0xff800000u;
+  int x = __float_as_int(v);
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(ninf, x, 0x111, 0xf, 0xf, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(ninf, x, 0x112, 0xf, 0xf, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(ninf, x, 0x114, 0xf, 0xf, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(ninf, x, 0x118, 0xf, 0xf, false))));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(x, 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(x, 31));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(x, 47));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(x, 63));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 template <typename T, int DP, int BQ>
-__global__ __launch_bounds__(256) void proxy_scores_kernel(const T* __restrict__ qp,
+__global__ __launch_bounds__(256, 2) void proxy_scores_kernel(const T* __restrict__ qp,
                                                            const T* __restrict__ kp,
                                                            float* __restrict__ scores, Geo g) {
   constexpr int KSL = DP / 16;
@@ -201,10 +217,10 @@ __global__ __launch_bounds__(256) void proxy_scores_kernel(const T* __restrict__
         for (int ks = 0; ks < KSL; ++ks) Bf[kt][ks] = ld8(src + ks * 16);
       }
     };
-    load_b(0, Bc);
-    for (int J = 0; J < ncand; ++J) {
-      frag_t<T> Bn[4][KSL];
-      if (J + 1 < ncand) load_b(J + 1, Bn);
+    // One KV block: 16 tiles (4 row tiles x 4 key tiles) of 4 products each
+    // and a per-lane maximum, then the wave maximum, stashed in lane J % 64
+    // and stored 64 blocks at a time.
+    auto block = [&](int J, const frag_t<T> (&Bf)[4][KSL]) __attribute__((always_inline)) {
       float m0 = NEG_BIG, m1 = NEG_BIG;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
@@ -212,15 +228,15 @@ __global__ __launch_bounds__(256) void proxy_scores_kernel(const T* __restrict__
         for (int kt = 0; kt < 4; ++kt) {
           f32x16 acc = zero16();
 #pragma unroll
-          for (int ks = 0; ks < KSL; ++ks) mma(acc, A[rt][ks], Bc[kt][ks]);
+          for (int ks = 0; ks < KSL; ++ks) mma(acc, A[rt][ks], Bf[kt][ks]);
           float mm = acc[0];
 #pragma unroll
           for (int i = 1; i < 16; ++i) mm = fmaxf(mm, acc[i]);
           if (BQ == 64 && rt >= 2) m1 = fmaxf(m1, mm); else m0 = fmaxf(m0, mm);
         }
       }
-      m0 = wave_max(m0);
-      if (BQ == 64) m1 = wave_max(m1);
+      m0 = wave_max_dpp(m0);
+      if (BQ == 64) m1 = wave_max_dpp(m1);
       if (lane == (J & 63)) { stash0 = m0; stash1 = m1; }
       if ((J & 63) == 63 || J == ncand - 1) {
         const int base = J & ~63;
@@ -229,12 +245,18 @@ __global__ __launch_bounds__(256) void proxy_scores_kernel(const T* __restrict__
           if (has1) out1[base + lane] = stash1;
         }
       }
-      if (J + 1 < ncand) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int ks = 0; ks < KSL; ++ks) Bc[kt][ks] = Bn[kt][ks];
-      }
+    };
+    // Two register buffers in turn: block J + 1 loads while block J is
+    // computed (the last block is fetched again past the end, so the count
+    // of loads in flight is always one block).
+    frag_t<T> B1[4][KSL];
+    load_b(0, Bc);
+    for (int J = 0; J < ncand; J += 2) {
+      load_b(J + 1 < ncand ? J + 1 : J, B1);
+      block(J, Bc);
+      if (J + 1 >= ncand) break;
+      load_b(J + 2 < ncand ? J + 2 : J + 1, Bc);
+      block(J + 1, B1);
     }
   }
 }
