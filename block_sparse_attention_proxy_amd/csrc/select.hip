@@ -355,7 +355,7 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x, int lane) {
 // l reads the four bins of digits 255 - 4l ... 252 - 4l, highest first) and
 // room for the 64 members of a threshold bin.
 struct SelLds {
-  uint32_t hist[256];
+  uint32_t hist[260];                             // 256 bins + a bin for keys that do not count
   uint32_t mkey[64];
   int32_t mj[64];
 };
@@ -400,7 +400,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
                                                      int32_t* __restrict__ q2k_cnt, Geo g) {
   __shared__ SelLds lds[4];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform, so that every per-row value below lives in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= (int64_t)g.Hkv * g.nqb) return;      // no workgroup barriers in this kernel
   const int grp = (int)(row / g.nqb);
@@ -426,12 +427,23 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
     if (ncand <= 64 * SEL_REG) {
       uint32_t key[SEL_REG];
       uint32_t kmin = 0xffffffffu, kmax = 0u;
+      // the row through a buffer descriptor: lane offsets are immediates and
+      // reads past the row's end return zero (and are marked invalid)
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)srow, (short)0, ncand * 4, 0x00020000);
+      // all of the row's loads are issued before the first is used
+      uint32_t raw[SEL_REG];
+#pragma unroll
+      for (int r = 0; r < SEL_REG; ++r)
+        if (r * 64 < ncand) raw[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4 + r * 256, 0, 0);
 #pragma unroll
       for (int r = 0; r < SEL_REG; ++r) {
         if (r * 64 >= ncand) break;
         const int j = r * 64 + lane;
-        key[r] = j < ncand ? order_key(srow[j]) : 0u;
-        if (j < ncand) { kmin = min(kmin, key[r]); kmax = max(kmax, key[r]); }
+        const uint32_t kv = order_key(__builtin_bit_cast(float, raw[r]));
+        key[r] = j < ncand ? kv : 0u;
+        kmin = min(kmin, j < ncand ? kv : 0xffffffffu);
+        kmax = max(kmax, key[r]);
       }
       kmin = wave_min(kmin);
       kmax = wave_max(kmax);
@@ -452,8 +464,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
 #pragma unroll
           for (int r = 0; r < SEL_REG; ++r) {
             if (r * 64 >= ncand) break;
-            if (r * 64 + lane < ncand && (key[r] & pmask) == prefix)
-              atomicAdd(&w.hist[255u - ((key[r] >> lo) & 255u)], 1u);
+            const bool cnt_it = r * 64 + lane < ncand && (key[r] & pmask) == prefix;
+            atomicAdd(&w.hist[cnt_it ? 255u - ((key[r] >> lo) & 255u) : 256u], 1u);
           }
           uint32_t digit;
           int cnt;
