@@ -96,7 +96,8 @@ KERNEL_SOURCES = {
     "fwd": ["block_sparse_attention_proxy_amd/csrc/attn_fwd.hip"] + _HDR,
     "proxy_lse": ["block_sparse_attention_proxy_amd/csrc/attn_fwd.hip"] + _HDR,
     "bwd_dq": ["block_sparse_attention_proxy_amd/csrc/attn_bwd.hip"] + _HDR,
-    "bwd_dkdv": ["block_sparse_attention_proxy_amd/csrc/attn_bwd.hip"] + _HDR,
+    "bwd_dkdv": ["block_sparse_attention_proxy_amd/csrc/attn_bwd.hip",
+                 "block_sparse_attention_proxy_amd/csrc/attn_bwd_kv.hip"] + _HDR,
 }
 
 

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
   typedef typename C::TK TK;
   typedef typename C::TP TP;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hi = lane >> 5;
   const int NU = g.G * (g.Bq / 32);
   const int nwg = (NU + 3) >> 2;
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
   typedef typename C::TQ TQ;
   typedef typename C::TP TP;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hi = lane >> 5;
   const int bid = xcd_remap_b(blockIdx.x, gridDim.x);
   const int grp = bid / g.nkb;

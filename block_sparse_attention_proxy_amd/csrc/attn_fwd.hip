@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(
   T* smem = reinterpret_cast<T*>(smem_raw);
   static_assert(C::NK >= 1, "tile split");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hi = lane >> 5;
   const int NU = g.G * (g.Bq / (32 * QT));
   const int nwg = (NU + 3) >> 2;
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(256, 4) void proxy_lse_kernel(const T* __restrict__
                                                         const int32_t* __restrict__ q2k_idx,
                                                         const int32_t* __restrict__ q2k_cnt,
                                                         float* __restrict__ lse_p, Geo g) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hi = lane >> 5;
   const int nwq = g.Bq / 32;                     // waves per query block
   const int per_wg = 4 / nwq;                    // query blocks per workgroup
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(256, 3) void proxy_lse128_kernel(const T* __restric
   typedef LseCfg<T, DP> C;
   typedef typename C::TP TP;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hi = lane >> 5;
   const int item = xcd_remap(blockIdx.x, gridDim.x);   // the grid is exactly Hkv * nqb
   const int grp = item / g.nqb;

@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256, 2) void proxy_scores_kernel(const T* __restric
                                                            float* __restrict__ scores, Geo g) {
   constexpr int KSL = DP / 16;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = blockIdx.x % g.Hkv;
   const int unit = (blockIdx.x / g.Hkv) * 4 + wave;
   if (unit >= g.n_units) return;   // no barriers below
