@@ -252,6 +252,67 @@ def calibrate_copy(mib):
     return 0
 
 
+# rocprofv3 kernel names (mangled or demangled) -> the library's kernel names
+_TRACE_KERNELS = (("proxy_scores_kernel", "proxy_scores"), ("select_kernel", "select"),
+                  ("proxy_lse", "proxy_lse"), ("fwd_kernel", "fwd"), ("dq_kernel", "bwd_dq"),
+                  ("dkdv", "bwd_dkdv"))
+
+
+def _counter_per_dispatch(csv_dir, counter):
+    """Mean value of one counter per dispatch of each library kernel (and of
+    the plain copy) in a rocprofv3 counter-collection CSV directory."""
+    import csv
+    import glob
+    sums = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                key = "copy" if "copyBuffer" in name else next(
+                    (k for pat, k in _TRACE_KERNELS if pat in name), None)
+                if key is None:
+                    continue
+                d = sums.setdefault(key, {})
+                d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in sums.items()}
+
+
+def write_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib):
+    """HBM bytes per launch of each kernel from two counter runs (FETCH_SIZE,
+    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
+    for a plain copy of copy_mib MiB; written to profiles/traffic.json with
+    the hash of the kernel sources they were taken on."""
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+    cf = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE")["copy"]
+    cw = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE")["copy"]
+    fetch_factor = copy_mib * 1024.0 / cf
+    write_factor = copy_mib * 1024.0 / cw
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    ent = {}
+    print(f"copy: FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB per dispatch "
+          f"-> factors {fetch_factor:.5f}, {write_factor:.5f}")
+    print("| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) |")
+    print("|---|---:|---:|---:|")
+    for k in KERNEL_SOURCES:
+        if k not in fetch or k not in write:
+            continue
+        b = fetch[k] * 1024 * fetch_factor + write[k] * 1024 * write_factor
+        ent[k] = {"bytes_per_launch": int(round(b)), "fetch_kib": round(fetch[k], 1),
+                  "write_kib": round(write[k], 1), "fetch_factor": round(fetch_factor, 5),
+                  "write_factor": round(write_factor, 5),
+                  "source_hash": source_hash(KERNEL_SOURCES[k])}
+        print(f"| {k} | {fetch[k]:.1f} | {write[k]:.1f} | {b:.4e} |")
+    data[workload] = ent
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1)
+        fh.write("\n")
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,9 +334,16 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB, 4 times (the "
                          "known-size reference for scaling HBM byte counters), then exit")
+    ap.add_argument("--write-traffic", nargs=4, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="no GPU work: turn four rocprofv3 counter runs (this workload's step with "
+                         "FETCH_SIZE, then WRITE_SIZE; the copy with each) into profiles/traffic.json")
+    ap.add_argument("--copy-mib", type=int, default=1024, help="size of the copy in --write-traffic")
     a = ap.parse_args(argv)
     if a.calibrate_copy:
         return calibrate_copy(a.calibrate_copy)
+    if a.write_traffic:
+        return write_traffic(a.workload, *a.write_traffic, a.copy_mib)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (this path has no "
               "multi-GPU mode: each GPU would run the same op on its own documents).", file=sys.stderr)

@@ -355,7 +355,7 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x, int lane) {
 // l reads the four bins of digits 255 - 4l ... 252 - 4l, highest first) and
 // room for the 64 members of a threshold bin.
 struct SelLds {
-  uint32_t hist[260];                             // 256 bins + a bin for keys that do not count
+  uint32_t hist[256];
   uint32_t mkey[64];
   int32_t mj[64];
 };
@@ -464,8 +464,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
 #pragma unroll
           for (int r = 0; r < SEL_REG; ++r) {
             if (r * 64 >= ncand) break;
-            const bool cnt_it = r * 64 + lane < ncand && (key[r] & pmask) == prefix;
-            atomicAdd(&w.hist[cnt_it ? 255u - ((key[r] >> lo) & 255u) : 256u], 1u);
+            if (r * 64 + lane < ncand && (key[r] & pmask) == prefix)
+              atomicAdd(&w.hist[255u - ((key[r] >> lo) & 255u)], 1u);
           }
           uint32_t digit;
           int cnt;
