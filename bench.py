@@ -81,11 +81,21 @@ def flop_model(w, seqlens, scored_pairs):
     return f
 
 
+def _code_only(text):
+    """The source without // and /* */ comments and without blank or
+    indentation-only differences (no string literal here holds either)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).strip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_hash(files):
+    """Hash of the code of a kernel's sources: edits to comments keep it."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -137,10 +137,10 @@ __device__ __forceinline__ bf16x8 tr_pair2(uint32_t a, uint32_t b) {
 //       in registers), P = exp2(S s log2e - lse2), dS = P (dP - D), both as
 //       bf16 fragments into an exchange buffer; T += P; at a chunk's last
 //       head the proxy scores Y = qp kp^T and dY / (lam s_p) = Q - T / G
-//       into a second exchange buffer.  It also issues every copy.
+//       into a second exchange buffer.
 //   accumulation wave, stage s - 1:  dV += P^T dO and dK += dS^T Q
 //       (16 MFMAs, transposed Q / dO fragments from the ring); at a chunk's
-//       last head dkp += dY^T qp.
+//       last head dkp += dY^T qp.  It also issues every copy.
 //
 // One workgroup barrier per stage orders the two: the exchange buffers are
 // double-buffered by stage parity, and the ring slot a stage occupies is
@@ -156,7 +156,7 @@ constexpr int WS_DY = WS_XB + 2 * 4 * WS_XB_KG;        // dY fragments [kg][2][6
 constexpr int WS_DUMMY = WS_DY + 4 * 2 * 1024;         // target of the placeholder copy, 256 B per wave
 constexpr int WS_LDS = WS_DUMMY + 4 * 256;
 static_assert(WS_LDS <= 160 * 1024, "LDS budget");
-constexpr int WS_COPIES = 6;                           // per softmax wave per stage (uniform)
+constexpr int WS_COPIES = 6;                           // per accumulation wave per stage (uniform)
 constexpr int WS_LATER = WS_COPIES * (WS_NB - 3);      // copies of stages s+1 .. s+NB-3
 
 __device__ __forceinline__ void lds_st16(uint32_t addr, const bf16x8& v) {
