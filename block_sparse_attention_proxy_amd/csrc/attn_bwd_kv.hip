@@ -419,37 +419,51 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
     int i_tr = t0 + (len > 0 ? lst[0] - qb0 : 0) * g.Bq;
     set_chunk(i_tr, len > 0);
     uint32_t i_so = 0, i_fo = 0, i_qo = 0;                 // LDS: slot, float slot, qp slot
-    auto issue = [&]() __attribute__((always_inline)) {
-      const i32x4 sq = make_srd(i_qa, i_nq);
-      const i32x4 sd = make_srd(i_qa + dq_off, i_nq);
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        bdma16(sq, voQ[jj], ldQ[jj] + i_so);
-        bdma16(sd, voQ[jj], ldQ[jj] + i_so + TILE_B);
-      }
-      bdma4(make_srd(i_fa, i_nf), voF, ldF + i_fo);
-      if (i_hl == G - 1) {
-        bdma16(make_srd(i_pa, i_np), voP, ldP + i_qo);
-        i_qo ^= QP_TILE;
-        i_hl = 0;
-        if (++i_c == nch) {
-          i_c = 0;
-          ++i_li;
-          i_tr = t0 + i_next * g.Bq;
-          const int nx = i_li + 1 < len ? i_li + 1 : len - 1;
-          if (nx >= 0) i_next = __builtin_amdgcn_readfirstlane(lst[nx]) - qb0;
-        } else {
-          i_tr += 32;
-        }
-        set_chunk(i_tr, i_li < len);
+    // One stage's copies in six parts, so that the main loop can spread them
+    // between its products: a part that waits for room in the memory
+    // pipeline then stalls one product, not the whole batch.
+    i32x4 i_sq, i_sd;
+    auto issue_part = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      if constexpr (k == 0) {
+        i_sq = make_srd(i_qa, i_nq);
+        i_sd = make_srd(i_qa + dq_off, i_nq);
+        bdma16(i_sq, voQ[0], ldQ[0] + i_so);
+      } else if constexpr (k == 1) {
+        bdma16(i_sd, voQ[0], ldQ[0] + i_so + TILE_B);
+      } else if constexpr (k == 2) {
+        bdma16(i_sq, voQ[1], ldQ[1] + i_so);
+      } else if constexpr (k == 3) {
+        bdma16(i_sd, voQ[1], ldQ[1] + i_so + TILE_B);
+      } else if constexpr (k == 4) {
+        bdma4(make_srd(i_fa, i_nf), voF, ldF + i_fo);
       } else {
-        bdma4(make_srd(fw, 0u), voF, ldD);               // placeholder: keeps the copy count uniform
-        ++i_hl;
-        i_qa += KD * 2;
-        i_fa += fstep;
+        if (i_hl == G - 1) {
+          bdma16(make_srd(i_pa, i_np), voP, ldP + i_qo);
+          i_qo ^= QP_TILE;
+          i_hl = 0;
+          if (++i_c == nch) {
+            i_c = 0;
+            ++i_li;
+            i_tr = t0 + i_next * g.Bq;
+            const int nx = i_li + 1 < len ? i_li + 1 : len - 1;
+            if (nx >= 0) i_next = __builtin_amdgcn_readfirstlane(lst[nx]) - qb0;
+          } else {
+            i_tr += 32;
+          }
+          set_chunk(i_tr, i_li < len);
+        } else {
+          bdma4(make_srd(fw, 0u), voF, ldD);             // placeholder: keeps the copy count uniform
+          ++i_hl;
+          i_qa += KD * 2;
+          i_fa += fstep;
+        }
+        i_so = i_so == (WS_NB - 1) * WS_SLOT ? 0u : i_so + WS_SLOT;
+        i_fo = i_fo == (WS_NB - 1) * FL_SLOT ? 0u : i_fo + FL_SLOT;
       }
-      i_so = i_so == (WS_NB - 1) * WS_SLOT ? 0u : i_so + WS_SLOT;
-      i_fo = i_fo == (WS_NB - 1) * FL_SLOT ? 0u : i_fo + FL_SLOT;
+    };
+    auto issue = [&]() __attribute__((always_inline)) {
+      static_for<WS_COPIES>([&](auto kc) __attribute__((always_inline)) { issue_part(kc); });
     };
     for (int j = 0; j < WS_NB - 2; ++j) issue();
     wait_vmcnt<WS_COPIES * (WS_NB - 3)>();               // stage 0
@@ -463,11 +477,10 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
     for (int dt = 0; dt < KDP / 32; ++dt) dKp[dt] = zero16();
     int hl = 0;                                            // head of stage s - 1
     uint32_t a_so = 0, a_qo = 0;                           // LDS: its slot, its chunk's qp slot
-    for (int s = 0; s <= nst; ++s) {
-      if (s < nst) wait_vmcnt<WS_COPIES * (WS_NB - 4)>();   // stage s + 1
-      __syncthreads();
-      if (s < nst) issue();
-      if (s == 0) continue;
+    // Stage s - 1's products, with stage s + 4's copies between them when
+    // ISSUE (every iteration but the last).
+    auto accumulate = [&](int s, auto issue_c) __attribute__((always_inline)) {
+      constexpr bool ISSUE = decltype(issue_c)::value;
       const int sp = s - 1;
       const uint32_t cb = bC + a_so;
       a_so = a_so == (WS_NB - 1) * WS_SLOT ? 0u : a_so + WS_SLOT;
@@ -497,6 +510,11 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
           if constexpr (m & 1) dK[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, op[m], dK[dt], 0, 0, 0);
           else dV[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, op[m], dV[dt], 0, 0, 0);
           if constexpr (m + LOOK < 16) rd(std::integral_constant<int, m + LOOK>());
+          if constexpr (ISSUE && (m & 1) && m / 2 < WS_COPIES) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_part(std::integral_constant<int, m / 2>());
+            __builtin_amdgcn_sched_barrier(0);
+          }
         });
       }
       if (hl == G - 1) {
@@ -518,7 +536,20 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
       } else {
         ++hl;
       }
+    };
+    if (nst > 0) {
+      // iteration 0: stage 0 has landed; stage 4's copies, no products
+      wait_vmcnt<WS_COPIES * (WS_NB - 4)>();
+      __syncthreads();
+      issue();
+      for (int s = 1; s < nst; ++s) {
+        wait_vmcnt<WS_COPIES * (WS_NB - 4)>();             // stage s + 1
+        __syncthreads();
+        accumulate(s, std::true_type());
+      }
     }
+    __syncthreads();
+    if (nst > 0) accumulate(nst, std::false_type());
     wait_vmcnt<0>();                                       // copies past the last stage
     // outputs: lane holds column d = dt * 32 + col for 16 key rows
     const float lam_ps = g.lam * g.pscale;
