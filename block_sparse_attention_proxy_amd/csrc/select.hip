@@ -208,33 +208,64 @@ __global__ __launch_bounds__(256, 2) void proxy_scores_kernel(const T* __restric
     float* out1 = out0 + nk;
     float stash0 = 0.f, stash1 = 0.f;
 
-    frag_t<T> Bc[4][KSL];
-    auto load_b = [&](int J, frag_t<T> (&Bf)[4][KSL]) __attribute__((always_inline)) {
+    // kp of one KV block as B fragments, in four 32-key slices.  Tiles run
+    // slice by slice (kt outer), so slice kt is refilled with the next
+    // block's keys as soon as its fourth tile has been issued: the load has
+    // the other three slices' products to land in.
+    frag_t<T> Bf[4][KSL];
+    auto load_slice = [&](int J, int kt) __attribute__((always_inline)) {
+      const T* src = kp + ((int64_t)(t0 + J * 128 + kt * 32 + col) * Hp + grp) * DP + hi8;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const T* src = kp + ((int64_t)(t0 + J * 128 + kt * 32 + col) * Hp + grp) * DP + hi8;
-#pragma unroll
-        for (int ks = 0; ks < KSL; ++ks) Bf[kt][ks] = ld8(src + ks * 16);
-      }
+      for (int ks = 0; ks < KSL; ++ks) Bf[kt][ks] = ld8(src + ks * 16);
     };
-    // One KV block: 16 tiles (4 row tiles x 4 key tiles) of 4 products each
-    // and a per-lane maximum, then the wave maximum, stashed in lane J % 64
-    // and stored 64 blocks at a time.
-    auto block = [&](int J, const frag_t<T> (&Bf)[4][KSL]) __attribute__((always_inline)) {
+    // maximum of a tile's 16 values folded into m: a tree of depth three
+    auto fold = [](float m, const f32x16& a) __attribute__((always_inline)) {
+      const float t0 = fmaxf(fmaxf(a[0], a[1]), a[2]), t1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+      const float t2 = fmaxf(fmaxf(a[6], a[7]), a[8]), t3 = fmaxf(fmaxf(a[9], a[10]), a[11]);
+      const float t4 = fmaxf(fmaxf(a[12], a[13]), a[14]);
+      const float u0 = fmaxf(fmaxf(t0, t1), t2), u1 = fmaxf(fmaxf(t3, t4), a[15]);
+      return fmaxf(fmaxf(m, u0), u1);
+    };
+    // slices issued in order (the loop waits for slice kt with the later
+    // slices still in flight)
+    static_for<4>([&](auto ktc) __attribute__((always_inline)) {
+      load_slice(0, decltype(ktc)::value);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    for (int J = 0; J < ncand; ++J) {
+      const int Jn = J + 1 < ncand ? J + 1 : J;       // past the end: the last block again
       float m0 = NEG_BIG, m1 = NEG_BIG;
+      // 16 tiles (4 key slices x 4 row tiles) of 4 products each, two tiles
+      // at a time with their products alternating (no product waits for the
+      // one before it), into four accumulators by turns: a pair's maxima are
+      // taken after the next pair's products have been issued.
+      f32x16 acc[4];
+      auto fold_tile = [&](auto nc) __attribute__((always_inline)) {
+        constexpr int n = decltype(nc)::value, rt = n % 4;
+        if (BQ == 64 && rt >= 2) m1 = fold(m1, acc[n & 3]);
+        else m0 = fold(m0, acc[n & 3]);
+      };
+      static_for<8>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int pr = decltype(pc)::value, n0 = 2 * pr, n1 = 2 * pr + 1;
+        constexpr int kt = n0 / 4, rt0 = n0 % 4, rt1 = n1 % 4;
+        acc[n0 & 3] = zero16();
+        acc[n1 & 3] = zero16();
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          f32x16 acc = zero16();
-#pragma unroll
-          for (int ks = 0; ks < KSL; ++ks) mma(acc, A[rt][ks], Bf[kt][ks]);
-          float mm = acc[0];
-#pragma unroll
-          for (int i = 1; i < 16; ++i) mm = fmaxf(mm, acc[i]);
-          if (BQ == 64 && rt >= 2) m1 = fmaxf(m1, mm); else m0 = fmaxf(m0, mm);
+        for (int ks = 0; ks < KSL; ++ks) {
+          mma(acc[n0 & 3], A[rt0][ks], Bf[kt][ks]);
+          mma(acc[n1 & 3], A[rt1][ks], Bf[kt][ks]);
         }
-      }
+        if constexpr (rt1 == 3) load_slice(Jn, kt);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (pr > 0) {
+          fold_tile(std::integral_constant<int, n0 - 2>());
+          fold_tile(std::integral_constant<int, n1 - 2>());
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      fold_tile(std::integral_constant<int, 14>());
+      fold_tile(std::integral_constant<int, 15>());
+      // the wave maximum, stashed in lane J % 64 and stored 64 blocks at a time
       m0 = wave_max_dpp(m0);
       if (BQ == 64) m1 = wave_max_dpp(m1);
       if (lane == (J & 63)) { stash0 = m0; stash1 = m1; }
@@ -245,18 +276,6 @@ __global__ __launch_bounds__(256, 2) void proxy_scores_kernel(const T* __restric
           if (has1) out1[base + lane] = stash1;
         }
       }
-    };
-    // Two register buffers in turn: block J + 1 loads while block J is
-    // computed (the last block is fetched again past the end, so the count
-    // of loads in flight is always one block).
-    frag_t<T> B1[4][KSL];
-    load_b(0, Bc);
-    for (int J = 0; J < ncand; J += 2) {
-      load_b(J + 1 < ncand ? J + 1 : J, B1);
-      block(J, Bc);
-      if (J + 1 >= ncand) break;
-      load_b(J + 2 < ncand ? J + 2 : J + 1, Bc);
-      block(J + 1, B1);
     }
   }
 }
