@@ -280,11 +280,178 @@ __global__ __launch_bounds__(256, 2) void proxy_scores_kernel(const T* __restric
   }
 }
 
+// bf16, dp = 64: the same units and tile order, with kp staged through LDS.
+// Loading B fragments straight from global memory makes every 16-byte lane
+// read touch its own 128-byte line (32 lines per instruction), which keeps
+// the L1 tag lookups, not the matrix cores, the bound.  Here each wave copies
+// its 32-key kp slices (4 KiB, 8 whole rows per instruction) into a private
+// ring of SC_NS slots by DMA, SC_NS - 1 slices ahead, and reads the fragments
+// back from the swizzled slot.  A wave reads only its own slots, so a count
+// of its copies in flight (vmcnt) is the only synchronisation.
+constexpr int SC_NS = 5;                            // slots per wave
+constexpr int SC_SLICE = 32 * 64 * 2;               // bytes per slice
+constexpr int SC_LDS = 4 * SC_NS * SC_SLICE;        // per workgroup: 80 KiB
+
+template <int BQ>
+__global__ __launch_bounds__(256, 2) void proxy_scores_lds_kernel(const bf16* __restrict__ qp,
+                                                               const bf16* __restrict__ kp,
+                                                               float* __restrict__ scores, Geo g) {
+  constexpr int DP = 64, KSL = DP / 16;
+  typedef Tile<bf16, DP> TP;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = blockIdx.x % g.Hkv;
+  const int unit = (blockIdx.x / g.Hkv) * 4 + wave;
+  if (unit >= g.n_units) return;   // no barriers below
+  const int r = find_segment<int32_t>(g.unit0, g.B, unit);
+  const int b = g.order[r];
+  const int p = unit - g.unit0[r];
+  const int t0 = g.cu[b];
+  const int L = g.cu[b + 1] - t0;
+  const int nt = (L + 127) >> 7;
+  const int nk = nt;
+  const int nq = (L + BQ - 1) / BQ;
+  const int64_t s0 = g.s0[b];
+  const int Hp = g.Hkv;
+  const int col = lane & 31;
+  const int hi8 = (lane >> 5) * 8;
+  const uint32_t ring = lds_offset(smem_raw) + (uint32_t)wave * SC_NS * SC_SLICE;
+  // copy side: lane l moves row 8 j + (l >> 3), 16-byte chunk l & 7 of a slice
+  // (source chunk swizzled so that the slot holds the Tile layout)
+  // (the swizzle of rows 8 j + r depends on j only through j & 1)
+  const int crow = lane >> 3;
+  const int64_t csrc0 = (int64_t)crow * Hp * DP + swz<8>(crow, lane & 7) * 8;
+  const int64_t csrc1 = (int64_t)(8 + crow) * Hp * DP + swz<8>(8 + crow, lane & 7) * 8;
+  const int64_t crow16 = (int64_t)16 * Hp * DP;
+  // read side: fragment ks of this lane's key row in a slot
+  const uint32_t rd0 = (uint32_t)TP::off(col, hi8) * 2;
+
+  for (int pass = 0; pass < 2; ++pass) {
+    const int tile = pass == 0 ? p : nt - 1 - p;
+    if (pass == 1 && tile == p) break;
+    const int ncand = tile - g.span;              // blocks below the window's span
+    if (ncand <= g.topk - 1) continue;            // all of them are taken; nothing to score
+
+    bf16x8 A[4][KSL];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      int row = tile * 128 + rt * 32 + col;
+      row = row < L ? row : L - 1;                // duplicate rows leave the max unchanged
+      const bf16* src = qp + ((int64_t)(t0 + row) * Hp + grp) * DP + hi8;
+#pragma unroll
+      for (int ks = 0; ks < KSL; ++ks) A[rt][ks] = ld8(src + ks * 16);
+    }
+    const int I0 = (BQ == 128) ? tile : 2 * tile;
+    const bool has1 = (BQ == 64) && (2 * tile + 1 < nq);
+    float* out0 = scores + (int64_t)grp * g.score_elems + s0 + (int64_t)I0 * nk;
+    float* out1 = out0 + nk;
+    float stash0 = 0.f, stash1 = 0.f;
+    // The register loads above complete before any copy is issued, so that
+    // the copies are the only vector-memory operations the waits count.
+    wait_vmcnt<0>();
+
+    const int nsl = ncand * 4;                    // slices: block J, key slice kt -> 4 J + kt
+    const bf16* kbase = kp + ((int64_t)t0 * Hp + grp) * DP;
+    int i_q = 0;                                  // next slice to copy
+    uint32_t i_slot = 0, c_slot = 0;              // byte offsets of the next copy's / read's slot
+    auto copy_next = [&]() __attribute__((always_inline)) {
+      const int q = i_q < nsl ? i_q : nsl - 1;    // past the end: the last slice again
+      const bf16* src = kbase + (int64_t)q * 32 * Hp * DP;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(src + (j & 1 ? csrc1 : csrc0) + (j >> 1) * crow16, ring + i_slot + j * 1024);
+      ++i_q;
+      i_slot = i_slot == (SC_NS - 1) * SC_SLICE ? 0u : i_slot + SC_SLICE;
+    };
+    auto read_slice = [&](bf16x8 (&Bf)[KSL]) __attribute__((always_inline)) {
+      const uint32_t a = ring + c_slot + rd0;
+#pragma unroll
+      for (int ks = 0; ks < KSL; ++ks) Bf[ks] = lds_ld8<0>(a ^ (uint32_t)(ks << 5));
+      c_slot = c_slot == (SC_NS - 1) * SC_SLICE ? 0u : c_slot + SC_SLICE;
+    };
+    auto fold = [](float m, const f32x16& a) __attribute__((always_inline)) {
+      const float t0 = fmaxf(fmaxf(a[0], a[1]), a[2]), t1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+      const float t2 = fmaxf(fmaxf(a[6], a[7]), a[8]), t3 = fmaxf(fmaxf(a[9], a[10]), a[11]);
+      const float t4 = fmaxf(fmaxf(a[12], a[13]), a[14]);
+      const float u0 = fmaxf(fmaxf(t0, t1), t2), u1 = fmaxf(fmaxf(t3, t4), a[15]);
+      return fmaxf(fmaxf(m, u0), u1);
+    };
+#pragma unroll
+    for (int j = 0; j < SC_NS - 1; ++j) copy_next();
+    wait_vmcnt<4 * (SC_NS - 2)>();                // slice 0
+    bf16x8 Bc[KSL], Bn[KSL];
+    read_slice(Bc);
+    f32x16 acc[4];
+    for (int J = 0; J < ncand; ++J) {
+      float m0 = NEG_BIG, m1 = NEG_BIG;
+      static_for<4>([&](auto ktc) __attribute__((always_inline)) {
+        constexpr int kt = decltype(ktc)::value;
+        // the slot of the slice before this one is free: refill it, then
+        // fetch the next slice's fragments once they have landed
+        copy_next();
+        wait_vmcnt<4 * (SC_NS - 2)>();
+        static_for<2>([&](auto hc) __attribute__((always_inline)) {
+          constexpr int h = decltype(hc)::value, rt0 = 2 * h, rt1 = 2 * h + 1;
+          constexpr int a0 = h ? 2 : 0;                 // accumulator pair of this half
+          acc[a0] = zero16();
+          acc[a0 + 1] = zero16();
+#pragma unroll
+          for (int ks = 0; ks < KSL; ++ks) {
+            mma(acc[a0], A[rt0][ks], Bc[ks]);
+            mma(acc[a0 + 1], A[rt1][ks], Bc[ks]);
+          }
+          if constexpr (h == 0) read_slice(Bn);
+          __builtin_amdgcn_sched_barrier(0);
+          // maxima of the previous pair (the last pair of the block before
+          // is folded at that block's end)
+          if constexpr (kt > 0 || h > 0) {
+            constexpr int pr0 = h == 0 ? 2 : 0;   // its first row tile
+            const int pa = a0 ^ 2;
+            if (BQ == 64 && pr0 >= 2) { m1 = fold(m1, acc[pa]); m1 = fold(m1, acc[pa + 1]); }
+            else { m0 = fold(m0, acc[pa]); m0 = fold(m0, acc[pa + 1]); }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int ks = 0; ks < KSL; ++ks) Bc[ks] = Bn[ks];
+      });
+      // last pair of the block: row tiles 2, 3 of key slice 3, accumulators 2, 3
+      if (BQ == 64) { m1 = fold(m1, acc[2]); m1 = fold(m1, acc[3]); }
+      else { m0 = fold(m0, acc[2]); m0 = fold(m0, acc[3]); }
+      m0 = wave_max_dpp(m0);
+      if (BQ == 64) m1 = wave_max_dpp(m1);
+      if (lane == (J & 63)) { stash0 = m0; stash1 = m1; }
+      if ((J & 63) == 63 || J == ncand - 1) {
+        const int base = J & ~63;
+        if (lane <= (J & 63)) {
+          out0[base + lane] = stash0;
+          if (has1) out1[base + lane] = stash1;
+        }
+      }
+    }
+    wait_vmcnt<0>();                              // copies past the end, before the ring is reused
+  }
+}
+
 template <typename T, int DP>
 static hipError_t scores_dispatch_bq(const Geo& g, const void* qp, const void* kp, float* scores,
                                      hipStream_t s) {
   int nblk = (g.n_units + 3) / 4 * g.Hkv;
   if (nblk == 0) return hipSuccess;
+  if constexpr (sizeof(T) == 2 && DP == 64) {
+    static LdsLimitOnce lds_limit;
+    const hipError_t e = lds_limit.ensure({{(const void*)proxy_scores_lds_kernel<128>, SC_LDS},
+                                           {(const void*)proxy_scores_lds_kernel<64>, SC_LDS}});
+    if (e != hipSuccess) return e;
+    { ProfScope _ps("proxy_scores", s);
+    if (g.Bq == 128)
+      hipLaunchKernelGGL((proxy_scores_lds_kernel<128>), dim3(nblk), dim3(256), SC_LDS, s,
+                         (const bf16*)qp, (const bf16*)kp, scores, g);
+    else
+      hipLaunchKernelGGL((proxy_scores_lds_kernel<64>), dim3(nblk), dim3(256), SC_LDS, s,
+                         (const bf16*)qp, (const bf16*)kp, scores, g); }
+    return hipGetLastError();
+  }
   if (g.Bq == 128)
     { ProfScope _ps("proxy_scores", s);
     hipLaunchKernelGGL((proxy_scores_kernel<T, DP, 128>), dim3(nblk), dim3(256), 0, s,
@@ -745,8 +912,8 @@ hipError_t launch_select(const Geo& g, const float* scores, int32_t* q2k_idx, in
 namespace msa {
 int select_kernels(KernelEntry* out, int max) {
   const KernelEntry all[] = {
-      {"proxy_scores<bf16,dp64,bq128>", (const void*)proxy_scores_kernel<bf16, 64, 128>, 256, 0},
-      {"proxy_scores<bf16,dp64,bq64>", (const void*)proxy_scores_kernel<bf16, 64, 64>, 256, 0},
+      {"proxy_scores<bf16,dp64,bq128>", (const void*)proxy_scores_lds_kernel<128>, 256, SC_LDS},
+      {"proxy_scores<bf16,dp64,bq64>", (const void*)proxy_scores_lds_kernel<64>, 256, SC_LDS},
       {"proxy_scores<bf16,dp32,bq64>", (const void*)proxy_scores_kernel<bf16, 32, 64>, 256, 0},
       {"proxy_scores<f32,dp32,bq64>", (const void*)proxy_scores_kernel<float, 32, 64>, 256, 0},
       {"select", (const void*)select_kernel, 256, 0},
