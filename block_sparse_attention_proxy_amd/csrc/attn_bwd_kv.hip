@@ -86,20 +86,6 @@ __device__ __forceinline__ f32x4 lds_f4(uint32_t base) {
   return *reinterpret_cast<lds_f32x4*>(reinterpret_cast<lds_u8*>((uintptr_t)base) + OFF);
 }
 
-// a ^ C in a vector register, opaque to the compiler so that it is formed
-// where it is used instead of being hoisted out of the stage loop (where it
-// would hold a register for the whole kernel).
-template <uint32_t C>
-__device__ __forceinline__ uint32_t xr(uint32_t a) {
-  if constexpr (C == 0) {
-    return a;
-  } else {
-    uint32_t r;
-    asm volatile("v_xor_b32 %0, %2, %1" : "=v"(r) : "v"(a), "i"(C));
-    return r;
-  }
-}
-
 // v if (x + C) < w as unsigned integers, else 0.  The causal / document mask
 // of an accumulator element with constant row offset C: x = (row of element
 // 0) - lo and w = hi - lo, so the test is lo <= row < hi.  One asm block per

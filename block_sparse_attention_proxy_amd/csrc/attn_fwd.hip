@@ -48,8 +48,9 @@ __device__ __forceinline__ void store4<float>(float* dst, float a, float b, floa
   *reinterpret_cast<f32x4*>(dst) = r;
 }
 
-template <typename T, int D, int DP, int QT>
+template <typename T, int D, int DP, int QT, int NW>
 struct FwdCfg {
+  static constexpr int NT = 64 * NW;                     // threads per workgroup
   static constexpr int KC = 64;                          // keys per stage
   typedef Tile<T, D> TK;                                 // K and V rows, swizzled
   static constexpr int KS = KC * D;
@@ -57,33 +58,34 @@ struct FwdCfg {
   static constexpr int NBUF = 3;                         // LDS ring (two stages in flight)
   static constexpr int LDS_BYTES = NBUF * STAGE * (int)sizeof(T);
   static constexpr int EPC = TK::EPC, CPR = TK::CPR;
-  static constexpr int NK = KC * CPR / 256;              // chunks per thread per tensor
+  static constexpr int NK = KC * CPR / NT;               // chunks per thread per tensor
 };
 
 template <typename U>
 struct TypeTag { using type = U; };
 
-template <typename T, int D, int DP, int QT>
-__global__ __launch_bounds__(256) void fwd_kernel(
+template <typename T, int D, int DP, int QT, int NW>
+__global__ __launch_bounds__(64 * NW) void fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_cnt,
     T* __restrict__ o, float* __restrict__ lse, Geo g) {
-  typedef FwdCfg<T, D, DP, QT> C;
+  typedef FwdCfg<T, D, DP, QT, NW> C;
   typedef typename C::TK TK;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* smem = reinterpret_cast<T*>(smem_raw);
+  constexpr int NT = C::NT;
   static_assert(C::NK >= 1, "tile split");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hi = lane >> 5;
   const int NU = g.G * (g.Bq / (32 * QT));
-  const int nwg = (NU + 3) >> 2;
+  const int nwg = (NU + NW - 1) / NW;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t item = bid / nwg;
   const int wgi = bid % nwg;
   const int grp = (int)(item / g.nqb);
   const int QB = (int)(item % g.nqb);
-  const int u = wgi * 4 + wave;
+  const int u = wgi * NW + wave;
   const bool active = u < NU;
   const int hl = u % g.G, chunk = u / g.G;
   const int h = grp * g.G + hl;
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(
     const int key0 = J * 128 + (s & 1) * C::KC;
 #pragma unroll
     for (int i = 0; i < C::NK; ++i) {
-      const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR, key = key0 + r;
+      const int c = tid + NT * i, r = c / C::CPR, cc = c % C::CPR, key = key0 + r;
       const int64_t off = ((int64_t)(t0 + key) * g.Hkv + grp) * D + cc * C::EPC;
       Kr[i] = key < L ? *reinterpret_cast<const uint4*>(k + off) : make_uint4(0, 0, 0, 0);
       Vr[i] = key < L ? *reinterpret_cast<const uint4*>(v + off) : make_uint4(0, 0, 0, 0);
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(
     T* Vs = Ks + C::KS;
 #pragma unroll
     for (int i = 0; i < C::NK; ++i) {
-      const int c = tid + 256 * i, r = c / C::CPR, cc = c % C::CPR;
+      const int c = tid + NT * i, r = c / C::CPR, cc = c % C::CPR;
       *reinterpret_cast<uint4*>(Ks + TK::off(r, cc * C::EPC)) = Kr[i];
       *reinterpret_cast<uint4*>(Vs + TK::off(r, cc * C::EPC)) = Vr[i];
     }
@@ -220,18 +222,18 @@ __global__ __launch_bounds__(256) void fwd_kernel(
   // fragments), then of tile 1.  Every operand is read LOOK pairs ahead of
   // its use; tile 0's exponentials run between tile 1's S products and tile
   // 1's between tile 0's P V products; scheduling fences keep that order.
-  constexpr bool FAST = sizeof(T) == 2 && D == 128 && QT == 2;
-  uint32_t oRow[D / 16], oColV[D / 32][2];
+  constexpr bool FAST = sizeof(T) == 2 && D == 128;
+  // This lane's LDS reads in a stage: the K row fragment of 16-column step
+  // ks sits at oRow ^ (ks << 5), and the two transpose reads of the V^T
+  // fragment of 32-column block dt at oColV ^ (dt << 6) and at that ^ 32 plus
+  // 8 rows (the swizzle is an XOR of the chunk index with a function of the
+  // row; rows 8 further down flip its bit 1).
+  uint32_t oRow = 0, oColV = 0;
   if constexpr (FAST) {
     const int s16 = lane & 15, g4 = lane >> 4;
     const int tr_r = hi * 4 + (s16 >> 2), tr_c = 16 * (g4 & 1) + 4 * (s16 & 3);
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) oRow[ks] = TK::off(col, ks * 16 + hi * 8) * (int)sizeof(T);
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      oColV[dt][0] = (C::KS + TK::off(tr_r, dt * 32 + tr_c)) * (int)sizeof(T);
-      oColV[dt][1] = (C::KS + TK::off(tr_r + 8, dt * 32 + tr_c)) * (int)sizeof(T);
-    }
+    oRow = TK::off(col, hi * 8) * (int)sizeof(T);
+    oColV = (C::KS + TK::off(tr_r, tr_c)) * (int)sizeof(T);
   }
   // (the element type comes in as a tag so that the body is type-checked only
   // where it is used, with bf16)
@@ -244,14 +246,17 @@ __global__ __launch_bounds__(256) void fwd_kernel(
     constexpr int LOOK = 4;
     const uint32_t sb = (uint32_t)__builtin_amdgcn_readfirstlane(
         (int)(lds_offset(smem_raw) + buf * C::STAGE * (int)sizeof(T)));
+    const uint32_t bRow = lds_base_add(sb, oRow), bCol = lds_base_add(sb, oColV);
     uint32_t aRow[D / 16], aCol[D / 32][2];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) aRow[ks] = lds_base_add(sb, oRow[ks]);
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      aCol[dt][0] = lds_base_add(sb, oColV[dt][0]);
-      aCol[dt][1] = lds_base_add(sb, oColV[dt][1]);
-    }
+    static_for<D / 16>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int ks = decltype(kc)::value;
+      aRow[ks] = xr<(uint32_t)(ks << 5)>(bRow);
+    });
+    static_for<D / 32>([&](auto dc) __attribute__((always_inline)) {
+      constexpr int dt = decltype(dc)::value;
+      aCol[dt][0] = xr<(uint32_t)(dt << 6)>(bCol);
+      aCol[dt][1] = xr<(uint32_t)(dt << 6) ^ 32u>(bCol) + 8u * D * (uint32_t)sizeof(T);
+    });
     f32x16 S[2][QT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -307,12 +312,12 @@ __global__ __launch_bounds__(256) void fwd_kernel(
       product(mc);
       if constexpr (m + LOOK < NO) operand(std::integral_constant<int, m + LOOK>());
       if constexpr (m >= NA && m < 2 * NA) {
-        constexpr int e0 = (m - NA) * 2 * 16 / NA, e1 = (m - NA + 1) * 2 * 16 / NA;
+        constexpr int e0 = (m - NA) * QT * 16 / NA, e1 = (m - NA + 1) * QT * 16 / NA;
 #pragma unroll
         for (int e = e0; e < e1; ++e) soft(0, e);
         if constexpr (m == 2 * NA - 1) pack(0);
       } else if constexpr (m >= 2 * NA && m < 2 * NA + NB) {
-        constexpr int e0 = (m - 2 * NA) * 2 * 16 / NB, e1 = (m - 2 * NA + 1) * 2 * 16 / NB;
+        constexpr int e0 = (m - 2 * NA) * QT * 16 / NB, e1 = (m - 2 * NA + 1) * QT * 16 / NB;
 #pragma unroll
         for (int e = e0; e < e1; ++e) soft(1, e);
         if constexpr (m == 2 * NA + NB - 1) pack(1);
@@ -336,10 +341,10 @@ __global__ __launch_bounds__(256) void fwd_kernel(
       const uint32_t base = lds0 + (uint32_t)((st % C::NBUF) * C::STAGE * (int)sizeof(T));
 #pragma unroll
       for (int i = 0; i < C::NK; ++i) {
-        const int c = i * 256 + tid, r = c / C::CPR, p = c % C::CPR;
+        const int c = i * NT + tid, r = c / C::CPR, p = c % C::CPR;
         const int key = key0 + r < L ? key0 + r : L - 1;
         const int64_t off = ((int64_t)(t0 + key) * g.Hkv + grp) * D + swz<C::CPR>(r, p) * C::EPC;
-        const uint32_t dst = base + (uint32_t)((i * 256 + wave * 64) * 16);
+        const uint32_t dst = base + (uint32_t)((i * NT + wave * 64) * 16);
         dma16(k + off, dst);
         dma16(v + off, dst + (uint32_t)(C::KS * (int)sizeof(T)));
       }
@@ -661,19 +666,22 @@ static hipError_t fwd_dispatch(const Geo& g, const void* q, const void* k, const
                                const void* qp, const void* kp, const int32_t* q2k_idx,
                                const int32_t* q2k_cnt, void* o, float* lse, float* lse_p,
                                hipStream_t s) {
-  constexpr int QT = 2;
-  typedef FwdCfg<T, D, DP, QT> C;
-  auto fn = fwd_kernel<T, D, DP, QT>;
+  // bf16, d = 128: eight waves of 32 queries (two waves per SIMD, each within
+  // 256 registers); otherwise four waves of 64 queries
+  constexpr bool W8 = sizeof(T) == 2 && D == 128;
+  constexpr int QT = W8 ? 1 : 2, NW = W8 ? 8 : 4;
+  typedef FwdCfg<T, D, DP, QT, NW> C;
+  auto fn = fwd_kernel<T, D, DP, QT, NW>;
   static LdsLimitOnce lds_limit;
   {
     const hipError_t e = lds_limit.ensure({{(const void*)fn, C::LDS_BYTES}});
     if (e != hipSuccess) return e;
   }
   const int NU = g.G * (g.Bq / (32 * QT));
-  const int64_t nblk = (int64_t)g.Hkv * g.nqb * ((NU + 3) / 4);
+  const int64_t nblk = (int64_t)g.Hkv * g.nqb * ((NU + NW - 1) / NW);
   if (nblk == 0) return hipSuccess;
   { ProfScope _ps("fwd", s);
-  hipLaunchKernelGGL(fn, dim3((unsigned)nblk), dim3(256), C::LDS_BYTES, s, (const T*)q, (const T*)k,
+  hipLaunchKernelGGL(fn, dim3((unsigned)nblk), dim3(C::NT), C::LDS_BYTES, s, (const T*)q, (const T*)k,
                      (const T*)v, q2k_idx, q2k_cnt, (T*)o, lse, g); }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -707,9 +715,9 @@ hipError_t launch_fwd(const Geo& g, int is_bf16, const void* q, const void* k, c
 namespace msa {
 int fwd_kernels(KernelEntry* out, int max) {
   const KernelEntry all[] = {
-      {"fwd<bf16,d128,dp64>", (const void*)fwd_kernel<bf16, 128, 64, 2>, 256, FwdCfg<bf16, 128, 64, 2>::LDS_BYTES},
-      {"fwd<bf16,d64,dp32>", (const void*)fwd_kernel<bf16, 64, 32, 2>, 256, FwdCfg<bf16, 64, 32, 2>::LDS_BYTES},
-      {"fwd<f32,d64,dp32>", (const void*)fwd_kernel<float, 64, 32, 2>, 256, FwdCfg<float, 64, 32, 2>::LDS_BYTES},
+      {"fwd<bf16,d128,dp64>", (const void*)fwd_kernel<bf16, 128, 64, 1, 8>, 512, FwdCfg<bf16, 128, 64, 1, 8>::LDS_BYTES},
+      {"fwd<bf16,d64,dp32>", (const void*)fwd_kernel<bf16, 64, 32, 2, 4>, 256, FwdCfg<bf16, 64, 32, 2, 4>::LDS_BYTES},
+      {"fwd<f32,d64,dp32>", (const void*)fwd_kernel<float, 64, 32, 2, 4>, 256, FwdCfg<float, 64, 32, 2, 4>::LDS_BYTES},
       {"proxy_lse<bf16,dp64>", (const void*)proxy_lse_kernel<bf16, 64>, 256, 0},
       {"proxy_lse<bf16,dp32>", (const void*)proxy_lse_kernel<bf16, 32>, 256, 0},
       {"proxy_lse<f32,dp32>", (const void*)proxy_lse_kernel<float, 32>, 256, 0},

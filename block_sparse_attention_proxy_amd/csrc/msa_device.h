@@ -125,6 +125,19 @@ __device__ __forceinline__ uint32_t lds_base_add(uint32_t uniform_base, uint32_t
   asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(uniform_base), "v"(lane_off));
   return r;
 }
+// a ^ C in a vector register, opaque to the compiler so that it is formed
+// where it is used instead of being hoisted out of the stage loop (where it
+// would hold a register for the whole kernel).
+template <uint32_t C>
+__device__ __forceinline__ uint32_t xr(uint32_t a) {
+  if constexpr (C == 0) {
+    return a;
+  } else {
+    uint32_t r;
+    asm volatile("v_xor_b32 %0, %2, %1" : "=v"(r) : "v"(a), "i"(C));
+    return r;
+  }
+}
 typedef __attribute__((address_space(3))) const unsigned char lds_u8;
 template <int OFF>
 __device__ __forceinline__ bf16x8 lds_ld8(uint32_t base) {
