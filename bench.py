@@ -263,7 +263,7 @@ def calibrate_copy(mib):
 
 
 # rocprofv3 kernel names (mangled or demangled) -> the library's kernel names
-_TRACE_KERNELS = (("proxy_scores_kernel", "proxy_scores"), ("select_kernel", "select"),
+_TRACE_KERNELS = (("proxy_scores", "proxy_scores"), ("select_kernel", "select"),
                   ("proxy_lse", "proxy_lse"), ("fwd_kernel", "fwd"), ("dq_kernel", "bwd_dq"),
                   ("dkdv", "bwd_dkdv"))
 
