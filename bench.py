@@ -105,7 +105,8 @@ KERNEL_SOURCES = {
     "select": ["block_sparse_attention_proxy_amd/csrc/select.hip"] + _HDR,
     "fwd": ["block_sparse_attention_proxy_amd/csrc/attn_fwd.hip"] + _HDR,
     "proxy_lse": ["block_sparse_attention_proxy_amd/csrc/attn_fwd.hip"] + _HDR,
-    "bwd_dq": ["block_sparse_attention_proxy_amd/csrc/attn_bwd.hip"] + _HDR,
+    "bwd_dq": ["block_sparse_attention_proxy_amd/csrc/attn_bwd.hip",
+               "block_sparse_attention_proxy_amd/csrc/attn_bwd_q.hip"] + _HDR,
     "bwd_dkdv": ["block_sparse_attention_proxy_amd/csrc/attn_bwd.hip",
                  "block_sparse_attention_proxy_amd/csrc/attn_bwd_kv.hip"] + _HDR,
 }
@@ -265,7 +266,7 @@ def calibrate_copy(mib):
 # rocprofv3 kernel names (mangled or demangled) -> the library's kernel names
 _TRACE_KERNELS = (("proxy_scores", "proxy_scores"), ("select_kernel", "select"),
                   ("proxy_lse", "proxy_lse"), ("fwd_kernel", "fwd"), ("dq_kernel", "bwd_dq"),
-                  ("dkdv", "bwd_dkdv"))
+                  ("dq128_kernel", "bwd_dq"), ("dkdv", "bwd_dkdv"))
 
 
 def _counter_per_dispatch(csv_dir, counter):

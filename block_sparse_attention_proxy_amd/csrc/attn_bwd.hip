@@ -15,6 +15,8 @@
 //                  the proxy term sum_u (Q - P/G) kp per head
 //   dqp_reduce     sums the per-head proxy terms when a group spans
 //                  several workgroups (G > 4)
+// For bf16, d = 128, dp = 64 the query-major pass is dq128_kernel
+// (attn_bwd_q.hip) and the KV-major pass dkdv_ws_kernel (attn_bwd_kv.hip).
 //   dkdv_kernel    KV-major over the inverted lists: dK, dV and dkp, each
 //                  KV block owned by one workgroup, so no atomics
 #include "msa_device.h"
@@ -851,7 +853,13 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
   hipError_t e;
   const int NU = g.G * (g.Bq / 32);
   const int64_t nq = (int64_t)g.Hkv * g.nqb * ((NU + 3) / 4);
-  if (nq > 0) {
+  const bool q8 = std::is_same<T, bf16>::value && D == 128 && DP == 64 && dq128_supported(g);
+  if (q8) {
+    { ProfScope _ps("bwd_dq", s);
+    e = launch_dq128(g, q, k, v, qp, kp, o, lse, lse_p, dout, w.delta, w.lse2, w.lsep2, q2k_idx,
+                     q2k_cnt, dq, dqp, s); }
+    if (e != hipSuccess) return e;
+  } else if (nq > 0) {
     { ProfScope _ps("bwd_dq", s);
     hipLaunchKernelGGL((dq_kernel<T, D, DP>), dim3((unsigned)nq), dim3(256), CQ::LDS_BYTES, s,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)qp, (const T*)kp, (const T*)o,
@@ -859,7 +867,7 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
                        w.cpart, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (g.G > 4 && g.T > 0) {
+  if (!q8 && g.G > 4 && g.T > 0) {
     { ProfScope _ps("bwd_dqp_reduce", s);
     hipLaunchKernelGGL((dqp_reduce_kernel<DP>), dim3(grid_for_b((int64_t)g.T * g.Hkv * DP, 256)),
                        dim3(256), 0, s, w.cpart, dqp, g); }

@@ -86,22 +86,6 @@ __device__ __forceinline__ f32x4 lds_f4(uint32_t base) {
   return *reinterpret_cast<lds_f32x4*>(reinterpret_cast<lds_u8*>((uintptr_t)base) + OFF);
 }
 
-// v if (x + C) < w as unsigned integers, else 0.  The causal / document mask
-// of an accumulator element with constant row offset C: x = (row of element
-// 0) - lo and w = hi - lo, so the test is lo <= row < hi.  One asm block per
-// element keeps the compiler from hoisting sixteen compare masks into scalar
-// registers ahead of the interleaved softmax.
-template <uint32_t C>
-__device__ __forceinline__ float keep_if(float v, uint32_t x, uint32_t w) {
-  float r;
-  uint32_t t;
-  asm volatile("v_add_u32 %1, %3, %4\n\tv_cmp_lt_u32 vcc, %1, %5\n\tv_cndmask_b32 %0, 0, %2, vcc"
-               : "=v"(r), "=&v"(t)
-               : "v"(v), "i"(C), "v"(x), "v"(w)
-               : "vcc");
-  return r;
-}
-
 // Two transpose reads joined into one fragment: the first at a + OFF, the
 // second (8 rows further down) at b + OFF + OFF2.
 template <int OFF, int OFF2>

@@ -509,6 +509,7 @@ static std::vector<msa::KernelEntry> all_kernels() {
   n += msa::fwd_kernels(v.data() + n, 64 - n);
   n += msa::bwd_kernels(v.data() + n, 64 - n);
   n += msa::bwd_kv_kernels(v.data() + n, 64 - n);
+  n += msa::bwd_q_kernels(v.data() + n, 64 - n);
   n += msa::share_kernels(v.data() + n, 64 - n);
   v.resize(n);
   return v;

@@ -138,6 +138,21 @@ __device__ __forceinline__ uint32_t xr(uint32_t a) {
     return r;
   }
 }
+// v if (x + C) < w as unsigned integers, else 0.  The causal / document mask
+// of an accumulator element with constant row offset C: x = (row of element
+// 0) - lo and w = hi - lo, so the test is lo <= row < hi.  One asm block per
+// element keeps the compiler from hoisting sixteen compare masks into scalar
+// registers ahead of the interleaved softmax.
+template <uint32_t C>
+__device__ __forceinline__ float keep_if(float v, uint32_t x, uint32_t w) {
+  float r;
+  uint32_t t;
+  asm volatile("v_add_u32 %1, %3, %4\n\tv_cmp_lt_u32 vcc, %1, %5\n\tv_cndmask_b32 %0, 0, %2, vcc"
+               : "=v"(r), "=&v"(t)
+               : "v"(v), "i"(C), "v"(x), "v"(w)
+               : "vcc");
+  return r;
+}
 typedef __attribute__((address_space(3))) const unsigned char lds_u8;
 template <int OFF>
 __device__ __forceinline__ bf16x8 lds_ld8(uint32_t base) {

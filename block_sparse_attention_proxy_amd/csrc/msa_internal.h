@@ -94,6 +94,16 @@ hipError_t launch_dkdv128(const Geo& g, const void* q, const void* k, const void
                           const void* dout, const float* delta, const int32_t* k2q_ptr,
                           const int32_t* k2q_idx, float* dk, float* dv, float* dkp, hipStream_t s);
 
+// Query-major backward for bf16, d = 128, dp = 64 and 1, 2, 4 or 8 heads per
+// group (eight waves of 32 queries, two per SIMD); other shapes use the
+// generic kernel.  Writes D and both LSEs in log2 units for the KV-major pass.
+bool dq128_supported(const Geo& g);
+hipError_t launch_dq128(const Geo& g, const void* q, const void* k, const void* v, const void* qp,
+                        const void* kp, const void* o, const float* lse, const float* lse_p,
+                        const void* dout, float* delta, float* lse2, float* lsep2,
+                        const int32_t* q2k_idx, const int32_t* q2k_cnt, float* dq, float* dqp,
+                        hipStream_t s);
+
 // Kernel registry for the resource report: each translation unit lists the
 // kernels it instantiates, with the block size and dynamic LDS of its launch.
 struct KernelEntry {
@@ -107,5 +117,6 @@ int share_kernels(KernelEntry* out, int max);
 int fwd_kernels(KernelEntry* out, int max);
 int bwd_kernels(KernelEntry* out, int max);
 int bwd_kv_kernels(KernelEntry* out, int max);
+int bwd_q_kernels(KernelEntry* out, int max);
 
 }  // namespace msa
