@@ -28,6 +28,11 @@ SMALL = {
     # one proxy head shared by every KV group
     "l32k-geom-shared": (WORKLOADS["layer-32k"], dict(topk=4, proxy_heads=1), (2500, 1277)),
     "l128k-geom-gqa8-shared": (WORKLOADS["layer-128k-gqa8"], dict(topk=3, proxy_heads=1), (1700, 300)),
+    # one and two query heads per KV group: the eight-wave forward and
+    # query-major kernels with several query chunks per workgroup, and the
+    # generic KV-major kernel
+    "l32k-geom-g1": (WORKLOADS["layer-32k"], dict(topk=4, heads_q=8), (2500, 1277)),
+    "l512k-geom-g2": (WORKLOADS["layer-512k-window2"], dict(topk=3, heads_q=16), (1900, 300, 77)),
 }
 
 
