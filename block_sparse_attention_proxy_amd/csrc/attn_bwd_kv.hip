@@ -30,7 +30,6 @@
 namespace msa {
 namespace {
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KD = 128, KDP = 64, KQC = 32;
 constexpr int TILE_B = KQC * KD * 2;                // one Q or dO tile of a stage: 8 KiB
@@ -42,42 +41,6 @@ __device__ __forceinline__ int xcd_remap_kv(int i, int n) {
   const int per = n / 8, rem = n % 8;
   const int x = i % 8, k = i / 8;
   return x * per + (x < rem ? x : rem) + k;
-}
-
-// Buffer descriptor of a raw byte range (gfx9 layout: base, stride 0,
-// num_records in bytes, 32-bit data format).  Every field is wave-uniform.
-__device__ __forceinline__ i32x4 make_srd(const void* base, uint32_t nbytes) {
-  const uint64_t a = (uint64_t)base;
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane((int)nbytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// Buffer -> LDS copies (lane l's bytes land at LDS byte address lds + l * size;
-// lds must be wave-uniform).  Issued from inline assembly for the same reason
-// as the global -> LDS copies elsewhere: hidden from the compiler, a barrier
-// does not wait for them; the kernel waits with explicit vmcnt counts.  M0 is
-// saved and restored around the copy.
-__device__ __forceinline__ void bdma16(const i32x4& srd, uint32_t voff, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_nop 0\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(srd), "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds))
-      : "memory");
-}
-__device__ __forceinline__ void bdma4(const i32x4& srd, uint32_t voff, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-      "buffer_load_dword %1, %2, 0 offen lds\n\ts_nop 0\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(srd), "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds))
-      : "memory");
 }
 
 template <int OFF>

@@ -104,31 +104,59 @@ __global__ __launch_bounds__(Q_NT) void dq128_kernel(
   if (diag * 128 + 64 > I * g.Bq + g.Bq - 1) nst -= 1;
   const int nst_plain = 2 * (cnt - 1);
 
-  // Copy stage s (clamped to the last) into ring slot s % Q_NBUF.  Key rows
-  // past the document end are clamped to its last row; they only occur in the
-  // diagonal block, where the causal mask removes them.
+  // Copy stage s (clamped to the last) into ring slot s % Q_NBUF through
+  // buffer descriptors over the stage's rows: each lane's byte offset is
+  // fixed.  A stage that runs past the document end (only in the diagonal
+  // block, where the causal mask removes those rows) has its rows past the
+  // end clamped to the last one: a copy past a descriptor's bound would leave
+  // its LDS row unwritten, holding whatever the slot held before.
   const uint32_t lds0 = lds_offset(smem_raw);
+  const uint32_t rsK = (uint32_t)g.Hkv * QD * 2, rsP = (uint32_t)g.Hkv * QDP * 2;
+  uint32_t voK[Q_KCOPY], voP[Q_PCOPY];
+  int rK[Q_KCOPY], rP[Q_PCOPY];
+#pragma unroll
+  for (int j = 0; j < Q_KCOPY; ++j) {
+    const int r = (wave * Q_KCOPY + j) * 4 + (lane >> 4), p = lane & 15;
+    rK[j] = r;
+    voK[j] = (uint32_t)r * rsK + (uint32_t)swz<16>(r, p) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < Q_PCOPY; ++j) {
+    const int r = (wave * Q_PCOPY + j) * 8 + (lane >> 3), p = lane & 7;
+    rP[j] = r;
+    voP[j] = (uint32_t)r * rsP + (uint32_t)swz<8>(r, p) * 16;
+  }
   auto issue = [&](int s) __attribute__((always_inline)) {
     const int ss = s < nst ? s : nst - 1;
     const uint32_t base = lds0 + (uint32_t)((s % Q_NBUF) * Q_STAGE);
     const int key0 = (sel[ss >> 1] - kb0) * 128 + (ss & 1) * QKC;
+    const int64_t row0 = (int64_t)(t0 + key0) * g.Hkv + grp;
+    const int last = L - 1 - key0;                  // last row of the document in the stage
+    const i32x4 sK = make_srd(k + row0 * QD, QKC * rsK);
+    const i32x4 sV = make_srd(v + row0 * QD, QKC * rsK);
+    const i32x4 sP = make_srd(kp + row0 * QDP, QKC * rsP);
+    uint32_t oK[Q_KCOPY], oP[Q_PCOPY];
+#pragma unroll
+    for (int j = 0; j < Q_KCOPY; ++j) oK[j] = voK[j];
+#pragma unroll
+    for (int j = 0; j < Q_PCOPY; ++j) oP[j] = voP[j];
+    if (last < QKC - 1) {
+#pragma unroll
+      for (int j = 0; j < Q_KCOPY; ++j)
+        if (rK[j] > last) oK[j] -= (uint32_t)(rK[j] - last) * rsK;
+#pragma unroll
+      for (int j = 0; j < Q_PCOPY; ++j)
+        if (rP[j] > last) oP[j] -= (uint32_t)(rP[j] - last) * rsP;
+    }
 #pragma unroll
     for (int j = 0; j < Q_KCOPY; ++j) {
-      const int rfirst = (wave * Q_KCOPY + j) * 4;
-      const int r = rfirst + (lane >> 4), p = lane & 15;
-      const int key = key0 + r < L ? key0 + r : L - 1;
-      const int64_t off = ((int64_t)(t0 + key) * g.Hkv + grp) * QD + swz<16>(r, p) * 8;
-      dma16(k + off, base + (uint32_t)(rfirst * QD * 2));
-      dma16(v + off, base + (uint32_t)(Q_KS + rfirst * QD * 2));
+      const uint32_t dst = base + (uint32_t)((wave * Q_KCOPY + j) * 4 * QD * 2);
+      bdma16(sK, oK[j], dst);
+      bdma16(sV, oK[j], dst + Q_KS);
     }
 #pragma unroll
-    for (int j = 0; j < Q_PCOPY; ++j) {
-      const int rfirst = (wave * Q_PCOPY + j) * 8;
-      const int r = rfirst + (lane >> 3), p = lane & 7;
-      const int key = key0 + r < L ? key0 + r : L - 1;
-      const int64_t off = ((int64_t)(t0 + key) * g.Hkv + grp) * QDP + swz<8>(r, p) * 8;
-      dma16(kp + off, base + (uint32_t)(2 * Q_KS + rfirst * QDP * 2));
-    }
+    for (int j = 0; j < Q_PCOPY; ++j)
+      bdma16(sP, oP[j], base + (uint32_t)(2 * Q_KS + (wave * Q_PCOPY + j) * 8 * QDP * 2));
   };
 
   bf16x8 Qf[QD / 16], dOf[QD / 16], QPf[QDP / 16];
