@@ -335,18 +335,40 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(
   // the causal mask drops them.  The reference maxima come from stage 0.
   auto pass_ring = [&](auto tag) __attribute__((always_inline)) {   // built only where called
     const uint32_t lds0 = lds_offset(smem_raw);
+    // copies through buffer descriptors over the stage's rows: each lane's
+    // byte offset is fixed; a stage running past the document end has its rows
+    // past the end clamped to the last one (a copy past a descriptor's bound
+    // would leave its LDS row unwritten)
+    const uint32_t rs = (uint32_t)g.Hkv * D * (uint32_t)sizeof(T);
+    uint32_t vo[C::NK];
+    int rr[C::NK];
+#pragma unroll
+    for (int i = 0; i < C::NK; ++i) {
+      const int c = i * NT + tid, r = c / C::CPR, p = c % C::CPR;
+      rr[i] = r;
+      vo[i] = (uint32_t)r * rs + (uint32_t)(swz<C::CPR>(r, p) * 16);
+    }
     auto issue = [&](int st) __attribute__((always_inline)) {
       const int sc = st < nst ? st : nst - 1;
       const int key0 = (sel[sc >> 1] - kb0) * 128 + (sc & 1) * C::KC;
       const uint32_t base = lds0 + (uint32_t)((st % C::NBUF) * C::STAGE * (int)sizeof(T));
+      const int64_t row0 = (int64_t)(t0 + key0) * g.Hkv + grp;
+      const int last = L - 1 - key0;
+      const i32x4 sk = make_srd(k + row0 * D, (uint32_t)C::KC * rs);
+      const i32x4 sv = make_srd(v + row0 * D, (uint32_t)C::KC * rs);
+      uint32_t o[C::NK];
+#pragma unroll
+      for (int i = 0; i < C::NK; ++i) o[i] = vo[i];
+      if (last < C::KC - 1) {
+#pragma unroll
+        for (int i = 0; i < C::NK; ++i)
+          if (rr[i] > last) o[i] -= (uint32_t)(rr[i] - last) * rs;
+      }
 #pragma unroll
       for (int i = 0; i < C::NK; ++i) {
-        const int c = i * NT + tid, r = c / C::CPR, p = c % C::CPR;
-        const int key = key0 + r < L ? key0 + r : L - 1;
-        const int64_t off = ((int64_t)(t0 + key) * g.Hkv + grp) * D + swz<C::CPR>(r, p) * C::EPC;
         const uint32_t dst = base + (uint32_t)((i * NT + wave * 64) * 16);
-        dma16(k + off, dst);
-        dma16(v + off, dst + (uint32_t)(C::KS * (int)sizeof(T)));
+        bdma16(sk, o[i], dst);
+        bdma16(sv, o[i], dst + (uint32_t)(C::KS * (int)sizeof(T)));
       }
     };
     wait_vmcnt<0>();                               // the Q fragments: the waits below count copies only
