@@ -319,11 +319,13 @@ __global__ __launch_bounds__(256, 2) void proxy_scores_lds_kernel(const bf16* __
   const uint32_t ring = lds_offset(smem_raw) + (uint32_t)wave * SC_NS * SC_SLICE;
   // copy side: lane l moves row 8 j + (l >> 3), 16-byte chunk l & 7 of a slice
   // (source chunk swizzled so that the slot holds the Tile layout)
-  // (the swizzle of rows 8 j + r depends on j only through j & 1)
+  // through a buffer descriptor over the slice's 32 rows, with fixed per-lane
+  // byte offsets (candidate blocks lie wholly inside the document)
   const int crow = lane >> 3;
-  const int64_t csrc0 = (int64_t)crow * Hp * DP + swz<8>(crow, lane & 7) * 8;
-  const int64_t csrc1 = (int64_t)(8 + crow) * Hp * DP + swz<8>(8 + crow, lane & 7) * 8;
-  const int64_t crow16 = (int64_t)16 * Hp * DP;
+  const uint32_t rsp = (uint32_t)Hp * DP * 2;
+  uint32_t coff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) coff[j] = (uint32_t)(8 * j + crow) * rsp + (uint32_t)swz<8>(8 * j + crow, lane & 7) * 16;
   // read side: fragment ks of this lane's key row in a slot
   const uint32_t rd0 = (uint32_t)TP::off(col, hi8) * 2;
 
@@ -357,9 +359,9 @@ __global__ __launch_bounds__(256, 2) void proxy_scores_lds_kernel(const bf16* __
     uint32_t i_slot = 0, c_slot = 0;              // byte offsets of the next copy's / read's slot
     auto copy_next = [&]() __attribute__((always_inline)) {
       const int q = i_q < nsl ? i_q : nsl - 1;    // past the end: the last slice again
-      const bf16* src = kbase + (int64_t)q * 32 * Hp * DP;
+      const i32x4 sd = make_srd(kbase + (int64_t)q * 32 * Hp * DP, 32u * rsp);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(src + (j & 1 ? csrc1 : csrc0) + (j >> 1) * crow16, ring + i_slot + j * 1024);
+      for (int j = 0; j < 4; ++j) bdma16(sd, coff[j], ring + i_slot + j * 1024);
       ++i_q;
       i_slot = i_slot == (SC_NS - 1) * SC_SLICE ? 0u : i_slot + SC_SLICE;
     };
