@@ -625,20 +625,41 @@ __global__ __launch_bounds__(256, 3) void proxy_lse128_kernel(const T* __restric
   // the register loads complete before the copies, so the waits count copies only
   wait_vmcnt<0>();
   const uint32_t lds0 = lds_offset(smem_raw);
+  // kp rows of a block through a buffer descriptor with fixed per-lane byte
+  // offsets; rows past the document end (diagonal block only, masked below)
+  // clamped to its last row, since a copy past the bound leaves its LDS row
+  // unwritten
+  const uint32_t rs = (uint32_t)g.Hkv * DP * (uint32_t)sizeof(T);
+  uint32_t vo[C::COPIES];
+  int rr[C::COPIES];
+#pragma unroll
+  for (int j = 0; j < C::COPIES; ++j) {
+    const int r = (wave * C::COPIES + j) * C::ROWS_PER_COPY + lane / TP::CPR, p = lane % TP::CPR;
+    rr[j] = r;
+    vo[j] = (uint32_t)r * rs + (uint32_t)(swz<TP::CPR>(r, p) * 16);
+  }
   auto issue = [&](int si) __attribute__((always_inline)) {
     const int J = sel[si < cnt ? si : cnt - 1] - kb0;    // past the end: the last block again
     const uint32_t base = lds0 + (uint32_t)((si % C::NBUF) * C::SLOT);
+    const i32x4 sd = make_srd(kp + ((int64_t)(t0 + J * 128) * g.Hkv + grp) * DP, 128u * rs);
+    const int last = L - 1 - J * 128;
+    uint32_t o[C::COPIES];
 #pragma unroll
-    for (int j = 0; j < C::COPIES; ++j) {
-      const int rfirst = (wave * C::COPIES + j) * C::ROWS_PER_COPY;
-      const int r = rfirst + lane / TP::CPR, p = lane % TP::CPR;
-      const int key = J * 128 + r < L ? J * 128 + r : L - 1;
-      dma16(kp + ((int64_t)(t0 + key) * g.Hkv + grp) * DP + swz<TP::CPR>(r, p) * TP::EPC,
-            base + (uint32_t)(rfirst * DP * (int)sizeof(T)));
+    for (int j = 0; j < C::COPIES; ++j) o[j] = vo[j];
+    if (last < 127) {
+#pragma unroll
+      for (int j = 0; j < C::COPIES; ++j)
+        if (rr[j] > last) o[j] -= (uint32_t)(rr[j] - last) * rs;
     }
+#pragma unroll
+    for (int j = 0; j < C::COPIES; ++j)
+      bdma16(sd, o[j], base + (uint32_t)((wave * C::COPIES + j) * C::ROWS_PER_COPY * DP * (int)sizeof(T)));
   };
 #pragma unroll
   for (int j = 0; j < C::AHEAD; ++j) issue(j);
+  // running maximum and sum in base 2; the maximum is taken on the raw scores
+  // (the scale is positive) and the scale folded into the exponent's fma
+  const float psl2 = g.pscale_log2;
   float mp = NEG_BIG, lp = 0.f;
   for (int si = 0; si < cnt; ++si) {
     wait_vmcnt<(C::AHEAD - 1) * C::COPIES>();   // this block's copies have landed
@@ -658,22 +679,22 @@ __global__ __launch_bounds__(256, 3) void proxy_lse128_kernel(const T* __restric
       Y[kt] = zero16();
 #pragma unroll
       for (int ks = 0; ks < DP / 16; ++ks) mma(Y[kt], TP::row8(KPs, kt * 32 + col, ks * 16 + hi * 8), QPf[ks]);
+      if (need_mask) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = Y[kt][i] * g.pscale_log2;
-        if (need_mask && J * 128 + kt * 32 + acc_row(i, lane) > qpos) x = -INFINITY;
-        Y[kt][i] = x;
-        mx = fmaxf(mx, x);
+        for (int i = 0; i < 16; ++i)
+          if (J * 128 + kt * 32 + acc_row(i, lane) > qpos) Y[kt][i] = -INFINITY;
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, Y[kt][i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * psl2;
     const float mnew = fmaxf(mp, mx);
     float ls = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       if (kt >= ntile) break;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ls += __builtin_amdgcn_exp2f(Y[kt][i] - mnew);
+      for (int i = 0; i < 16; ++i) ls += __builtin_amdgcn_exp2f(fmaf(Y[kt][i], psl2, -mnew));
     }
     lp = lp * __builtin_amdgcn_exp2f(mp - mnew) + ls;
     mp = mnew;
