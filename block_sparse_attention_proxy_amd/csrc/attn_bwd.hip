@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
     lsep2 = lse_p[(int64_t)grp * g.T + tq] * LOG2E;
     // per-query values the KV-major pass reads: D and both LSEs in log2 units
     if (hi == 0 && qpos < L) {
-      delta[(int64_t)h * g.T + tq] = dl;
+      delta[(int64_t)h * g.T + tq] = -dl;             // stored negated: -rowsum(dO * O)
       lse2_out[(int64_t)h * g.T + tq] = lse2;
       if (hl == 0) lsep2_out[(int64_t)grp * g.T + tq] = lsep2;
     }
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
         const int i = kk * 8 + j;
         float p = __builtin_amdgcn_exp2f(fmaf(S[i], g.scale_log2, -lr[kk][j]));
         if (masked) p = (acc_row(i, lane) >= lo && acc_row(i, lane) < hi_) ? p : 0.f;
-        dP[i] = p * (dP[i] - dl[kk][j]);
+        dP[i] = p * (dP[i] + dl[kk][j]);              // dl holds -D
         S[i] = p;
         Tacc[i] += p;
       }

@@ -181,10 +181,18 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
     auto next_slot = [](uint32_t o, uint32_t step) __attribute__((always_inline)) {
       return o == (WS_NB - 1) * step ? 0u : o + step;
     };
-    auto products = [&](uint32_t so, auto par_c, auto&& between) __attribute__((always_inline)) {
+    // dP starts from -D (the delta vectors hold -rowsum(dO O)), so that the
+    // products give dP - D directly.
+    auto products = [&](uint32_t so, uint32_t fo, auto par_c, auto&& between) __attribute__((always_inline)) {
       constexpr int PAR = decltype(par_c)::value;
       constexpr int LOOK = 4;
       const uint32_t rb = bR + so;
+      const uint32_t fd = oF + fo;
+      const f32x4 n0 = lds_f4<FL_VEC>(fd), n1 = lds_f4<FL_VEC + 32>(fd);
+      const f32x4 n2 = lds_f4<FL_VEC + 64>(fd), n3 = lds_f4<FL_VEC + 96>(fd);
+      f32x16 nD;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { nD[j] = n0[j]; nD[4 + j] = n1[j]; nD[8 + j] = n2[j]; nD[12 + j] = n3[j]; }
       bf16x8 op[16];
       uint32_t ad = 0;
       auto rd = [&](auto mc) __attribute__((always_inline)) {
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
       static_for<LOOK>([&](auto mc) __attribute__((always_inline)) { rd(mc); });
       static_for<16>([&](auto mc) __attribute__((always_inline)) {
         constexpr int m = decltype(mc)::value, ks = m / 2;
-        if constexpr (m & 1) dP[PAR] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], Vf[ks], m == 1 ? zero16() : dP[PAR], 0, 0, 0);
+        if constexpr (m & 1) dP[PAR] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], Vf[ks], m == 1 ? nD : dP[PAR], 0, 0, 0);
         else S[PAR] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], Kf[ks], m == 0 ? zero16() : S[PAR], 0, 0, 0);
         if constexpr (m + LOOK < 16) rd(std::integral_constant<int, m + LOOK>());
         between(mc);
@@ -206,7 +214,7 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
     // prologue: stage 0 has landed at the second barrier; its products.
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    products(0u, std::integral_constant<int, 0>(), [&](auto) __attribute__((always_inline)) {});
+    products(0u, 0u, std::integral_constant<int, 0>(), [&](auto) __attribute__((always_inline)) {});
 
     // Iteration s: the products of stage s + 1 with the softmax of stage s
     // between them (P, dS to the exchange buffer), then at a chunk's last head
@@ -222,21 +230,18 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
       const uint32_t xb = xb_lane + (uint32_t)(s & 1) * 4 * WS_XB_KG;
       auto run = [&](auto masked_c) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_c)::value;
-        f32x4 lv[4], dl[4];
+        f32x4 lv[4];
         bf16x8 ap[2], as[2];
         lv[0] = lds_f4<0>(fb);
-        dl[0] = lds_f4<FL_VEC>(fb);
-        products(next_slot(c_so, WS_SLOT), std::integral_constant<int, PAR ^ 1>(), [&](auto mc) __attribute__((always_inline)) {
+        products(next_slot(c_so, WS_SLOT), next_slot(c_fo, FL_SLOT), std::integral_constant<int, PAR ^ 1>(),
+                 [&](auto mc) __attribute__((always_inline)) {
           constexpr int i = decltype(mc)::value;
-          if constexpr ((i & 3) == 1 && i < 13) {
-            lv[(i + 3) / 4] = lds_f4<((i + 3) / 4) * 32>(fb);
-            dl[(i + 3) / 4] = lds_f4<FL_VEC + ((i + 3) / 4) * 32>(fb);
-          }
+          if constexpr ((i & 3) == 1 && i < 13) lv[(i + 3) / 4] = lds_f4<((i + 3) / 4) * 32>(fb);
           float pv = __builtin_amdgcn_exp2f(fmaf(S[PAR][i], sl2, -lv[i >> 2][i & 3]));
           if constexpr (MASKED) pv = keep_if<(uint32_t)(((i >> 2) << 3) + (i & 3))>(pv, mx, mw);
           Tacc[i] += pv;
           ap[i >> 3][i & 7] = (bf16)pv;
-          as[i >> 3][i & 7] = (bf16)(pv * (dP[PAR][i] - dl[i >> 2][i & 3]));
+          as[i >> 3][i & 7] = (bf16)(pv * dP[PAR][i]);
           if constexpr ((i & 7) == 7) {
             lds_st16(xb + (i >> 3) * 1024, ap[i >> 3]);
             lds_st16(xb + (2 + (i >> 3)) * 1024, as[i >> 3]);

@@ -180,9 +180,9 @@ __global__ __launch_bounds__(Q_NT) void dq128_kernel(
     for (int ks = 0; ks < QDP / 16; ++ks) QPf[ks] = ld8(sp + ks * 16);
     lse2 = lse[(int64_t)h * g.T + tq] * LOG2E;
     lsep2 = lse_p[(int64_t)grp * g.T + tq] * LOG2E;
-    // per-query values the KV-major pass reads: D and both LSEs in log2 units
+    // per-query values the KV-major pass reads: -D and both LSEs in log2 units
     if (hi == 0 && qpos < L) {
-      delta[(int64_t)h * g.T + tq] = dl;
+      delta[(int64_t)h * g.T + tq] = -dl;             // stored negated: -rowsum(dO * O)
       lse2_out[(int64_t)h * g.T + tq] = lse2;
       if (hl == 0) lsep2_out[(int64_t)grp * g.T + tq] = lsep2;
     }
