@@ -259,19 +259,25 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
           constexpr int ks = decltype(ksc)::value;
           Y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld8<0>(xr<(uint32_t)(ks << 5)>(pb)), KPf[ks], Y, 0, 0, 0);
         });
-        static_for<2>([&](auto hc) __attribute__((always_inline)) {
-          constexpr int h8 = decltype(hc)::value;
-          const f32x4 l0 = lds_f4<2 * FL_VEC + (2 * h8) * 32>(fb), l1 = lds_f4<2 * FL_VEC + (2 * h8 + 1) * 32>(fb);
-          bf16x8 ay;
-          static_for<8>([&](auto ec) __attribute__((always_inline)) {
-            constexpr int e = decltype(ec)::value, i = h8 * 8 + e;
-            const float lpv = e < 4 ? l0[e & 3] : l1[e & 3];
-            float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], psl2, -lpv));
-            qv = keep_if<(uint32_t)(((i >> 2) << 3) + (i & 3))>(qv, mx, mw);
-            ay[e] = (bf16)fmaf(-invG, Tacc[i], qv);
+        // (the causal / document mask only where the chunk's stages are masked)
+        auto proxy_dy = [&](auto masked_c) __attribute__((always_inline)) {
+          constexpr bool MASKED = decltype(masked_c)::value;
+          static_for<2>([&](auto hc) __attribute__((always_inline)) {
+            constexpr int h8 = decltype(hc)::value;
+            const f32x4 l0 = lds_f4<2 * FL_VEC + (2 * h8) * 32>(fb), l1 = lds_f4<2 * FL_VEC + (2 * h8 + 1) * 32>(fb);
+            bf16x8 ay;
+            static_for<8>([&](auto ec) __attribute__((always_inline)) {
+              constexpr int e = decltype(ec)::value, i = h8 * 8 + e;
+              const float lpv = e < 4 ? l0[e & 3] : l1[e & 3];
+              float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], psl2, -lpv));
+              if constexpr (MASKED) qv = keep_if<(uint32_t)(((i >> 2) << 3) + (i & 3))>(qv, mx, mw);
+              ay[e] = (bf16)fmaf(-invG, Tacc[i], qv);
+            });
+            lds_st16(dy_lane + h8 * 1024, ay);
           });
-          lds_st16(dy_lane + h8 * 1024, ay);
-        });
+        };
+        if (masked) proxy_dy(std::true_type());
+        else proxy_dy(std::false_type());
         Tacc = zero16();
         c_hl = 0;
         c_qo ^= QP_TILE;
