@@ -10,10 +10,13 @@ Default workload: ``varlen-1m-packed`` (1,048,576 tokens packed from seeded
 log-uniform document lengths, 32 query / 8 KV heads, d 128, dp 64, query
 block 128, top-k 64), bf16 inputs with fp32 accumulation.
 
-Prints one JSON line.  ``value`` is the step's TFLOP/s: the proxy-scoring
-FLOPs plus the forward and backward FLOPs over the selected (query, key)
-pairs (FlashAttention convention: 4 d per pair forward, 10 d backward; proxy
-2 dp forward, 6 dp backward), divided by the measured step time.
+Prints one JSON line.  ``value`` is the attention rate over the selected
+(query, key) pairs: the counted forward and backward FLOPs (FlashAttention
+convention: 4 d per pair and head forward, 10 d backward; proxy 2 dp forward,
+6 dp backward, per pair and proxy head) divided by the forward and backward
+kernel time (``attn_fwd_bwd_ms``).  ``ms_per_step`` is the whole step
+(scoring, selection, forward, backward) between two events, and
+``step_tflops`` adds the quadratic scoring FLOPs over that whole step.
 """
 from __future__ import annotations
 
@@ -134,11 +137,21 @@ def cpu_baseline(w, seqlens, x, budget_s, seed):
     import numpy as np
     import torch
     from oracle import msa_oracle as om
+    # the host cores this process may run on; BLAS gets that many threads,
+    # unless the environment caps the thread count lower
+    affinity = len(os.sched_getaffinity(0))
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    want = min(affinity, cap) if cap > 0 else affinity
+    vendor, threads, limiter = "unknown", want, None
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=want, user_api="blas")
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if blas:
+            vendor = ",".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in blas}))
+            threads = max(p.get("num_threads", want) for p in blas)
     except Exception:
-        threads = os.cpu_count() or 1
+        pass
     ocfg = om.Config(w.heads_q, w.heads_kv, w.head_dim, w.proxy_dim, w.q_block, w.topk, w.local_window)
     b = max(range(len(seqlens)), key=lambda i: seqlens[i])
     s0 = int(sum(seqlens[:b]))
@@ -172,7 +185,10 @@ def cpu_baseline(w, seqlens, x, budget_s, seed):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "affinity_cores": affinity, "blas": vendor,
             "sample": f"{done} query blocks (group 0, all {G} heads) of the longest document "
                       f"({L} tokens): scoring, selection, forward and backward in fp64 numpy, "
                       f"{dt:.1f} s wall", "seconds": dt}
@@ -426,10 +442,14 @@ def main(argv=None):
         total_flops = f["scoring"] + f["fwd_counted"]
     else:
         total_flops = f["scoring"] + f["fwd_counted"] + f["bwd_counted"]
-    value = total_flops / (step_ms * 1e-3) / 1e12
+    step_tflops = total_flops / (step_ms * 1e-3) / 1e12
     attn_ms = stages.get("fwd", 0.0) + stages.get("bwd", 0.0)
     attn_flops = f["fwd_counted"] + (f["bwd_counted"] if a.mode == "train" else 0)
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12 if attn_ms else None
+    # the headline: counted (forward + backward) FLOPs over the selected pairs
+    # per forward + backward time; prefill keeps its own metric (scoring and
+    # forward over the forward pass)
+    value = attn_tflops if a.mode == "train" else step_tflops
     bwd_ms = stages.get("bwd", 0.0)
     bwd_rates = None
     if bwd_ms:
@@ -487,6 +507,8 @@ def main(argv=None):
         "roofline": roofline,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
         "stages_ms": {k: round(v, 3) for k, v in sorted(stages.items())},
+        "step_tflops": round(step_tflops, 2),
+        "attn_fwd_bwd_ms": round(attn_ms, 3),
         "attn_fwd_bwd_tflops": None if attn_tflops is None else round(attn_tflops, 2),
         "attn_mfma_frac": None if attn_tflops is None else round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "selection_roofline": selection,

@@ -28,13 +28,16 @@ class _MSAFunction(torch.autograd.Function):
         # reuses them only for work ordered after this point on the stream)
         buf.release_transients()
         ctx.cfg, ctx.vl, ctx.buf = cfg, vl, buf
-        ctx.save_for_backward(q, k, v, qp, kp)
+        # O is saved like the inputs, so that an in-place change of the
+        # returned output is caught by autograd's version check
+        ctx.save_for_backward(q, k, v, qp, kp, buf.o)
         return buf.o
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v, qp, kp = ctx.saved_tensors
+        q, k, v, qp, kp, o = ctx.saved_tensors
         buf = ctx.buf
+        buf.o = o
         buf.alloc_backward()
         run_backward(ctx.cfg, ctx.vl, q, k, v, qp, kp, dout.contiguous().to(q.dtype), buf)
         dt = q.dtype

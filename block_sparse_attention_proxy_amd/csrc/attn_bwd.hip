@@ -921,12 +921,22 @@ namespace msa {
 int bwd_kernels(KernelEntry* out, int max) {
   const KernelEntry all[] = {
       {"bwd_dq<bf16,d128,dp64>", (const void*)dq_kernel<bf16, 128, 64>, 256, DqCfg<bf16, 128, 64>::LDS_BYTES},
+      {"bwd_dkdv<bf16,d128,dp64,g1>", (const void*)dkdv_kernel<bf16, 128, 64, 1>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
+      {"bwd_dkdv<bf16,d128,dp64,g2>", (const void*)dkdv_kernel<bf16, 128, 64, 2>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
       {"bwd_dkdv<bf16,d128,dp64,g4>", (const void*)dkdv_kernel<bf16, 128, 64, 4>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
       {"bwd_dkdv<bf16,d128,dp64,g8>", (const void*)dkdv_kernel<bf16, 128, 64, 8>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
       {"bwd_dq<bf16,d64,dp32>", (const void*)dq_kernel<bf16, 64, 32>, 256, DqCfg<bf16, 64, 32>::LDS_BYTES},
+      {"bwd_dkdv<bf16,d64,dp32,g1>", (const void*)dkdv_kernel<bf16, 64, 32, 1>, 256, KvCfg<bf16, 64, 32>::LDS_BYTES},
+      {"bwd_dkdv<bf16,d64,dp32,g2>", (const void*)dkdv_kernel<bf16, 64, 32, 2>, 256, KvCfg<bf16, 64, 32>::LDS_BYTES},
       {"bwd_dkdv<bf16,d64,dp32,g4>", (const void*)dkdv_kernel<bf16, 64, 32, 4>, 256, KvCfg<bf16, 64, 32>::LDS_BYTES},
+      {"bwd_dkdv<bf16,d64,dp32,g8>", (const void*)dkdv_kernel<bf16, 64, 32, 8>, 256, KvCfg<bf16, 64, 32>::LDS_BYTES},
       {"bwd_dq<f32,d64,dp32>", (const void*)dq_kernel<float, 64, 32>, 256, DqCfg<float, 64, 32>::LDS_BYTES},
+      {"bwd_dkdv<f32,d64,dp32,g1>", (const void*)dkdv_kernel<float, 64, 32, 1>, 256, KvCfg<float, 64, 32>::LDS_BYTES},
+      {"bwd_dkdv<f32,d64,dp32,g2>", (const void*)dkdv_kernel<float, 64, 32, 2>, 256, KvCfg<float, 64, 32>::LDS_BYTES},
       {"bwd_dkdv<f32,d64,dp32,g4>", (const void*)dkdv_kernel<float, 64, 32, 4>, 256, KvCfg<float, 64, 32>::LDS_BYTES},
+      {"bwd_dkdv<f32,d64,dp32,g8>", (const void*)dkdv_kernel<float, 64, 32, 8>, 256, KvCfg<float, 64, 32>::LDS_BYTES},
+      {"bwd_dqp_reduce<dp64>", (const void*)dqp_reduce_kernel<64>, 256, 0},
+      {"bwd_dqp_reduce<dp32>", (const void*)dqp_reduce_kernel<32>, 256, 0},
   };
   int n = (int)(sizeof(all) / sizeof(all[0]));
   for (int i = 0; i < n && i < max; ++i) out[i] = all[i];

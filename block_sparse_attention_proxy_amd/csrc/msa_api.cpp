@@ -503,14 +503,15 @@ msa_status msa_bwd(const msa_config* cfg, const msa_varlen* vl, const void* q, c
 }
 
 static std::vector<msa::KernelEntry> all_kernels() {
-  std::vector<msa::KernelEntry> v(64);
+  constexpr int kMax = 128;
+  std::vector<msa::KernelEntry> v(kMax);
   int n = 0;
-  n += msa::select_kernels(v.data() + n, 64 - n);
-  n += msa::fwd_kernels(v.data() + n, 64 - n);
-  n += msa::bwd_kernels(v.data() + n, 64 - n);
-  n += msa::bwd_kv_kernels(v.data() + n, 64 - n);
-  n += msa::bwd_q_kernels(v.data() + n, 64 - n);
-  n += msa::share_kernels(v.data() + n, 64 - n);
+  n += msa::select_kernels(v.data() + n, kMax - n);
+  n += msa::fwd_kernels(v.data() + n, kMax - n);
+  n += msa::bwd_kernels(v.data() + n, kMax - n);
+  n += msa::bwd_kv_kernels(v.data() + n, kMax - n);
+  n += msa::bwd_q_kernels(v.data() + n, kMax - n);
+  n += msa::share_kernels(v.data() + n, kMax - n);
   v.resize(n);
   return v;
 }

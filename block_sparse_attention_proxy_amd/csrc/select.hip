@@ -917,8 +917,14 @@ int select_kernels(KernelEntry* out, int max) {
       {"proxy_scores<bf16,dp64,bq128>", (const void*)proxy_scores_lds_kernel<128>, 256, SC_LDS},
       {"proxy_scores<bf16,dp64,bq64>", (const void*)proxy_scores_lds_kernel<64>, 256, SC_LDS},
       {"proxy_scores<bf16,dp32,bq64>", (const void*)proxy_scores_kernel<bf16, 32, 64>, 256, 0},
+      {"proxy_scores<bf16,dp32,bq128>", (const void*)proxy_scores_kernel<bf16, 32, 128>, 256, 0},
       {"proxy_scores<f32,dp32,bq64>", (const void*)proxy_scores_kernel<float, 32, 64>, 256, 0},
+      {"proxy_scores<f32,dp32,bq128>", (const void*)proxy_scores_kernel<float, 32, 128>, 256, 0},
       {"select", (const void*)select_kernel, 256, 0},
+      {"k2q_count", (const void*)k2q_count_kernel, 256, 0},
+      {"k2q_scan", (const void*)k2q_scan_kernel, 256, 0},
+      {"k2q_scatter", (const void*)k2q_scatter_kernel, 256, 0},
+      {"k2q_tail", (const void*)k2q_tail_kernel, 256, 0},
       {"k2q_sort", (const void*)k2q_sort_kernel, 256, 4096 * 4},
   };
   int n = (int)(sizeof(all) / sizeof(all[0]));

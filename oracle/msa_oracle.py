@@ -535,9 +535,12 @@ def sampled_query_side(q, k, v, qp, kp, dO, cu_seqlens, q2k_idx, q2k_cnt, cfg: C
 
 
 def sampled_key_side(q, k, v, qp, kp, dO, cu_seqlens, q2k_idx, q2k_cnt, cfg: Config,
-                     samples: List[Tuple[int, int]], O_for_D=None):
+                     samples: List[Tuple[int, int]], O_for_D=None,
+                     qblocks: Optional[Tuple[int, int]] = None):
     """For sampled (g, global KV block) pairs: dK, dV and dkp of that block's
-    keys, summed over every query block whose selection holds it."""
+    keys, summed over every query block whose selection holds it.  With
+    ``qblocks = (lo, hi)`` only the document's query blocks lo <= I < hi
+    contribute (the full sums are the sums of such parts)."""
     assert cfg.proxy_heads != 1, "sampled evaluation covers one proxy head per group"
     docs = doc_grid(cu_seqlens, cfg)
     out = []
@@ -547,7 +550,8 @@ def sampled_key_side(q, k, v, qp, kp, dO, cu_seqlens, q2k_idx, q2k_cnt, cfg: Con
         dK = np.zeros((len(kr), cfg.head_dim))
         dV = np.zeros((len(kr), cfg.head_dim))
         dKp = np.zeros((len(kr), cfg.proxy_dim))
-        for I in range(doc.nq):
+        lo, hi = (0, doc.nq) if qblocks is None else (max(0, qblocks[0]), min(doc.nq, qblocks[1]))
+        for I in range(lo, hi):
             sel = _sel_of(q2k_idx, q2k_cnt, g, doc.qb0 + I)
             if KB not in sel:
                 continue

@@ -91,3 +91,21 @@ def test_autograd_dense_is_causal_attention():
     _, _, _, dqp, dkp = om.backward(*args, case.cu_seqlens, idx, cnt, ocfg_d)
     assert_close("dqp", got["dqp"], dqp)
     assert_close("dkp", got["dkp"], dkp)
+
+
+def test_autograd_inplace_output_edit_raises():
+    """O is saved for the backward like the inputs: changing the returned
+    output in place before the backward is an autograd error, not a silent
+    change of D = rowsum(dO O)."""
+    w, cfg, ocfg = cfgs(WORKLOADS["layer-32k"], topk=4)
+    case = small_case(w, (900,), seed=8)
+    leaves = [torch.from_numpy(getattr(case, n)).to(torch.bfloat16).cuda().requires_grad_(True)
+              for n in ("q", "k", "v", "qp", "kp")]
+    cu = torch.from_numpy(case.cu_seqlens).cuda()
+    o = msa.msa_attention(*leaves, cu, topk=w.topk, q_block=w.q_block,
+                          cu_seqlens_host=[int(c) for c in case.cu_seqlens])
+    o.data.mul_(1.0)          # no version bump: allowed
+    with torch.no_grad():
+        o.mul_(2.0)           # a real in-place edit
+    with pytest.raises(RuntimeError, match="modified by an inplace operation"):
+        o.backward(torch.from_numpy(case.dO).to(torch.bfloat16).cuda())

@@ -13,12 +13,16 @@ one by one, with the inputs gathered row by row from the seeded device tensors:
 * sampled KV blocks (the last block of a document, and random blocks with
   short inverted lists so that the oracle finishes in seconds): dK, dV and dkp
   summed over every query block that selected them;
+* the KV blocks with the longest inverted list and with the list at the 99th
+  percentile: the same element-wise check, the oracle's sum taken in ranges of
+  query blocks (one progress line per range);
 * whole-layer identities that hold at any size: per group, the sum over keys
   of dV equals the sum over queries and heads of dO (softmax rows sum to one),
   and the sums over keys of dK and dkp vanish (each row of dS and of dY sums to
   zero), within bounds set by bf16 rounding of the probabilities.
 """
 import math
+import time
 
 import numpy as np
 import pytest
@@ -223,3 +227,46 @@ def test_fullsize_sum_identities(full_run):
     log(f"[{name}] sum dkp: max {sp.abs().max().item():.3e}, max ratio to bound {(sp.abs() / bp).max().item():.3f}")
     assert bool((sp.abs() <= bp).all())
     assert math.isfinite(buf.dq.abs().max().item())
+
+
+@pytest.mark.timeout(1800)
+def test_fullsize_hot_lists(full_run):
+    """dK, dV and dkp element-wise on the KV block chosen by the most query
+    blocks, and on one at the 99th percentile of list length.  The list
+    lengths (per group: max, 99th percentile, mean) are logged."""
+    name, w, ocfg, x, cu, buf = full_run
+    k2q_ptr = buf.k2q_ptr.cpu().numpy()
+    lens = np.diff(k2q_ptr, axis=1)                       # [Hkv, NKB]
+    for g in range(lens.shape[0]):
+        nz = lens[g][lens[g] > 0]
+        log(f"[{name}] group {g}: inverted lists max {nz.max()}, p99 {int(np.percentile(nz, 99))}, "
+            f"mean {nz.mean():.1f} over {nz.size} KV blocks")
+    g_hot, kb_hot = np.unravel_index(int(np.argmax(lens)), lens.shape)
+    flat = lens.ravel()
+    p99 = np.percentile(flat[flat > 0], 99)
+    j99 = int(np.argmin(np.where(flat > 0, np.abs(flat - p99), np.inf)))
+    g99, kb99 = np.unravel_index(j99, lens.shape)
+    docs = om.doc_grid(cu, ocfg)
+    L = {n: DeviceRows(x[n]) for n in ("q", "k", "v", "qp", "kp", "dO")}
+    q2k_idx = buf.q2k_idx.cpu().numpy()
+    q2k_cnt = buf.q2k_cnt.cpu().numpy()
+    step = 64
+    for tag, g, KB in (("longest", int(g_hot), int(kb_hot)), ("p99", int(g99), int(kb99))):
+        doc = next(d for d in docs if d.kb0 <= KB < d.kb0 + d.nk)
+        n = int(lens[g, KB])
+        log(f"[{name}] {tag} list: g={g} KB={KB} (block {KB - doc.kb0} of a {doc.length}-token document), "
+            f"{n} query blocks")
+        acc = None
+        t0 = time.time()
+        for lo in range(0, doc.nq, step):
+            part = om.sampled_key_side(L["q"], L["k"], L["v"], L["qp"], L["kp"], L["dO"], cu, q2k_idx,
+                                       q2k_cnt, ocfg, [(g, KB)], qblocks=(lo, lo + step))[0]
+            if acc is None:
+                acc = part
+            else:
+                for k_ in ("dK", "dV", "dkp"):
+                    acc[k_] = acc[k_] + part[k_]
+            log(f"  query blocks {lo}..{min(doc.nq, lo + step) - 1} of {doc.nq} done, {time.time() - t0:.0f} s")
+        kt = torch.as_tensor(acc["keys"], device="cuda")
+        for k_, t in (("dK", buf.dk), ("dV", buf.dv), ("dkp", buf.dkp)):
+            _close(k_, t.index_select(0, kt)[:, g, :].cpu().numpy(), acc[k_])

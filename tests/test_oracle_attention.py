@@ -290,6 +290,12 @@ def test_sampled_matches_full():
         np.testing.assert_allclose(r["dK"], full["dk"][r["keys"], r["g"]], atol=1e-12)
         np.testing.assert_allclose(r["dV"], full["dv"][r["keys"], r["g"]], atol=1e-12)
         np.testing.assert_allclose(r["dkp"], full["dkp"][r["keys"], r["g"]], atol=1e-12)
+    # restricted to ranges of query blocks, the parts sum to the whole
+    parts = [om.sampled_key_side(*X, cu, full["q2k_idx"], full["q2k_cnt"], cfg, [(0, 0), (1, 4), (0, 7)],
+                                 qblocks=(lo, lo + 4)) for lo in range(0, 12, 4)]
+    for i, r in enumerate(ks):
+        for key in ("dK", "dV", "dkp"):
+            np.testing.assert_allclose(sum(p[i][key] for p in parts), r[key], atol=1e-12)
 
 
 # ---------------------------------------------------------------------------
