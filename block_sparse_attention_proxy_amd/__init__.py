@@ -8,6 +8,7 @@ device memory and streams.
 """
 from ._lib import EXPORTS, LIB_PATH, MsaError, load  # noqa: F401
 from .ops import (Buffers, Config, Varlen, kernel_resources, msa_bwd, msa_fwd,  # noqa: F401
-                  msa_get_layout, msa_proxy_scores, msa_select_blocks, profile_collect,
+                  msa_get_layout, msa_proxy_scores, msa_select_blocks, msa_select_blocks_noalloc,
+                  profile_collect,
                   profile_enable, run_backward, run_forward)
 from .attention import msa_attention  # noqa: F401

@@ -17,9 +17,10 @@ MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_HIP, MSA_ERR_WORKSPACE
 MSA_BF16, MSA_F32 = 0, 1
 
 # Every symbol include/msa.h declares.
-ABI_VERSION = 3        # include/msa.h MSA_ABI_VERSION; msa_config / msa_layout below
+ABI_VERSION = 4        # include/msa.h MSA_ABI_VERSION; msa_config / msa_layout below
 EXPORTS = ("msa_abi_version", "msa_status_string", "msa_last_error", "msa_get_layout",
-           "msa_proxy_scores", "msa_select_blocks", "msa_fwd", "msa_bwd", "msa_kernel_count",
+           "msa_proxy_scores", "msa_select_blocks", "msa_select_blocks_noalloc",
+           "msa_select_blocks_noalloc_max_bytes", "msa_fwd", "msa_bwd", "msa_kernel_count",
            "msa_kernel_info", "msa_profile_enable", "msa_profile_collect", "msa_profile_entry")
 
 
@@ -78,6 +79,10 @@ def load():
     lib.msa_proxy_scores.argtypes = [pc, pv, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.msa_select_blocks.restype = c_int32
     lib.msa_select_blocks.argtypes = [pc, pv, c_void_p] + [c_void_p] * 4 + [c_void_p, c_size_t, c_void_p]
+    lib.msa_select_blocks_noalloc.restype = c_int32
+    lib.msa_select_blocks_noalloc.argtypes = [pc, pv, c_void_p] + [c_void_p] * 4 + [c_void_p]
+    lib.msa_select_blocks_noalloc_max_bytes.restype = c_int64
+    lib.msa_select_blocks_noalloc_max_bytes.argtypes = []
     lib.msa_fwd.restype = c_int32
     lib.msa_fwd.argtypes = [pc, pv] + [c_void_p] * 10 + [c_void_p, c_size_t, c_void_p]
     lib.msa_bwd.restype = c_int32

@@ -424,6 +424,52 @@ msa_status msa_select_blocks(const msa_config* cfg, const msa_varlen* vl, const 
   return MSA_OK;
 }
 
+msa_status msa_select_blocks_noalloc(const msa_config* cfg, const msa_varlen* vl,
+                                     const float* block_scores, int32_t* q2k_idx, int32_t* q2k_cnt,
+                                     int32_t* k2q_ptr, int32_t* k2q_idx, void* stream) {
+  Plan P;
+  msa_status s = plan(cfg, vl, &P);
+  if (s != MSA_OK) return s;
+  if (P.g.T == 0) return MSA_OK;
+  if ((s = check_ptrs({{block_scores, "block_scores"}, {q2k_idx, "q2k_idx"}, {q2k_cnt, "q2k_cnt"},
+                       {k2q_ptr, "k2q_ptr"}, {k2q_idx, "k2q_idx"}})) != MSA_OK)
+    return s;
+  if (!P.g.cu) return fail(MSA_ERR_INVALID_ARG, "cu_seqlens (device) must be non-null");
+  // selection reads the workspace prefix only: the per-document tables and
+  // the inverted-index counters, which end where the backward's vectors begin
+  const int64_t need = P.off_delta;
+  if (need > (int64_t)msa::kNoAllocScratchBytes)
+    return fail(MSA_ERR_WORKSPACE,
+                "msa_select_blocks_noalloc needs %lld bytes of scratch; its static scratch holds %lld "
+                "(use msa_select_blocks with a workspace)",
+                (long long)need, (long long)msa::kNoAllocScratchBytes);
+  void* scr = nullptr;
+  hipError_t e = msa::noalloc_scratch(&scr);
+  if (e != hipSuccess) return hip_fail(e, "scratch address");
+  char* base = static_cast<char*>(scr);
+  P.g.qb0 = reinterpret_cast<int32_t*>(base + P.off_qb0);
+  P.g.kb0 = reinterpret_cast<int32_t*>(base + P.off_kb0);
+  P.g.s0 = reinterpret_cast<int64_t*>(base + P.off_s0);
+  P.g.order = reinterpret_cast<int32_t*>(base + P.off_order);
+  P.g.unit0 = reinterpret_cast<int32_t*>(base + P.off_unit0);
+  P.g.qdoc = reinterpret_cast<int32_t*>(base + P.off_qdoc);
+  P.g.kdoc = reinterpret_cast<int32_t*>(base + P.off_kdoc);
+  msa::Work w{};
+  w.counts = reinterpret_cast<int32_t*>(base + P.off_counts);
+  w.cursor = reinterpret_cast<int32_t*>(base + P.off_cursor);
+  if ((s = check_bound(P.g)) != MSA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  e = msa::launch_meta(P.g, st);
+  if (e != hipSuccess) return hip_fail(e, "metadata");
+  const msa::Geo gp = proxy_geo(P);
+  if ((s = check_bound(gp)) != MSA_OK) return s;
+  e = msa::launch_select(gp, block_scores, q2k_idx, q2k_cnt, k2q_ptr, k2q_idx, w, st);
+  if (e != hipSuccess) return hip_fail(e, "select_blocks");
+  return MSA_OK;
+}
+
+int64_t msa_select_blocks_noalloc_max_bytes(void) { return (int64_t)msa::kNoAllocScratchBytes; }
+
 msa_status msa_fwd(const msa_config* cfg, const msa_varlen* vl, const void* q, const void* k,
                    const void* v, const void* qp, const void* kp, const int32_t* q2k_idx,
                    const int32_t* q2k_cnt, void* o, float* lse, float* lse_p, void* workspace,

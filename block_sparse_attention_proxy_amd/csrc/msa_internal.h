@@ -65,6 +65,12 @@ struct Work {
   float* cpart;                      // [Hkv * nhg * T * DP] proxy-gradient partials (G > 4)
 };
 
+// Scratch of the allocation-free selection entry point: a file-scope device
+// array of this many bytes per GPU.  noalloc_scratch() returns the current
+// device's address of it (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_meta(const Geo& g, hipStream_t s);
 // shared proxy head: row broadcast (dst[r][c] = src[r], rows of row_bytes, a
 // multiple of 4) and the in-order average over copies of fp32 rows

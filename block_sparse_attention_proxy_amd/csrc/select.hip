@@ -12,7 +12,39 @@
 #include "msa_internal.h"
 #include "msa_profile.h"
 
+#include <mutex>
+
 namespace msa {
+
+// ---------------------------------------------------------------------------
+// Static scratch of the allocation-free selection entry point: the
+// per-document tables and the inverted-index counters live here instead of
+// in a caller's workspace.  Every GPU the library runs on holds its own copy
+// until the process ends.  In host code the array's name is only a stand-in:
+// its device address comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEV] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;

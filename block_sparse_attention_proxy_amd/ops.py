@@ -123,6 +123,23 @@ def msa_select_blocks(cfg: Config, vl: Varlen, block_scores, q2k_idx, q2k_cnt, k
                                 _stream(stream)))
 
 
+def msa_select_blocks_noalloc(cfg: Config, vl: Varlen, block_scores, q2k_idx, q2k_cnt, k2q_ptr, k2q_idx,
+                              stream=None):
+    """msa_select_blocks with the library's static scratch instead of a
+    workspace (no device allocation); calls on one GPU must not overlap."""
+    lib = load()
+    lay = msa_get_layout(cfg, vl)
+    Hp = lay["proxy_heads"]
+    i32 = torch.int32
+    a = [_ptr(block_scores, "block_scores", torch.float32, (Hp, lay["score_elems"])),
+         _ptr(q2k_idx, "q2k_idx", i32, (Hp, lay["total_qblocks"], lay["sel_stride"])),
+         _ptr(q2k_cnt, "q2k_cnt", i32, (Hp, lay["total_qblocks"])),
+         _ptr(k2q_ptr, "k2q_ptr", i32, (Hp, lay["total_kvblocks"] + 1)),
+         _ptr(k2q_idx, "k2q_idx", i32, (Hp, lay["k2q_capacity"]))]
+    c, v = cfg.to_c(), vl.to_c()
+    check(lib.msa_select_blocks_noalloc(ctypes.byref(c), ctypes.byref(v), *a, _stream(stream)))
+
+
 def msa_fwd(cfg: Config, vl: Varlen, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, workspace,
             stream=None):
     lib = load()

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 3
+#define MSA_ABI_VERSION 4
 
 typedef enum {
   MSA_OK = 0,
@@ -152,6 +152,27 @@ msa_status msa_select_blocks(const msa_config* cfg, const msa_varlen* vl, const 
                              int32_t* q2k_idx, int32_t* q2k_cnt, int32_t* k2q_ptr,
                              int32_t* k2q_idx, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * msa_select_blocks without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments as msa_select_blocks minus the
+ * workspace, same outputs bit for bit, same kernels.  The per-document tables
+ * and inverted-index counters live in a static device array of
+ * msa_select_blocks_noalloc_max_bytes() bytes (8 MiB) that the library holds
+ * on every GPU it runs on until the process ends; this call allocates
+ * nothing.  Needed: about 0.6 bytes per token with 8 proxy heads (the tables
+ * and counters of the packing), so packings up to about 14M tokens fit; a
+ * larger one returns MSA_ERR_WORKSPACE before anything is launched.  Every
+ * call on a GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must be ordered by
+ * the caller.  The counters are cleared by the call itself (with kernels, no
+ * memset), so nothing has to be zeroed between calls.
+ */
+msa_status msa_select_blocks_noalloc(const msa_config* cfg, const msa_varlen* vl,
+                                     const float* block_scores, int32_t* q2k_idx, int32_t* q2k_cnt,
+                                     int32_t* k2q_ptr, int32_t* k2q_idx, void* stream);
+int64_t msa_select_blocks_noalloc_max_bytes(void);
 
 /*
  * Sparse GQA forward over the selected blocks (socker-news summary 要約;

@@ -23,7 +23,7 @@ def test_exports_match_header():
     assert declared == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.msa_abi_version() == _lib.ABI_VERSION == 3
+    assert lib.msa_abi_version() == _lib.ABI_VERSION == 4
     assert ctypes.sizeof(_lib.MsaConfig) == 14 * 4
     assert ctypes.sizeof(_lib.MsaLayout) == 9 * 8
     assert lib.msa_status_string(0).decode() == "ok"
@@ -160,3 +160,26 @@ def test_layout_proxy_heads(proxy_heads, Hp):
         assert lay["workspace_bytes"] >= base["workspace_bytes"] + copies
     else:
         assert lay["workspace_bytes"] == base["workspace_bytes"]
+
+
+def test_select_noalloc_rejects_packings_beyond_its_scratch():
+    """The allocation-free selection entry point checks its scratch need on the
+    host and refuses a packing that does not fit, before anything is launched
+    (so this runs without a GPU: the device pointers are never used)."""
+    lib = msa.load()
+    cap = lib.msa_select_blocks_noalloc_max_bytes()
+    assert cap == 8 << 20
+    seqlens = [1 << 21] * 8                     # 16M tokens: 2^21 per document
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    cfg = msa.Config(32, 8, 128, 64, 128, 64, 0, dtype="bf16").to_c()
+    fake = 1 << 20                              # aligned, never dereferenced
+    vl = _lib.MsaVarlen(fake, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(seqlens), int(cu[-1]))
+    st = lib.msa_select_blocks_noalloc(ctypes.byref(cfg), ctypes.byref(vl), fake, fake, fake, fake, fake, None)
+    assert st == _lib.MSA_ERR_WORKSPACE
+    msg = lib.msa_last_error().decode()
+    assert "scratch" in msg and str(cap) in msg
+    # a small packing passes the host checks up to the first device call
+    small = np.array([0, 4096], dtype=np.int32)
+    vl2 = _lib.MsaVarlen(fake, small.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 1, 4096)
+    lay = _lib.MsaLayout()
+    assert lib.msa_get_layout(ctypes.byref(cfg), ctypes.byref(vl2), ctypes.byref(lay)) == _lib.MSA_OK
