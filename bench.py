@@ -429,7 +429,7 @@ def main(argv=None):
     f = flop_model(w, seqlens, lay["scored_pairs"])
     per_kernel = {k: {"avg_ms": ms / n, "launches_per_step": n / a.steps} for k, (ms, n) in kern.items()}
     stage_of = {"proxy_scores": "scores", "select": "select", "k2q_count": "select", "k2q_scan": "select",
-                "k2q_scatter": "select", "k2q_tail": "select", "k2q_sort": "select", "fill": "select",
+                "k2q_emit": "select",
                 "fwd": "fwd", "proxy_lse": "fwd", "bwd_dq": "bwd",
                 "bwd_dqp_reduce": "bwd", "bwd_dkdv": "bwd", "meta": "meta"}
     stages = {}

@@ -39,8 +39,8 @@ int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Plan {
   msa::Geo g{};
   msa_layout lay{};
-  int64_t off_qb0, off_kb0, off_s0, off_order, off_unit0, off_qdoc, off_kdoc, off_counts, off_cursor, off_delta, off_lse2, off_lsep2,
-      off_cpart;
+  int64_t off_qb0, off_kb0, off_s0, off_order, off_unit0, off_slab0, off_qdoc, off_kdoc, off_counts, off_totals;
+  int64_t off_delta, off_lse2, off_lsep2, off_cpart;
   // one proxy head shared by every KV group: the per-group copies the
   // forward and backward run on (used only when shared)
   bool shared = false;
@@ -90,7 +90,7 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
   if (!vl->cu_seqlens_host) return fail(MSA_ERR_INVALID_ARG, "cu_seqlens_host must be non-null");
   const int32_t* cu = vl->cu_seqlens_host;
   if (cu[0] != 0) return fail(MSA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
-  int64_t nqb = 0, nkb = 0, se = 0, pairs = 0, max_nq = 0, units = 0;
+  int64_t nqb = 0, nkb = 0, se = 0, pairs = 0, max_nq = 0, units = 0, slabs = 0;
   for (int b = 0; b < vl->batch; ++b) {
     const int64_t L = (int64_t)cu[b + 1] - cu[b];
     if (L < 0) return fail(MSA_ERR_INVALID_ARG, "cu_seqlens decreases at index %d", b + 1);
@@ -100,6 +100,7 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
     se += nq * nk;
     if (nq > max_nq) max_nq = nq;
     units += ((L + 127) / 128 + 1) / 2;
+    slabs += (nk + msa::K2Q_SLAB - 1) / msa::K2Q_SLAB;
     for (int64_t I = 0; I < nq; ++I) {
       const int64_t diag = I * c.q_block / 128;
       const int64_t pool = diag - span;           // candidates: blocks below the window's span
@@ -122,6 +123,8 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
   g.dil = (int32_t)dil; g.span = (int32_t)span;
   g.B = vl->batch; g.T = vl->total_tokens; g.nqb = (int32_t)nqb; g.nkb = (int32_t)nkb;
   g.max_nq = (int32_t)max_nq; g.cap = nqb * g.stride; g.score_elems = se; g.n_units = (int32_t)units;
+  g.nslab = (int32_t)slabs;
+  g.k2q_chunks = (int32_t)((max_nq + msa::K2Q_CHUNK - 1) / msa::K2Q_CHUNK);
   g.scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.f / std::sqrt((float)c.head_dim);
   g.pscale = c.proxy_scale > 0.f ? c.proxy_scale : 1.f / std::sqrt((float)c.proxy_dim);
   g.lam = c.proxy_loss_weight;
@@ -136,10 +139,12 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
   P->off_s0 = off;     off = align_up(off + 8 * (B + 1));
   P->off_order = off;  off = align_up(off + 4 * B);
   P->off_unit0 = off;  off = align_up(off + 4 * (B + 1));
+  P->off_slab0 = off;  off = align_up(off + 4 * (B + 1));
   P->off_qdoc = off;   off = align_up(off + 4 * nqb);
   P->off_kdoc = off;   off = align_up(off + 4 * nkb);
-  P->off_counts = off; off = align_up(off + 4 * (int64_t)c.heads_kv * nkb);
-  P->off_cursor = off; off = align_up(off + 4 * (int64_t)c.heads_kv * nkb);
+  P->off_counts = off;
+  off = align_up(off + 4 * (int64_t)c.heads_kv * slabs * ((max_nq + msa::K2Q_CHUNK - 1) / msa::K2Q_CHUNK) * msa::K2Q_SLAB);
+  P->off_totals = off; off = align_up(off + 4 * (int64_t)c.heads_kv * nkb);
   P->off_delta = off;  off = align_up(off + 4 * (int64_t)c.heads_q * vl->total_tokens);
   P->off_lse2 = off;   off = align_up(off + 4 * (int64_t)c.heads_q * vl->total_tokens);
   P->off_lsep2 = off;  off = align_up(off + 4 * (int64_t)c.heads_kv * vl->total_tokens);
@@ -188,9 +193,10 @@ msa_status bind_workspace(Plan* P, void* ws, size_t ws_bytes, msa::Work* w) {
   P->g.unit0 = reinterpret_cast<int32_t*>(base + P->off_unit0);
   P->g.qdoc = reinterpret_cast<int32_t*>(base + P->off_qdoc);
   P->g.kdoc = reinterpret_cast<int32_t*>(base + P->off_kdoc);
+  P->g.slab0 = reinterpret_cast<int32_t*>(base + P->off_slab0);
   if (w) {
     w->counts = reinterpret_cast<int32_t*>(base + P->off_counts);
-    w->cursor = reinterpret_cast<int32_t*>(base + P->off_cursor);
+    w->totals = reinterpret_cast<int32_t*>(base + P->off_totals);
     w->delta = reinterpret_cast<float*>(base + P->off_delta);
     w->lse2 = reinterpret_cast<float*>(base + P->off_lse2);
     w->lsep2 = reinterpret_cast<float*>(base + P->off_lsep2);
@@ -209,7 +215,7 @@ msa::Geo proxy_geo(const Plan& P) {
 
 // Every per-document table a kernel reads must point into a bound workspace.
 msa_status check_bound(const msa::Geo& g) {
-  if (!g.cu || !g.qb0 || !g.kb0 || !g.s0 || !g.order || !g.unit0 || !g.qdoc || !g.kdoc)
+  if (!g.cu || !g.qb0 || !g.kb0 || !g.s0 || !g.order || !g.unit0 || !g.qdoc || !g.kdoc || !g.slab0)
     return fail(MSA_ERR_INVALID_ARG, "internal: workspace tables not bound");
   return MSA_OK;
 }
@@ -436,7 +442,7 @@ msa_status msa_select_blocks_noalloc(const msa_config* cfg, const msa_varlen* vl
     return s;
   if (!P.g.cu) return fail(MSA_ERR_INVALID_ARG, "cu_seqlens (device) must be non-null");
   // selection reads the workspace prefix only: the per-document tables and
-  // the inverted-index counters, which end where the backward's vectors begin
+  // the inverted-index counts, which end where the backward's vectors begin
   const int64_t need = P.off_delta;
   if (need > (int64_t)msa::kNoAllocScratchBytes)
     return fail(MSA_ERR_WORKSPACE,
@@ -454,9 +460,10 @@ msa_status msa_select_blocks_noalloc(const msa_config* cfg, const msa_varlen* vl
   P.g.unit0 = reinterpret_cast<int32_t*>(base + P.off_unit0);
   P.g.qdoc = reinterpret_cast<int32_t*>(base + P.off_qdoc);
   P.g.kdoc = reinterpret_cast<int32_t*>(base + P.off_kdoc);
+  P.g.slab0 = reinterpret_cast<int32_t*>(base + P.off_slab0);
   msa::Work w{};
   w.counts = reinterpret_cast<int32_t*>(base + P.off_counts);
-  w.cursor = reinterpret_cast<int32_t*>(base + P.off_cursor);
+  w.totals = reinterpret_cast<int32_t*>(base + P.off_totals);
   if ((s = check_bound(P.g)) != MSA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   e = msa::launch_meta(P.g, st);

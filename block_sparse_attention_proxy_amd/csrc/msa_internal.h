@@ -42,6 +42,8 @@ struct Geo {
   int64_t cap;                       // k2q capacity per group = nqb * stride
   int64_t score_elems;               // per group
   int32_t n_units;                   // proxy-scoring units (pairs of 128-row tiles)
+  int32_t nslab;                     // column slabs (K2Q_SLAB blocks) of the inverted index, per group
+  int32_t k2q_chunks;                // 256-row chunks per slab (the most any slab needs)
   float scale, pscale, lam;          // softmax scale, proxy scale, proxy loss weight
   float scale_log2, pscale_log2;     // scale * log2(e), pscale * log2(e)
   const int32_t* cu;                 // device cu_seqlens [B + 1]
@@ -53,22 +55,28 @@ struct Geo {
   int32_t* unit0;                    // [B + 1] first scoring unit, in that order
   int32_t* qdoc;                     // [nqb] document of each global query block
   int32_t* kdoc;                     // [nkb] document of each global KV block
+  int32_t* slab0;                    // [B + 1] first column slab of each document
 };
 
 // Workspace regions (byte offsets are computed by the host layout routine).
 struct Work {
-  int32_t* counts;                   // [Hkv * nkb]
-  int32_t* cursor;                   // [Hkv * nkb]
+  int32_t* counts;                   // [Hkv * nslab * k2q_chunks * 64] selections per (slab, chunk, block)
+  int32_t* totals;                   // [Hkv * nkb] selections per KV block
   float* delta;                      // [Hq * T]       rowsum(dO * O)
   float* lse2;                       // [Hq * T]       main LSE in log2 units
   float* lsep2;                      // [Hkv * T]      proxy LSE in log2 units
   float* cpart;                      // [Hkv * nhg * T * DP] proxy-gradient partials (G > 4)
 };
 
+// Inverted-index build: KV blocks of a document are taken in slabs of this
+// many, the rows that can select a slab in chunks of 256.
+constexpr int K2Q_SLAB = 256;
+constexpr int K2Q_CHUNK = 256;
+
 // Scratch of the allocation-free selection entry point: a file-scope device
 // array of this many bytes per GPU.  noalloc_scratch() returns the current
 // device's address of it (looked up once per device).
-constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 hipError_t noalloc_scratch(void** ptr);
 
 hipError_t launch_meta(const Geo& g, hipStream_t s);

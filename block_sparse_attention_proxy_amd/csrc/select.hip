@@ -46,21 +46,6 @@ hipError_t noalloc_scratch(void** ptr) {
   return hipSuccess;
 }
 
-__global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t step = (int64_t)gridDim.x * blockDim.x;
-  for (; i < n; i += step) p[i] = v;
-}
-
-static hipError_t fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  { ProfScope _ps("fill", s);
-  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, v, n);
-  return hipGetLastError(); }
-}
-
 // Index b in [0, n) with a[b] <= x < a[b + 1] (a has n + 1 non-decreasing entries).
 template <typename I>
 __device__ __forceinline__ int find_segment(const I* a, int n, I x) {
@@ -139,6 +124,15 @@ __global__ __launch_bounds__(256) void meta_kernel(Geo g) {
     }
     int64_t e = block_exscan256(n, sh, cu_);
     if (r <= B) g.unit0[r] = (int32_t)e;
+  }
+  // column slabs of the inverted index (K2Q_SLAB blocks each), in document order
+  int64_t cs_ = 0;
+  for (int base = 0; base < B + 1; base += 256) {
+    int bb = base + threadIdx.x;
+    int64_t n = 0;
+    if (bb < B) n = ((g.cu[bb + 1] - g.cu[bb] + 127) / 128 + K2Q_SLAB - 1) / K2Q_SLAB;
+    int64_t e = block_exscan256(n, sh, cs_);
+    if (bb <= B) g.slab0[bb] = (int32_t)e;
   }
 }
 
@@ -607,14 +601,65 @@ __device__ __forceinline__ void radix_pick(SelLds& w, int lane, uint32_t& digit,
   wave_lds_sync();
 }
 
+// Float wave reductions (DPP within rows of 16 lanes, then the four row results).
+template <int SHIFT>
+__device__ __forceinline__ float row_shr_f(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), 0x110 + SHIFT,
+                                                    0xf, 0xf, false));
+}
+__device__ __forceinline__ float rd_lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_fmax(float v) {
+  v = fmaxf(v, row_shr_f<1>(-INFINITY, v));
+  v = fmaxf(v, row_shr_f<2>(-INFINITY, v));
+  v = fmaxf(v, row_shr_f<4>(-INFINITY, v));
+  v = fmaxf(v, row_shr_f<8>(-INFINITY, v));
+  return fmaxf(fmaxf(rd_lane_f(v, 15), rd_lane_f(v, 31)), fmaxf(rd_lane_f(v, 47), rd_lane_f(v, 63)));
+}
+__device__ __forceinline__ float wave_fmin(float v) {
+  v = fminf(v, row_shr_f<1>(INFINITY, v));
+  v = fminf(v, row_shr_f<2>(INFINITY, v));
+  v = fminf(v, row_shr_f<4>(INFINITY, v));
+  v = fminf(v, row_shr_f<8>(INFINITY, v));
+  return fminf(fminf(rd_lane_f(v, 15), rd_lane_f(v, 31)), fminf(rd_lane_f(v, 47), rd_lane_f(v, 63)));
+}
+
 // Emission modes of the register path.
 enum SelMode { SEL_WHOLE = 0, SEL_CUT = 1, SEL_EQ = 2 };
 
 // Selection: one wave per (group, query block).  Rows of up to 64 * SEL_REG
 // candidates are read once into registers; longer rows re-read the scores in
 // each of four fixed 8-bit steps.
-constexpr int SEL_REG = 32;
+constexpr int SEL_REG = 20;
 
+// Rank the members of the cut bin (at most 64, collected in ascending block
+// order into LDS) by (key descending, block ascending) and return the one of
+// rank rem - 1: its key and block.
+__device__ __forceinline__ void rank_members(SelLds& w, int lane, int cnt, int rem, uint32_t& cut_key,
+                                             int& cut_j) {
+  wave_lds_sync();
+  const uint32_t K = lane < cnt ? w.mkey[lane] : 0u;
+  const int J = lane < cnt ? w.mj[lane] : 0;
+  int rank = 0;
+  for (int m = 0; m < cnt; ++m) {
+    const uint32_t Km = rd_lane(K, m);
+    rank += (Km > K || (Km == K && m < lane)) ? 1 : 0;
+  }
+  const int src = __ffsll((unsigned long long)__ballot(lane < cnt && rank == rem - 1)) - 1;
+  cut_key = rd_lane(K, src);
+  cut_j = (int)rd_lane((uint32_t)J, src);
+  wave_lds_sync();
+}
+
+// The first step on a row held in registers: 256 bins of equal width over
+// [min, max] of the row's scores, bin(s) = min(255, (int)((max - s) * 256 /
+// (max - min))).  Rounding is monotone, so bin(s) is non-increasing in s and a
+// score in a lower bin is strictly larger than every score in a higher one:
+// the bins refine the order (score descending, block ascending).  One
+// histogram locates the bin of the (k-1)-th key; a bin holding at most 64
+// keys is ranked exactly.  Rows whose range is not finite, or whose cut bin is
+// larger, take the radix steps on order-preserving integer keys instead.
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ scores,
                                                      int32_t* __restrict__ q2k_idx,
                                                      int32_t* __restrict__ q2k_cnt, Geo g) {
@@ -639,96 +684,162 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
   if (pool <= g.topk - 1) {                       // all of them are taken
     for (int j = lane; j < pool; j += 64) out[j] = kb0 + j;
     pos = pool > 0 ? pool : 0;
-  } else {
+  } else if (g.topk > 1) {
     const int ncand = pool;
     const float* srow = scores + (int64_t)grp * g.score_elems + g.s0[b] + (int64_t)I * nk;
     int rem = g.topk - 1;
-    uint32_t prefix = 0, pmask = 0;
+    // emit the taken candidates in ascending block order (ballot prefix)
+    auto emit = [&](int r, bool take) __attribute__((always_inline)) {
+      const int j = r * 64 + lane;
+      const uint64_t tm = __ballot(take);
+      if (take) out[pos + __popcll(tm & lanes_below(lane))] = kb0 + j;
+      pos += __popcll(tm);
+    };
     if (ncand <= 64 * SEL_REG) {
-      uint32_t key[SEL_REG];
-      uint32_t kmin = 0xffffffffu, kmax = 0u;
       // the row through a buffer descriptor: lane offsets are immediates and
       // reads past the row's end return zero (and are marked invalid)
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)srow, (short)0, ncand * 4, 0x00020000);
       // all of the row's loads are issued before the first is used
-      uint32_t raw[SEL_REG];
+      uint32_t key[SEL_REG];
 #pragma unroll
       for (int r = 0; r < SEL_REG; ++r)
-        if (r * 64 < ncand) raw[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4 + r * 256, 0, 0);
+        if (r * 64 < ncand) key[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4 + r * 256, 0, 0);
+      float fhi = -INFINITY, flo = INFINITY;
 #pragma unroll
       for (int r = 0; r < SEL_REG; ++r) {
         if (r * 64 >= ncand) break;
-        const int j = r * 64 + lane;
-        const uint32_t kv = order_key(__builtin_bit_cast(float, raw[r]));
-        key[r] = j < ncand ? kv : 0u;
-        kmin = min(kmin, j < ncand ? kv : 0xffffffffu);
-        kmax = max(kmax, key[r]);
+        const float sv = __builtin_bit_cast(float, key[r]);
+        const bool valid = r * 64 + lane < ncand;
+        fhi = fmaxf(fhi, valid ? sv : -INFINITY);
+        flo = fminf(flo, valid ? sv : INFINITY);
       }
-      kmin = wave_min(kmin);
-      kmax = wave_max(kmax);
-      int mode = SEL_EQ;
-      uint32_t cut_key = 0;
-      int cut_j = 0;
-      if (rem > 0 && kmin == kmax) {
-        prefix = kmin;                            // all keys equal: lowest indices win
-        pmask = 0xffffffffu;
-      } else if (rem > 0) {
-        int top = 31 - __clz(kmin ^ kmax);        // highest bit where the keys differ
-        pmask = ~((2u << top) - 1u);              // 0 when top is 31
-        prefix = kmin & pmask;
-        for (;;) {
-          const int lo = top >= 7 ? top - 7 : 0;
-          const uint32_t wmask = ((2u << top) - 1u) & ~((1u << lo) - 1u);
-          hist_clear(w, lane);
+      fhi = wave_fmax(fhi);
+      flo = wave_fmin(flo);
+      const float inv = 256.f / (fhi - flo);
+      bool done = false;
+      if (fhi - flo <= 3.0e38f && inv <= 3.0e38f) {     // finite, non-zero range
+        uint32_t bins[(SEL_REG + 3) / 4];                 // one byte per key
+        hist_clear(w, lane);
+#pragma unroll
+        for (int r = 0; r < SEL_REG; ++r) {
+          if (r * 64 >= ncand) break;
+          const float sv = __builtin_bit_cast(float, key[r]);
+          const int bn = min(255, max(0, (int)((fhi - sv) * inv)));
+          if ((r & 3) == 0) bins[r >> 2] = 0u;
+          bins[r >> 2] |= (uint32_t)bn << (8 * (r & 3));
+          if (r * 64 + lane < ncand) atomicAdd(&w.hist[bn], 1u);
+        }
+        uint32_t digit;
+        int cnt;
+        int brem = rem;
+        radix_pick(w, lane, digit, brem, cnt);        // hist[i] holds bin i: bin = 255 - digit
+        const uint32_t bstar = 255u - digit;
+        if (cnt == brem) {                            // the cut bin is taken whole
 #pragma unroll
           for (int r = 0; r < SEL_REG; ++r) {
             if (r * 64 >= ncand) break;
-            if (r * 64 + lane < ncand && (key[r] & pmask) == prefix)
-              atomicAdd(&w.hist[255u - ((key[r] >> lo) & 255u)], 1u);
+            const uint32_t bn = (bins[r >> 2] >> (8 * (r & 3))) & 255u;
+            emit(r, r * 64 + lane < ncand && bn <= bstar);
           }
-          uint32_t digit;
-          int cnt;
-          radix_pick(w, lane, digit, rem, cnt);
-          prefix |= (digit << lo) & wmask;
-          pmask |= wmask;
-          if (cnt == rem) { mode = SEL_WHOLE; break; }
-          if (cnt <= 64) {
-            // rank the bin's members (collected in ascending block order)
-            int base = 0;
+          done = true;
+        } else if (cnt <= 64) {
+          int base = 0;
+#pragma unroll
+          for (int r = 0; r < SEL_REG; ++r) {
+            if (r * 64 >= ncand) break;
+            const int j = r * 64 + lane;
+            const uint32_t bn = (bins[r >> 2] >> (8 * (r & 3))) & 255u;
+            const bool in = j < ncand && bn == bstar;
+            const uint64_t m = __ballot(in);
+            if (in) {
+              const int p = base + __popcll(m & lanes_below(lane));
+              w.mkey[p] = order_key(__builtin_bit_cast(float, key[r]));
+              w.mj[p] = j;
+            }
+            base += __popcll(m);
+          }
+          uint32_t cut_key;
+          int cut_j;
+          rank_members(w, lane, cnt, brem, cut_key, cut_j);
+#pragma unroll
+          for (int r = 0; r < SEL_REG; ++r) {
+            if (r * 64 >= ncand) break;
+            const int j = r * 64 + lane;
+            const uint32_t bn = (bins[r >> 2] >> (8 * (r & 3))) & 255u;
+            const uint32_t kv = order_key(__builtin_bit_cast(float, key[r]));
+            emit(r, j < ncand && (bn < bstar || (bn == bstar && (kv > cut_key || (kv == cut_key && j <= cut_j)))));
+          }
+          done = true;
+        }
+      }
+      if (!done) {
+        // radix steps over 8-bit windows of order-preserving keys, the first
+        // at the highest bit where the row's keys differ
+#pragma unroll
+        for (int r = 0; r < SEL_REG; ++r) {
+          if (r * 64 >= ncand) break;
+          key[r] = r * 64 + lane < ncand ? order_key(__builtin_bit_cast(float, key[r])) : 0u;
+        }
+        uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+        for (int r = 0; r < SEL_REG; ++r) {
+          if (r * 64 >= ncand) break;
+          kmin = min(kmin, r * 64 + lane < ncand ? key[r] : 0xffffffffu);
+          kmax = max(kmax, key[r]);
+        }
+        kmin = wave_min(kmin);
+        kmax = wave_max(kmax);
+        int mode = SEL_EQ;
+        uint32_t cut_key = 0, prefix = 0, pmask = 0;
+        int cut_j = 0;
+        if (kmin == kmax) {
+          prefix = kmin;                            // all keys equal: lowest indices win
+          pmask = 0xffffffffu;
+        } else {
+          int top = 31 - __clz(kmin ^ kmax);        // highest bit where the keys differ
+          pmask = ~((2u << top) - 1u);              // 0 when top is 31
+          prefix = kmin & pmask;
+          for (;;) {
+            const int lo = top >= 7 ? top - 7 : 0;
+            const uint32_t wmask = ((2u << top) - 1u) & ~((1u << lo) - 1u);
+            hist_clear(w, lane);
 #pragma unroll
             for (int r = 0; r < SEL_REG; ++r) {
               if (r * 64 >= ncand) break;
-              const int j = r * 64 + lane;
-              const bool in = j < ncand && (key[r] & pmask) == prefix;
-              const uint64_t m = __ballot(in);
-              if (in) {
-                const int p = base + __popcll(m & lanes_below(lane));
-                w.mkey[p] = key[r];
-                w.mj[p] = j;
+              if (r * 64 + lane < ncand && (key[r] & pmask) == prefix)
+                atomicAdd(&w.hist[255u - ((key[r] >> lo) & 255u)], 1u);
+            }
+            uint32_t digit;
+            int cnt;
+            radix_pick(w, lane, digit, rem, cnt);
+            prefix |= (digit << lo) & wmask;
+            pmask |= wmask;
+            if (cnt == rem) { mode = SEL_WHOLE; break; }
+            if (cnt <= 64) {
+              // rank the bin's members (collected in ascending block order)
+              int base = 0;
+#pragma unroll
+              for (int r = 0; r < SEL_REG; ++r) {
+                if (r * 64 >= ncand) break;
+                const int j = r * 64 + lane;
+                const bool in = j < ncand && (key[r] & pmask) == prefix;
+                const uint64_t m = __ballot(in);
+                if (in) {
+                  const int p = base + __popcll(m & lanes_below(lane));
+                  w.mkey[p] = key[r];
+                  w.mj[p] = j;
+                }
+                base += __popcll(m);
               }
-              base += __popcll(m);
+              rank_members(w, lane, cnt, rem, cut_key, cut_j);
+              mode = SEL_CUT;
+              break;
             }
-            wave_lds_sync();
-            const uint32_t K = lane < cnt ? w.mkey[lane] : 0u;
-            const int J = lane < cnt ? w.mj[lane] : 0;
-            int rank = 0;
-            for (int m = 0; m < cnt; ++m) {
-              const uint32_t Km = rd_lane(K, m);
-              rank += (Km > K || (Km == K && m < lane)) ? 1 : 0;
-            }
-            const int src = __ffsll((unsigned long long)__ballot(lane < cnt && rank == rem - 1)) - 1;
-            cut_key = rd_lane(K, src);
-            cut_j = (int)rd_lane((uint32_t)J, src);
-            mode = SEL_CUT;
-            break;
+            if (lo == 0) break;                     // the whole key is decided: equal keys by index
+            top = lo - 1;
           }
-          if (lo == 0) break;                     // the whole key is decided: equal keys by index
-          top = lo - 1;
         }
-      }
-      // emit in ascending block order
-      if (g.topk > 1) {
         int eq_taken = 0;
 #pragma unroll
         for (int r = 0; r < SEL_REG; ++r) {
@@ -747,13 +858,68 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
             take = (valid && key[r] > prefix) || (eq && eq_rank < rem);
             eq_taken += __popcll(eqm);
           }
-          const uint64_t tm = __ballot(take);
-          if (take) out[pos + __popcll(tm & lanes_below(lane))] = kb0 + j;
-          pos += __popcll(tm);
+          emit(r, take);
         }
       }
     } else {
-      if (rem > 0) {
+      // rows too long for registers: the same bins, the row re-read for each
+      // step (it stays in cache), the radix steps over the whole key only
+      // when the cut bin holds more than 64 keys or the range is not finite
+      float fhi = -INFINITY, flo = INFINITY;
+      for (int j = lane; j < ncand; j += 64) {
+        const float sv = srow[j];
+        fhi = fmaxf(fhi, sv);
+        flo = fminf(flo, sv);
+      }
+      fhi = wave_fmax(fhi);
+      flo = wave_fmin(flo);
+      const float inv = 256.f / (fhi - flo);
+      auto bin_of = [&](float sv) __attribute__((always_inline)) {
+        return (uint32_t)min(255, max(0, (int)((fhi - sv) * inv)));
+      };
+      bool done = false;
+      if (fhi - flo <= 3.0e38f && inv <= 3.0e38f) {
+        hist_clear(w, lane);
+        for (int j = lane; j < ncand; j += 64) atomicAdd(&w.hist[bin_of(srow[j])], 1u);
+        uint32_t digit;
+        int cnt;
+        int brem = rem;
+        radix_pick(w, lane, digit, brem, cnt);
+        const uint32_t bstar = 255u - digit;
+        if (cnt == brem) {
+          for (int base = 0; base < ncand; base += 64) {
+            const int j = base + lane;
+            emit(base >> 6, j < ncand && bin_of(srow[j < ncand ? j : 0]) <= bstar);
+          }
+          done = true;
+        } else if (cnt <= 64) {
+          int nb = 0;
+          for (int base = 0; base < ncand; base += 64) {
+            const int j = base + lane;
+            const float sv = srow[j < ncand ? j : 0];
+            const bool in = j < ncand && bin_of(sv) == bstar;
+            const uint64_t m = __ballot(in);
+            if (in) {
+              const int p = nb + __popcll(m & lanes_below(lane));
+              w.mkey[p] = order_key(sv);
+              w.mj[p] = j;
+            }
+            nb += __popcll(m);
+          }
+          uint32_t cut_key;
+          int cut_j;
+          rank_members(w, lane, cnt, brem, cut_key, cut_j);
+          for (int base = 0; base < ncand; base += 64) {
+            const int j = base + lane;
+            const float sv = srow[j < ncand ? j : 0];
+            const uint32_t bn = bin_of(sv), kv = order_key(sv);
+            emit(base >> 6, j < ncand && (bn < bstar || (bn == bstar && (kv > cut_key || (kv == cut_key && j <= cut_j)))));
+          }
+          done = true;
+        }
+      }
+      if (!done) {
+        uint32_t prefix = 0, pmask = 0;
         for (int shift = 24; shift >= 0; shift -= 8) {
           hist_clear(w, lane);
           for (int j = lane; j < ncand; j += 64) {
@@ -766,21 +932,18 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
           prefix |= digit << shift;
           pmask |= 255u << shift;
         }
-      }
-      int eq_taken = 0;
-      for (int base = 0; base < ncand; base += 64) {
-        const int j = base + lane;
-        const uint32_t key = j < ncand ? order_key(srow[j]) : 0u;
-        const bool valid = j < ncand && rem > 0;
-        const bool gt = valid && key > prefix;
-        const bool eq = valid && key == prefix;
-        const uint64_t eqm = __ballot(eq);
-        const int eq_rank = eq_taken + __popcll(eqm & lanes_below(lane));
-        const bool take = gt || (eq && eq_rank < rem);
-        const uint64_t tm = __ballot(take);
-        if (take) out[pos + __popcll(tm & lanes_below(lane))] = kb0 + j;
-        pos += __popcll(tm);
-        eq_taken += __popcll(eqm);
+        int eq_taken = 0;
+        for (int base = 0; base < ncand; base += 64) {
+          const int j = base + lane;
+          const uint32_t key = j < ncand ? order_key(srow[j]) : 0u;
+          const bool valid = j < ncand;
+          const bool gt = valid && key > prefix;
+          const bool eq = valid && key == prefix;
+          const uint64_t eqm = __ballot(eq);
+          const int eq_rank = eq_taken + __popcll(eqm & lanes_below(lane));
+          emit(base >> 6, gt || (eq && eq_rank < rem));
+          eq_taken += __popcll(eqm);
+        }
       }
     }
   }
@@ -794,97 +957,215 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
 }
 
 // ---------------------------------------------------------------------------
-// inverted index: count -> exclusive scan -> scatter -> per-list sort
+// inverted index: counts -> exclusive scan -> emission, with no atomics
+// outside LDS.  The KV blocks of each document are cut into slabs of 256, and
+// the rows (query blocks) that can select a slab's blocks -- those whose
+// diagonal block is at or past the slab's first block -- into chunks of 256
+// consecutive rows.  A workgroup owns one (group, slab, chunk): it counts the
+// chunk's selections per block into a table, the scan turns the table into
+// k2q_ptr, and the emission places each row of the chunk, in ascending row
+// order, after the rows of earlier chunks.  Every list therefore comes out
+// ascending, and the result is the same on every run.
 // ---------------------------------------------------------------------------
 
-__global__ void k2q_count_kernel(const int32_t* __restrict__ q2k_idx,
-                                 const int32_t* __restrict__ q2k_cnt, int32_t* counts, Geo g) {
-  const int64_t n = (int64_t)g.Hkv * g.nqb * g.stride;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t rowi = e / g.stride;
-    const int slot = (int)(e % g.stride);
-    if (slot < q2k_cnt[rowi]) {
-      const int grp = (int)(rowi / g.nqb);
-      atomicAdd(&counts[(int64_t)grp * g.nkb + q2k_idx[e]], 1);
-    }
-  }
+struct SlabView {
+  int grp, slab, chunk, jlo, ncol, r0, r1, qb0;
+  uint32_t glo;                      // global id of the slab's first KV block
+};
+
+// Workgroup wg -> (group, slab, chunk); r0 >= r1 when the chunk lies past the
+// slab's rows.
+__device__ __forceinline__ SlabView slab_view(const Geo& g, int64_t wg) {
+  SlabView v;
+  v.chunk = (int)(wg % g.k2q_chunks);
+  const int64_t gs = wg / g.k2q_chunks;
+  v.grp = (int)(gs / g.nslab);
+  v.slab = (int)(gs % g.nslab);
+  const int b = find_segment<int32_t>(g.slab0, g.B, v.slab);
+  v.jlo = (v.slab - g.slab0[b]) * K2Q_SLAB;
+  const int L = g.cu[b + 1] - g.cu[b];
+  const int nk = (L + 127) >> 7;
+  v.ncol = min(K2Q_SLAB, nk - v.jlo);
+  const int nq = (L + g.Bq - 1) / g.Bq;
+  const int imin = (v.jlo * 128 + g.Bq - 1) / g.Bq;   // first row whose diagonal reaches the slab
+  v.r0 = imin + v.chunk * K2Q_CHUNK;
+  v.r1 = min(nq, v.r0 + K2Q_CHUNK);
+  v.qb0 = g.qb0[b];
+  v.glo = (uint32_t)(g.kb0[b] + v.jlo);
+  return v;
 }
 
-__global__ __launch_bounds__(256) void k2q_scan_kernel(const int32_t* __restrict__ counts,
-                                                       int32_t* __restrict__ k2q_ptr, Geo g) {
-  __shared__ int64_t sh[256];
-  const int grp = blockIdx.x;
-  int64_t carry = 0;
-  for (int base = 0; base < g.nkb + 1; base += 256) {
-    const int i = base + threadIdx.x;
-    const int64_t v = i < g.nkb ? counts[(int64_t)grp * g.nkb + i] : 0;
-    const int64_t e = block_exscan256(v, sh, carry);
-    if (i <= g.nkb) k2q_ptr[(int64_t)grp * (g.nkb + 1) + i] = (int32_t)e;
-  }
-}
-
-__global__ void k2q_scatter_kernel(const int32_t* __restrict__ q2k_idx,
-                                   const int32_t* __restrict__ q2k_cnt,
-                                   const int32_t* __restrict__ k2q_ptr, int32_t* cursor,
-                                   int32_t* __restrict__ k2q_idx, Geo g) {
-  const int64_t n = (int64_t)g.Hkv * g.nqb * g.stride;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t rowi = e / g.stride;
-    const int slot = (int)(e % g.stride);
-    if (slot < q2k_cnt[rowi]) {
-      const int grp = (int)(rowi / g.nqb);
-      const int QB = (int)(rowi % g.nqb);
-      const int KB = q2k_idx[e];
-      const int at = atomicAdd(&cursor[(int64_t)grp * g.nkb + KB], 1);
-      k2q_idx[(int64_t)grp * g.cap + k2q_ptr[(int64_t)grp * (g.nkb + 1) + KB] + at] = QB;
-    }
-  }
-}
-
-__global__ void k2q_tail_kernel(const int32_t* __restrict__ k2q_ptr, int32_t* __restrict__ k2q_idx,
-                                Geo g) {
-  const int64_t n = (int64_t)g.Hkv * g.cap;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int grp = (int)(e / g.cap);
-    const int64_t i = e % g.cap;
-    if (i >= k2q_ptr[(int64_t)grp * (g.nkb + 1) + g.nkb]) k2q_idx[e] = -1;
-  }
-}
-
-// Sort one inverted list ascending (bitonic, in LDS).  Lists hold distinct
-// query-block ids, so the sorted list is unique whatever order the scatter's
-// atomics produced.
-__global__ __launch_bounds__(256) void k2q_sort_kernel(const int32_t* __restrict__ k2q_ptr,
-                                                       int32_t* __restrict__ k2q_idx, Geo g) {
-  extern __shared__ int32_t sh[];
-  const int grp = blockIdx.x / g.nkb;
-  const int KB = blockIdx.x % g.nkb;
-  const int32_t* ptr = k2q_ptr + (int64_t)grp * (g.nkb + 1);
-  const int beg = ptr[KB];
-  const int len = ptr[KB + 1] - beg;
-  if (len <= 1) return;
-  int P = 1;
-  while (P < len) P <<= 1;
-  int32_t* seg = k2q_idx + (int64_t)grp * g.cap + beg;
-  for (int i = threadIdx.x; i < P; i += blockDim.x) sh[i] = i < len ? seg[i] : 0x7fffffff;
-  __syncthreads();
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const bool up = (i & k) == 0;
-          const int32_t a = sh[i], c = sh[ixj];
-          if ((a > c) == up) { sh[i] = c; sh[ixj] = a; }
-        }
+// Count, into cnt[c], the rows in [i0, i1) that selected block glo + c of
+// the slab (LDS adds; a row never holds a block twice).
+__device__ __forceinline__ void slab_count_rows(const Geo& g, const int32_t* rows0, const SlabView& v, int i0,
+                                                int i1, uint32_t* cnt, int lane) {
+  constexpr int U = 8;                              // rows in flight per wave
+  for (int I = i0; I < i1; I += U) {
+    int32_t e[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t* row = rows0 + (int64_t)(I + u) * g.stride;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = h * 64 + lane;
+        e[u][h] = (I + u < i1 && k < g.stride) ? row[k] : -1;
       }
-      __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t c = (uint32_t)e[u][h] - v.glo;
+        if (c < (uint32_t)K2Q_SLAB) atomicAdd(&cnt[c], 1u);
+      }
+    }
+    for (int k = 128 + lane; k < g.stride; k += 64) {   // rows longer than 128 entries
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (I + u >= i1) break;
+        const uint32_t c = (uint32_t)rows0[(int64_t)(I + u) * g.stride + k] - v.glo;
+        if (c < (uint32_t)K2Q_SLAB) atomicAdd(&cnt[c], 1u);
+      }
     }
   }
-  for (int i = threadIdx.x; i < len; i += blockDim.x) seg[i] = sh[i];
+}
+
+// table[((grp * nslab + slab) * k2q_chunks + chunk) * 64 + c] = selections of
+// the slab's block c by the chunk's rows.
+__global__ __launch_bounds__(256) void k2q_count_kernel(const int32_t* __restrict__ q2k_idx,
+                                                        int32_t* __restrict__ table, Geo g) {
+  __shared__ uint32_t cnt[K2Q_SLAB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const SlabView v = slab_view(g, blockIdx.x);
+  for (int c = tid; c < K2Q_SLAB; c += 256) cnt[c] = 0u;
+  __syncthreads();
+  const int32_t* rows0 = q2k_idx + ((int64_t)v.grp * g.nqb + v.qb0) * g.stride;
+  const int w0 = v.r0 + wave * (K2Q_CHUNK / 4);
+  slab_count_rows(g, rows0, v, w0, min(v.r1, w0 + K2Q_CHUNK / 4), cnt, lane);
+  __syncthreads();
+  for (int c = tid; c < K2Q_SLAB; c += 256) table[(int64_t)blockIdx.x * K2Q_SLAB + c] = (int32_t)cnt[c];
+}
+
+// Each KV block's count: the sum of its chunks' counts (one thread per block).
+__global__ __launch_bounds__(256) void k2q_total_kernel(const int32_t* __restrict__ table,
+                                                        int32_t* __restrict__ totals, Geo g) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)g.Hkv * g.nkb) return;
+  const int grp = (int)(i / g.nkb);
+  const int KB = (int)(i % g.nkb);
+  const int b = g.kdoc[KB];
+  const int J = KB - g.kb0[b];
+  const int slab = g.slab0[b] + J / K2Q_SLAB;
+  const int32_t* tc = table + ((int64_t)grp * g.nslab + slab) * g.k2q_chunks * K2Q_SLAB + (J % K2Q_SLAB);
+  int32_t c = 0;
+  for (int ch = 0; ch < g.k2q_chunks; ++ch) c += tc[ch * K2Q_SLAB];
+  totals[i] = c;
+}
+
+// Exclusive scan of one group's totals into k2q_ptr (nkb + 1 entries), one
+// workgroup of 1024 threads per group: every thread sums a contiguous run,
+// the run sums are scanned by DPP within waves and then over the 16 wave
+// totals, and each run is written out; -1 fills the unused capacity.
+__global__ __launch_bounds__(1024) void k2q_scan_kernel(const int32_t* __restrict__ totals,
+                                                        int32_t* __restrict__ k2q_ptr,
+                                                        int32_t* __restrict__ k2q_idx, Geo g) {
+  __shared__ uint32_t wsum[16];
+  __shared__ uint32_t total;
+  const int grp = blockIdx.x;
+  const int n = g.nkb;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int per = (n + 1 + 1023) / 1024;
+  const int lo = t * per, hi = min(lo + per, n);
+  const int32_t* c = totals + (int64_t)grp * n;
+  uint32_t local = 0;
+  for (int i = lo; i < hi; ++i) local += (uint32_t)c[i];
+  const uint32_t incl = wave_incl_sum(local, lane);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int v = 0; v < wave; ++v) before += wsum[v];
+  uint32_t run = before + incl - local;
+  int32_t* p = k2q_ptr + (int64_t)grp * (n + 1);
+  for (int i = lo; i < min(lo + per, n + 1); ++i) {
+    p[i] = (int32_t)run;
+    if (i == n) total = run;
+    if (i < n) run += (uint32_t)c[i];
+  }
+  __syncthreads();
+  int32_t* dst = k2q_idx + (int64_t)grp * g.cap;
+  for (int64_t i = (int64_t)total + t; i < g.cap; i += 1024) dst[i] = -1;
+}
+
+// Emission for one (group, slab, chunk): wave w owns rows [r0 + 64 w, r0 +
+// 64 w + 64); its place in each block's list starts after k2q_ptr, the earlier
+// chunks (from the table) and the earlier waves (counted again here), and the
+// wave walks its rows in ascending order, taking the next place of every slab
+// block the row selected (an LDS add with return: one wave owns each counter).
+__global__ __launch_bounds__(256) void k2q_emit_kernel(const int32_t* __restrict__ q2k_idx,
+                                                       const int32_t* __restrict__ table,
+                                                       const int32_t* __restrict__ k2q_ptr,
+                                                       int32_t* __restrict__ k2q_idx, Geo g) {
+  __shared__ uint32_t part[4][K2Q_SLAB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const SlabView v = slab_view(g, blockIdx.x);
+  if (v.r0 >= v.r1) return;                        // uniform over the workgroup
+  const int w0 = v.r0 + wave * (K2Q_CHUNK / 4), w1 = min(v.r1, w0 + K2Q_CHUNK / 4);
+#pragma unroll
+  for (int m = 0; m < K2Q_SLAB / 64; ++m) part[wave][m * 64 + lane] = 0u;
+  __syncthreads();
+  const int32_t* rows0 = q2k_idx + ((int64_t)v.grp * g.nqb + v.qb0) * g.stride;
+  slab_count_rows(g, rows0, v, w0, w1, part[wave], lane);
+  __syncthreads();
+  uint32_t start[K2Q_SLAB / 64];
+#pragma unroll
+  for (int m = 0; m < K2Q_SLAB / 64; ++m) {
+    const int c = m * 64 + lane;
+    start[m] = 0u;
+    if (c < v.ncol) {
+      uint32_t st = (uint32_t)k2q_ptr[(int64_t)v.grp * (g.nkb + 1) + v.glo + c];
+      const int32_t* tc = table + ((int64_t)blockIdx.x - v.chunk) * K2Q_SLAB + c;
+      for (int ch = 0; ch < v.chunk; ++ch) st += (uint32_t)tc[ch * K2Q_SLAB];
+      for (int w = 0; w < wave; ++w) st += part[w][c];
+      start[m] = st;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < K2Q_SLAB / 64; ++m) part[wave][m * 64 + lane] = start[m];   // the wave's next places
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  int32_t* dst = k2q_idx + (int64_t)v.grp * g.cap;
+  constexpr int U = 8;
+  for (int I = w0; I < w1; I += U) {
+    int32_t e[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t* row = rows0 + (int64_t)(I + u) * g.stride;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = h * 64 + lane;
+        e[u][h] = (I + u < w1 && k < g.stride) ? row[k] : -1;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t c = (uint32_t)e[u][h] - v.glo;
+        if (c < (uint32_t)K2Q_SLAB) dst[atomicAdd(&part[wave][c], 1u)] = v.qb0 + I + u;
+      }
+    }
+    for (int k = 128 + lane; k < g.stride; k += 64) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (I + u >= w1) break;
+        const uint32_t c = (uint32_t)rows0[(int64_t)(I + u) * g.stride + k] - v.glo;
+        if (c < (uint32_t)K2Q_SLAB) dst[atomicAdd(&part[wave][c], 1u)] = v.qb0 + I + u;
+      }
+    }
+  }
 }
 
 static int grid_for(int64_t n, int threads) {
@@ -904,37 +1185,25 @@ hipError_t launch_select(const Geo& g, const float* scores, int32_t* q2k_idx, in
                        q2k_idx, q2k_cnt, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int64_t nc = (int64_t)g.Hkv * g.nkb;
-  if ((e = fill_i32(w.counts, 0, nc, s)) != hipSuccess) return e;
-  if ((e = fill_i32(w.cursor, 0, nc, s)) != hipSuccess) return e;
-  const int64_t ne = rows * g.stride;
-  if (ne > 0) {
+  const int64_t nwg = (int64_t)g.Hkv * g.nslab * g.k2q_chunks;
+  if (nwg > 0) {
     { ProfScope _ps("k2q_count", s);
-    hipLaunchKernelGGL(k2q_count_kernel, dim3(grid_for(ne, 256)), dim3(256), 0, s, q2k_idx,
-                       q2k_cnt, w.counts, g); }
+    hipLaunchKernelGGL(k2q_count_kernel, dim3((unsigned)nwg), dim3(256), 0, s, q2k_idx, w.counts, g); }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t nc = (int64_t)g.Hkv * g.nkb;
+  if (nc > 0) {
+    { ProfScope _ps("k2q_scan", s);
+    hipLaunchKernelGGL(k2q_total_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, w.counts,
+                       w.totals, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   { ProfScope _ps("k2q_scan", s);
-  hipLaunchKernelGGL(k2q_scan_kernel, dim3(g.Hkv), dim3(256), 0, s, w.counts, k2q_ptr, g); }
+  hipLaunchKernelGGL(k2q_scan_kernel, dim3(g.Hkv), dim3(1024), 0, s, w.totals, k2q_ptr, k2q_idx, g); }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ne > 0) {
-    { ProfScope _ps("k2q_scatter", s);
-    hipLaunchKernelGGL(k2q_scatter_kernel, dim3(grid_for(ne, 256)), dim3(256), 0, s, q2k_idx,
-                       q2k_cnt, k2q_ptr, w.cursor, k2q_idx, g); }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  const int64_t ncap = (int64_t)g.Hkv * g.cap;
-  if (ncap > 0) {
-    { ProfScope _ps("k2q_tail", s);
-    hipLaunchKernelGGL(k2q_tail_kernel, dim3(grid_for(ncap, 256)), dim3(256), 0, s, k2q_ptr,
-                       k2q_idx, g); }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (nc > 0) {
-    int P = 1;
-    while (P < g.max_nq) P <<= 1;
-    { ProfScope _ps("k2q_sort", s);
-    hipLaunchKernelGGL(k2q_sort_kernel, dim3((unsigned)nc), dim3(256), (size_t)P * 4, s, k2q_ptr,
+  if (nwg > 0) {
+    { ProfScope _ps("k2q_emit", s);
+    hipLaunchKernelGGL(k2q_emit_kernel, dim3((unsigned)nwg), dim3(256), 0, s, q2k_idx, w.counts, k2q_ptr,
                        k2q_idx, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -954,10 +1223,9 @@ int select_kernels(KernelEntry* out, int max) {
       {"proxy_scores<f32,dp32,bq128>", (const void*)proxy_scores_kernel<float, 32, 128>, 256, 0},
       {"select", (const void*)select_kernel, 256, 0},
       {"k2q_count", (const void*)k2q_count_kernel, 256, 0},
-      {"k2q_scan", (const void*)k2q_scan_kernel, 256, 0},
-      {"k2q_scatter", (const void*)k2q_scatter_kernel, 256, 0},
-      {"k2q_tail", (const void*)k2q_tail_kernel, 256, 0},
-      {"k2q_sort", (const void*)k2q_sort_kernel, 256, 4096 * 4},
+      {"k2q_total", (const void*)k2q_total_kernel, 256, 0},
+      {"k2q_scan", (const void*)k2q_scan_kernel, 1024, 0},
+      {"k2q_emit", (const void*)k2q_emit_kernel, 256, 0},
   };
   int n = (int)(sizeof(all) / sizeof(all[0]));
   for (int i = 0; i < n && i < max; ++i) out[i] = all[i];

@@ -161,13 +161,13 @@ msa_status msa_select_blocks(const msa_config* cfg, const msa_varlen* vl, const 
  * and inverted-index counters live in a static device array of
  * msa_select_blocks_noalloc_max_bytes() bytes (8 MiB) that the library holds
  * on every GPU it runs on until the process ends; this call allocates
- * nothing.  Needed: about 0.6 bytes per token with 8 proxy heads (the tables
- * and counters of the packing), so packings up to about 14M tokens fit; a
- * larger one returns MSA_ERR_WORKSPACE before anything is launched.  Every
+ * nothing.  Needed: about 0.35 bytes per token with 8 proxy heads (the tables
+ * and per-block counts of the packing), so packings up to about 24M tokens
+ * fit; a larger one returns MSA_ERR_WORKSPACE before anything is launched.  Every
  * call on a GPU shares that GPU's array: calls that overlap on one GPU (on
  * different streams, or from different threads) race and must be ordered by
- * the caller.  The counters are cleared by the call itself (with kernels, no
- * memset), so nothing has to be zeroed between calls.
+ * the caller.  Every count is written by the call itself (no memset), so
+ * nothing has to be zeroed between calls.
  */
 msa_status msa_select_blocks_noalloc(const msa_config* cfg, const msa_varlen* vl,
                                      const float* block_scores, int32_t* q2k_idx, int32_t* q2k_cnt,

@@ -168,8 +168,8 @@ def test_select_noalloc_rejects_packings_beyond_its_scratch():
     (so this runs without a GPU: the device pointers are never used)."""
     lib = msa.load()
     cap = lib.msa_select_blocks_noalloc_max_bytes()
-    assert cap == 8 << 20
-    seqlens = [1 << 21] * 8                     # 16M tokens: 2^21 per document
+    assert cap == 16 << 20
+    seqlens = [1 << 21] * 16                    # 32M tokens: 2^21 per document
     cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
     cfg = msa.Config(32, 8, 128, 64, 128, 64, 0, dtype="bf16").to_c()
     fake = 1 << 20                              # aligned, never dereferenced
