@@ -159,11 +159,15 @@ msa_status msa_select_blocks(const msa_config* cfg, const msa_varlen* vl, const 
  * that forbid hipMalloc).  Same arguments as msa_select_blocks minus the
  * workspace, same outputs bit for bit, same kernels.  The per-document tables
  * and inverted-index counters live in a static device array of
- * msa_select_blocks_noalloc_max_bytes() bytes (8 MiB) that the library holds
+ * msa_select_blocks_noalloc_max_bytes() bytes (16 MiB) that the library holds
  * on every GPU it runs on until the process ends; this call allocates
- * nothing.  Needed: about 0.35 bytes per token with 8 proxy heads (the tables
- * and per-block counts of the packing), so packings up to about 24M tokens
- * fit; a larger one returns MSA_ERR_WORKSPACE before anything is launched.  Every
+ * nothing.  Needed: the per-document tables (about 0.1 byte per token) and the
+ * inverted-index counts, 4 bytes per (proxy head, KV block, 256 query blocks
+ * of the longest document).  That is 2.5 MiB for 1M tokens packed as 14
+ * documents of at most 207k tokens, about 2 bytes per token for documents of
+ * 256k tokens (some 7M tokens fit), and 8.3 MiB for one 1M-token document (the
+ * longest single document that fits is about 1.45M tokens, 8 proxy heads); a
+ * larger problem returns MSA_ERR_WORKSPACE before anything is launched.  Every
  * call on a GPU shares that GPU's array: calls that overlap on one GPU (on
  * different streams, or from different threads) race and must be ordered by
  * the caller.  Every count is written by the call itself (no memset), so
