@@ -93,7 +93,9 @@ __global__ __launch_bounds__(256) void dq_kernel(
   const int kb0 = g.kb0[b];
   const int diag = (I * g.Bq) >> 7;
   const int qbase = I * g.Bq + chunk * 32;
-  const int64_t rowi = (int64_t)grp * g.nqb + QB;
+  const int pg = proxy_head(g, grp);                 // the proxy head this group reads
+  const float qw = proxy_qweight(g, grp);            // weight of its proxy-softmax term
+  const int64_t rowi = (int64_t)pg * g.nqb + QB;
   const int cnt = q2k_cnt[rowi];
   const int32_t* sel = q2k_idx + rowi * g.stride;
   const int qpos = qbase + col;
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
       const int rfirst = (wave * C::NPCOPY + j) * C::PROWS_PER_COPY;
       const int r = rfirst + lane / TP::CPR, p = lane % TP::CPR;
       const int key = key0 + r < L ? key0 + r : L - 1;
-      const int64_t off = ((int64_t)(t0 + key) * g.Hkv + grp) * DP + swz<TP::CPR>(r, p) * C::EPC;
+      const int64_t off = ((int64_t)(t0 + key) * g.Hp + pg) * DP + swz<TP::CPR>(r, p) * C::EPC;
       dma16(kp + off, base + (2 * C::KS + rfirst * DP) * (int)sizeof(T));
     }
   };
@@ -146,11 +148,11 @@ __global__ __launch_bounds__(256) void dq_kernel(
       for (int j = 0; j < 8; ++j) part = fmaf(to_f32(dOf[ks][j]), to_f32(of[j]), part);
     }
     dl = part + __shfl_xor(part, 32, 64);
-    const T* sp = qp + (tq * g.Hkv + grp) * DP + hi * 8;
+    const T* sp = qp + (tq * g.Hp + pg) * DP + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < DP / 16; ++ks) QPf[ks] = ld8(sp + ks * 16);
     lse2 = lse[(int64_t)h * g.T + tq] * LOG2E;
-    lsep2 = lse_p[(int64_t)grp * g.T + tq] * LOG2E;
+    lsep2 = lse_p[(int64_t)pg * g.T + tq] * LOG2E;
     // per-query values the KV-major pass reads: D and both LSEs in log2 units
     if (hi == 0 && qpos < L) {
       delta[(int64_t)h * g.T + tq] = -dl;             // stored negated: -rowsum(dO * O)
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
     });
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      if (((s * 2 + kt) % g.G) != hl) continue;
+      if (((s * 2 + kt) % g.G) != hl || qw == 0.f) continue;
       f32x16 Y = zero16();
 #pragma unroll
       for (int ks = 0; ks < DP / 16; ++ks) mma(Y, TP::row8(KPs, kt * 32 + col, ks * 16 + hi * 8), QPf[ks]);
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
 #pragma unroll
   for (int dt = 0; dt < DP / 32; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Cd[dt][i] = Cq[dt][i] - Cp[dt][i] * invG;
+    for (int i = 0; i < 16; ++i) Cd[dt][i] = (qw == 1.f ? Cq[dt][i] : qw * Cq[dt][i]) - Cp[dt][i] * invG;
 
   // dQ out (fp32)
   if (active && qpos < L) {
@@ -471,8 +473,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
   const int kpos = J * 128 + wave * 32 + col;               // this lane's key (B-fragment column)
   const int krow = kpos < L ? kpos : L - 1;
   const int64_t tk = t0 + krow;
-  const int32_t* ptr = k2q_ptr + (int64_t)grp * (g.nkb + 1);
-  const int32_t* lst = k2q_idx + (int64_t)grp * g.cap + ptr[KB];
+  const int pg = proxy_head(g, grp);                        // the proxy head this group reads
+  const float qw = proxy_qweight(g, grp);                   // weight of its proxy-softmax term
+  const int32_t* ptr = k2q_ptr + (int64_t)pg * (g.nkb + 1);
+  const int32_t* lst = k2q_idx + (int64_t)pg * g.cap + ptr[KB];
   const int len = ptr[KB + 1] - ptr[KB];
   const int nch = g.Bq / 32;
   const float invG = 1.f / (float)G;
@@ -493,7 +497,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
     const int rfirst = wave * 32 + j * C::PROWS_PER_COPY;
     const int r = rfirst + lane / TP::CPR, p = lane % TP::CPR;
     const int key = J * 128 + r < L ? J * 128 + r : L - 1;
-    dma16(kp + ((int64_t)(t0 + key) * g.Hkv + grp) * DP + swz<TP::CPR>(r, p) * C::EPC,
+    dma16(kp + ((int64_t)(t0 + key) * g.Hp + pg) * DP + swz<TP::CPR>(r, p) * C::EPC,
           lds_offset(smem_raw) + C::KP_OFF + rfirst * DP * (int)sizeof(T));
   }
 
@@ -532,7 +536,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
         const int r = rfirst + lane / TP::CPR;
         const int p = lane % TP::CPR;
         const int pos = row0 + r < L ? row0 + r : L - 1;
-        const int64_t off = ((int64_t)(t0 + pos) * g.Hkv + grp) * DP + swz<TP::CPR>(r, p) * C::EPC;
+        const int64_t off = ((int64_t)(t0 + pos) * g.Hp + pg) * DP + swz<TP::CPR>(r, p) * C::EPC;
         dma16(qp + off, base + (2 * C::QS + rfirst * DP) * (int)sizeof(T));
       }
     }
@@ -637,34 +641,47 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
     }
   };
+  // dkp += dY^T qp over a chunk: dY / (lam s_p) = qw Q - T / G (only -T / G
+  // where qw = 0, with no proxy scores taken)
   auto proxy_part = [&](const unsigned char* base, int lo, int hi_, bool masked) __attribute__((always_inline)) {
     const T* Ps = reinterpret_cast<const T*>(base) + 2 * C::QS;
     const float* fl = reinterpret_cast<const float*>(base + C::FL_OFF);
     __builtin_amdgcn_sched_barrier(0);
-    frag_t<T> ya[DP / 16], yb[DP / 16], bp[2][DP / 32];
-    float lp[2][8];
+    frag_t<T> bp[2][DP / 32];
 #pragma unroll
-    for (int ks = 0; ks < DP / 16; ++ks) {
-      ya[ks] = TP::row8(Ps, col, ks * 16 + hi * 8);
-      yb[ks] = TP::row8(KPs, wave * 32 + col, ks * 16 + hi * 8);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      rows8(fl + 2 * C::QC, kk, lp[kk]);
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int dt = 0; dt < DP / 32; ++dt) bp[kk][dt] = TP::col(Ps, kk * 16, dt * 32, lane);
-    }
     f32x16 Y = zero16();
+    if (qw != 0.f) {
+      frag_t<T> ya[DP / 16], yb[DP / 16];
+      float lp[2][8];
 #pragma unroll
-    for (int ks = 0; ks < DP / 16; ++ks) mma(Y, ya[ks], yb[ks]);
+      for (int ks = 0; ks < DP / 16; ++ks) {
+        ya[ks] = TP::row8(Ps, col, ks * 16 + hi * 8);
+        yb[ks] = TP::row8(KPs, wave * 32 + col, ks * 16 + hi * 8);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) rows8(fl + 2 * C::QC, kk, lp[kk]);
+#pragma unroll
+      for (int ks = 0; ks < DP / 16; ++ks) mma(Y, ya[ks], yb[ks]);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = kk * 8 + j;
+          float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], g.pscale_log2, -lp[kk][j]));
+          if (masked) qv = (acc_row(i, lane) >= lo && acc_row(i, lane) < hi_) ? qv : 0.f;
+          Y[i] = qv * qw;
+        }
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = kk * 8 + j;
-        float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], g.pscale_log2, -lp[kk][j]));
-        if (masked) qv = (acc_row(i, lane) >= lo && acc_row(i, lane) < hi_) ? qv : 0.f;
-        Y[i] = fmaf(-invG, Tacc[i], qv);                     // dY / (lam * s_p)
+        Y[i] = fmaf(-invG, Tacc[i], Y[i]);                   // dY / (lam * s_p)
       }
       const frag_t<T> ay = acc_frag<T>(Y, kk);
 #pragma unroll
@@ -841,20 +858,31 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
                                float* dkp, const Work& w, hipStream_t s) {
   typedef DqCfg<T, D, DP> CQ;
   typedef KvCfg<T, D, DP> CK;
+  // bf16, d = 128, dp = 64: the query-major pass is dq128 for every group
+  // size and the KV-major pass the two-role kernel for 4 and 8 heads per
+  // group, so the generic kernels are built for the other shapes (and, here,
+  // the KV-major pass of 1 and 2 heads per group) only
+  constexpr bool FAST = std::is_same<T, bf16>::value && D == 128 && DP == 64;
   static LdsLimitOnce lds_limit;
   {
-    const hipError_t e = lds_limit.ensure({{(const void*)dq_kernel<T, D, DP>, CQ::LDS_BYTES},
-                                           {(const void*)dkdv_kernel<T, D, DP, 1>, CK::LDS_BYTES},
-                                           {(const void*)dkdv_kernel<T, D, DP, 2>, CK::LDS_BYTES},
-                                           {(const void*)dkdv_kernel<T, D, DP, 4>, CK::LDS_BYTES},
-                                           {(const void*)dkdv_kernel<T, D, DP, 8>, CK::LDS_BYTES}});
+    hipError_t e;
+    if constexpr (FAST) {
+      e = lds_limit.ensure({{(const void*)dkdv_kernel<T, D, DP, 1>, CK::LDS_BYTES},
+                            {(const void*)dkdv_kernel<T, D, DP, 2>, CK::LDS_BYTES}});
+    } else {
+      e = lds_limit.ensure({{(const void*)dq_kernel<T, D, DP>, CQ::LDS_BYTES},
+                            {(const void*)dkdv_kernel<T, D, DP, 1>, CK::LDS_BYTES},
+                            {(const void*)dkdv_kernel<T, D, DP, 2>, CK::LDS_BYTES},
+                            {(const void*)dkdv_kernel<T, D, DP, 4>, CK::LDS_BYTES},
+                            {(const void*)dkdv_kernel<T, D, DP, 8>, CK::LDS_BYTES}});
+    }
     if (e != hipSuccess) return e;
   }
   hipError_t e;
   const int NU = g.G * (g.Bq / 32);
   const int64_t nq = (int64_t)g.Hkv * g.nqb * ((NU + 3) / 4);
-  const bool q8 = std::is_same<T, bf16>::value && D == 128 && DP == 64 && dq128_supported(g);
-  if (q8) {
+  if constexpr (FAST) {
+    if (!dq128_supported(g)) return hipErrorInvalidValue;
     { ProfScope _ps("bwd_dq", s);
     e = launch_dq128(g, q, k, v, qp, kp, o, lse, lse_p, dout, w.delta, w.lse2, w.lsep2, q2k_idx,
                      q2k_cnt, dq, dqp, s); }
@@ -867,14 +895,14 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
                        w.cpart, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (!q8 && g.G > 4 && g.T > 0) {
+  if (!FAST && g.G > 4 && g.T > 0) {
     { ProfScope _ps("bwd_dqp_reduce", s);
     hipLaunchKernelGGL((dqp_reduce_kernel<DP>), dim3(grid_for_b((int64_t)g.T * g.Hkv * DP, 256)),
                        dim3(256), 0, s, w.cpart, dqp, g); }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t nk = (int64_t)g.Hkv * g.nkb;
-  if (nk > 0 && std::is_same<T, bf16>::value && D == 128 && DP == 64 && dkdv128_supported(g)) {
+  if (nk > 0 && FAST && dkdv128_supported(g)) {
     { ProfScope _ps("bwd_dkdv", s);
     e = launch_dkdv128(g, q, k, v, qp, kp, w.lse2, w.lsep2, dout, w.delta, k2q_ptr, k2q_idx, dk, dv,
                        dkp, s); }
@@ -885,11 +913,19 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
     hipLaunchKernelGGL((dkdv_kernel<T, D, DP, GG>), dim3((unsigned)nk), dim3(256), CK::LDS_BYTES, s, \
                        (const T*)q, (const T*)k, (const T*)v, (const T*)qp, (const T*)kp, w.lse2,      \
                        w.lsep2, (const T*)dout, w.delta, k2q_ptr, k2q_idx, dk, dv, dkp, g)
-    switch (g.G) {
-      case 1: MSA_LAUNCH_DKDV(1); break;
-      case 2: MSA_LAUNCH_DKDV(2); break;
-      case 4: MSA_LAUNCH_DKDV(4); break;
-      default: MSA_LAUNCH_DKDV(8); break;
+    if constexpr (FAST) {
+      switch (g.G) {
+        case 1: MSA_LAUNCH_DKDV(1); break;
+        case 2: MSA_LAUNCH_DKDV(2); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      switch (g.G) {
+        case 1: MSA_LAUNCH_DKDV(1); break;
+        case 2: MSA_LAUNCH_DKDV(2); break;
+        case 4: MSA_LAUNCH_DKDV(4); break;
+        default: MSA_LAUNCH_DKDV(8); break;
+      }
     }
 #undef MSA_LAUNCH_DKDV
     }
@@ -920,11 +956,8 @@ hipError_t launch_bwd(const Geo& g, int is_bf16, const void* q, const void* k, c
 namespace msa {
 int bwd_kernels(KernelEntry* out, int max) {
   const KernelEntry all[] = {
-      {"bwd_dq<bf16,d128,dp64>", (const void*)dq_kernel<bf16, 128, 64>, 256, DqCfg<bf16, 128, 64>::LDS_BYTES},
       {"bwd_dkdv<bf16,d128,dp64,g1>", (const void*)dkdv_kernel<bf16, 128, 64, 1>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
       {"bwd_dkdv<bf16,d128,dp64,g2>", (const void*)dkdv_kernel<bf16, 128, 64, 2>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
-      {"bwd_dkdv<bf16,d128,dp64,g4>", (const void*)dkdv_kernel<bf16, 128, 64, 4>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
-      {"bwd_dkdv<bf16,d128,dp64,g8>", (const void*)dkdv_kernel<bf16, 128, 64, 8>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
       {"bwd_dq<bf16,d64,dp32>", (const void*)dq_kernel<bf16, 64, 32>, 256, DqCfg<bf16, 64, 32>::LDS_BYTES},
       {"bwd_dkdv<bf16,d64,dp32,g1>", (const void*)dkdv_kernel<bf16, 64, 32, 1>, 256, KvCfg<bf16, 64, 32>::LDS_BYTES},
       {"bwd_dkdv<bf16,d64,dp32,g2>", (const void*)dkdv_kernel<bf16, 64, 32, 2>, 256, KvCfg<bf16, 64, 32>::LDS_BYTES},

@@ -121,8 +121,9 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
   const int L = g.cu[b + 1] - t0;
   const int qb0 = g.qb0[b];
   const int kpos = J * 128 + kg * 32 + col;               // this lane's key (fragment column)
-  const int32_t* ptr = k2q_ptr + (int64_t)grp * (g.nkb + 1);
-  const int32_t* lst = k2q_idx + (int64_t)grp * g.cap + ptr[KB];
+  const int pg = proxy_head(g, grp);                      // the proxy head this group reads
+  const int32_t* ptr = k2q_ptr + (int64_t)pg * (g.nkb + 1);
+  const int32_t* lst = k2q_idx + (int64_t)pg * g.cap + ptr[KB];
   const int len = ptr[KB + 1] - ptr[KB];
   const int nch = g.Bq / 32;
   const int nst = len * nch * G;
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
     {
       const bf16* sk = k + (tk * g.Hkv + grp) * KD + hi * 8;
       const bf16* sv = v + (tk * g.Hkv + grp) * KD + hi * 8;
-      const bf16* sp = kp + (tk * g.Hkv + grp) * KDP + hi * 8;
+      const bf16* sp = kp + (tk * g.Hp + pg) * KDP + hi * 8;
 #pragma unroll
       for (int ks = 0; ks < KD / 16; ++ks) { Kf[ks] = ld8(sk + ks * 16); Vf[ks] = ld8(sv + ks * 16); }
 #pragma unroll
@@ -173,6 +174,7 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
     f32x16 Tacc = zero16();
     const float sl2 = g.scale_log2, psl2 = g.pscale_log2;
     const float invG = 1.f / (float)G;
+    const float qw = proxy_qweight(g, grp);                // weight of the proxy-softmax term
     const uint32_t mw = (uint32_t)(L - kpos);
     f32x16 S[2], dP[2];                                    // [stage parity]
     // S, dP of stage t (16 products, operand reads LOOK ahead) into S[PAR],
@@ -252,32 +254,55 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
       else run(std::false_type());
 
       if (c_hl == G - 1) {
-        // proxy term of the chunk: Y = qp kp^T, dY / (lam s_p) = Q - T / G
-        const uint32_t pb = bP + c_qo;
-        f32x16 Y = zero16();
-        static_for<KDP / 16>([&](auto ksc) __attribute__((always_inline)) {
-          constexpr int ks = decltype(ksc)::value;
-          Y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld8<0>(xr<(uint32_t)(ks << 5)>(pb)), KPf[ks], Y, 0, 0, 0);
-        });
-        // (the causal / document mask only where the chunk's stages are masked)
-        auto proxy_dy = [&](auto masked_c) __attribute__((always_inline)) {
+        // proxy term of the chunk: Y = qp kp^T, dY / (lam s_p) = qw Q - T / G
+        // (only -T / G where qw = 0)
+        // Q_MODE: 0 no proxy-softmax term (qw = 0), 1 weight 1, 2 weight qw
+        auto proxy_dy = [&](auto masked_c, auto q_mode_c) __attribute__((always_inline)) {
           constexpr bool MASKED = decltype(masked_c)::value;
+          constexpr int Q_MODE = decltype(q_mode_c)::value;
+          f32x16 Y;
+          if constexpr (Q_MODE != 0) {
+            const uint32_t pb = bP + c_qo;
+            Y = zero16();
+            static_for<KDP / 16>([&](auto ksc) __attribute__((always_inline)) {
+              constexpr int ks = decltype(ksc)::value;
+              Y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld8<0>(xr<(uint32_t)(ks << 5)>(pb)), KPf[ks], Y, 0, 0, 0);
+            });
+          }
           static_for<2>([&](auto hc) __attribute__((always_inline)) {
             constexpr int h8 = decltype(hc)::value;
-            const f32x4 l0 = lds_f4<2 * FL_VEC + (2 * h8) * 32>(fb), l1 = lds_f4<2 * FL_VEC + (2 * h8 + 1) * 32>(fb);
             bf16x8 ay;
-            static_for<8>([&](auto ec) __attribute__((always_inline)) {
-              constexpr int e = decltype(ec)::value, i = h8 * 8 + e;
-              const float lpv = e < 4 ? l0[e & 3] : l1[e & 3];
-              float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], psl2, -lpv));
-              if constexpr (MASKED) qv = keep_if<(uint32_t)(((i >> 2) << 3) + (i & 3))>(qv, mx, mw);
-              ay[e] = (bf16)fmaf(-invG, Tacc[i], qv);
-            });
+            if constexpr (Q_MODE != 0) {
+              const f32x4 l0 = lds_f4<2 * FL_VEC + (2 * h8) * 32>(fb), l1 = lds_f4<2 * FL_VEC + (2 * h8 + 1) * 32>(fb);
+              static_for<8>([&](auto ec) __attribute__((always_inline)) {
+                constexpr int e = decltype(ec)::value, i = h8 * 8 + e;
+                const float lpv = e < 4 ? l0[e & 3] : l1[e & 3];
+                float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], psl2, -lpv));
+                if constexpr (MASKED) qv = keep_if<(uint32_t)(((i >> 2) << 3) + (i & 3))>(qv, mx, mw);
+                if constexpr (Q_MODE == 2) qv *= qw;
+                ay[e] = (bf16)fmaf(-invG, Tacc[i], qv);
+              });
+            } else {
+              static_for<8>([&](auto ec) __attribute__((always_inline)) {
+                constexpr int e = decltype(ec)::value, i = h8 * 8 + e;
+                ay[e] = (bf16)(-invG * Tacc[i]);
+              });
+            }
             lds_st16(dy_lane + h8 * 1024, ay);
           });
         };
-        if (masked) proxy_dy(std::true_type());
-        else proxy_dy(std::false_type());
+        using Q0 = std::integral_constant<int, 0>;
+        using Q1 = std::integral_constant<int, 1>;
+        using Q2 = std::integral_constant<int, 2>;
+        if (qw == 1.f) {
+          if (masked) proxy_dy(std::true_type(), Q1());
+          else proxy_dy(std::false_type(), Q1());
+        } else if (qw != 0.f) {
+          if (masked) proxy_dy(std::true_type(), Q2());
+          else proxy_dy(std::false_type(), Q2());
+        } else {
+          proxy_dy(std::false_type(), Q0());
+        }
         Tacc = zero16();
         c_hl = 0;
         c_qo ^= QP_TILE;
@@ -309,7 +334,7 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
     // barrier), and after it stage s + 4 refills the slot of stage s - 2,
     // which this wave finished before the barrier.
     const uint32_t rs_q = (uint32_t)g.Hq * KD * 2;
-    const uint32_t rs_p = (uint32_t)g.Hkv * KDP * 2;
+    const uint32_t rs_p = (uint32_t)g.Hp * KDP * 2;
     uint32_t voQ[2], ldQ[2];
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
@@ -330,7 +355,7 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
     const uint32_t ldD = lb + WS_DUMMY + kg * 256;
     const bf16* qh = q + (int64_t)grp * G * KD;
     const bf16* dh = dout + (int64_t)grp * G * KD;
-    const bf16* qpg = qp + (int64_t)grp * KDP;
+    const bf16* qpg = qp + (int64_t)pg * KDP;
     const float* fw = kg == 0 ? lse2 + (int64_t)grp * G * g.T
                     : kg == 1 ? delta + (int64_t)grp * G * g.T
                     : lsep2 + (int64_t)grp * g.T;
@@ -355,7 +380,7 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
       const uint32_t rows = rows_of(tr, live);
       i_qa = (const char*)(qh + (int64_t)tr * g.Hq * KD);
       i_fa = (const char*)(fw + tr);
-      i_pa = (const char*)(qpg + (int64_t)tr * g.Hkv * KDP);
+      i_pa = (const char*)(qpg + (int64_t)tr * g.Hp * KDP);
       i_nq = rows * rs_q;
       i_nf = rows * 4;
       i_np = rows * rs_p;

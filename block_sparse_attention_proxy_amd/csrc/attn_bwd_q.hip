@@ -91,7 +91,9 @@ __global__ __launch_bounds__(Q_NT) void dq128_kernel(
   const int kb0 = g.kb0[b];
   const int diag = (I * g.Bq) >> 7;
   const int qbase = I * g.Bq + chunk * 32;
-  const int64_t rowi = (int64_t)grp * g.nqb + QB;
+  const int pg = proxy_head(g, grp);                 // the proxy head this group reads
+  const float qw = proxy_qweight(g, grp);            // weight of its proxy-softmax term
+  const int64_t rowi = (int64_t)pg * g.nqb + QB;
   const int cnt = q2k_cnt[rowi];
   const int32_t* sel = q2k_idx + rowi * g.stride;
   const int qpos = qbase + col;
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(Q_NT) void dq128_kernel(
   // end clamped to the last one: a copy past a descriptor's bound would leave
   // its LDS row unwritten, holding whatever the slot held before.
   const uint32_t lds0 = lds_offset(smem_raw);
-  const uint32_t rsK = (uint32_t)g.Hkv * QD * 2, rsP = (uint32_t)g.Hkv * QDP * 2;
+  const uint32_t rsK = (uint32_t)g.Hkv * QD * 2, rsP = (uint32_t)g.Hp * QDP * 2;
   uint32_t voK[Q_KCOPY], voP[Q_PCOPY];
   int rK[Q_KCOPY], rP[Q_PCOPY];
 #pragma unroll
@@ -131,10 +133,11 @@ __global__ __launch_bounds__(Q_NT) void dq128_kernel(
     const uint32_t base = lds0 + (uint32_t)((s % Q_NBUF) * Q_STAGE);
     const int key0 = (sel[ss >> 1] - kb0) * 128 + (ss & 1) * QKC;
     const int64_t row0 = (int64_t)(t0 + key0) * g.Hkv + grp;
+    const int64_t rowp = (int64_t)(t0 + key0) * g.Hp + pg;
     const int last = L - 1 - key0;                  // last row of the document in the stage
     const i32x4 sK = make_srd(k + row0 * QD, QKC * rsK);
     const i32x4 sV = make_srd(v + row0 * QD, QKC * rsK);
-    const i32x4 sP = make_srd(kp + row0 * QDP, QKC * rsP);
+    const i32x4 sP = make_srd(kp + rowp * QDP, QKC * rsP);
     uint32_t oK[Q_KCOPY], oP[Q_PCOPY];
 #pragma unroll
     for (int j = 0; j < Q_KCOPY; ++j) oK[j] = voK[j];
@@ -175,11 +178,11 @@ __global__ __launch_bounds__(Q_NT) void dq128_kernel(
       for (int j = 0; j < 8; ++j) part = fmaf((float)dOf[ks][j], (float)of[j], part);
     }
     dl = part + __shfl_xor(part, 32, 64);
-    const bf16* sp = qp + (tq * g.Hkv + grp) * QDP + hi * 8;
+    const bf16* sp = qp + (tq * g.Hp + pg) * QDP + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < QDP / 16; ++ks) QPf[ks] = ld8(sp + ks * 16);
     lse2 = lse[(int64_t)h * g.T + tq] * LOG2E;
-    lsep2 = lse_p[(int64_t)grp * g.T + tq] * LOG2E;
+    lsep2 = lse_p[(int64_t)pg * g.T + tq] * LOG2E;
     // per-query values the KV-major pass reads: -D and both LSEs in log2 units
     if (hi == 0 && qpos < L) {
       delta[(int64_t)h * g.T + tq] = -dl;             // stored negated: -rowsum(dO * O)
@@ -212,6 +215,10 @@ __global__ __launch_bounds__(Q_NT) void dq128_kernel(
   const uint32_t oRowP = (uint32_t)(2 * Q_KS + TP::off(col, hi * 8) * 2);
   const uint32_t oColP = (uint32_t)(2 * Q_KS + TP::off(tr_r, tr_c) * 2);
   const float sl2 = g.scale_log2, psl2 = g.pscale_log2;
+  // the weight of the proxy-softmax term folded into its exponent: qw Q =
+  // exp2(Y s_p log2e - (lsep2 - log2 qw)) (exact for the weights used: 1 and
+  // a power-of-two group count)
+  const float lsepq = qw > 1.f ? lsep2 - __builtin_log2f(qw) : lsep2;
   const float ninvG = -1.f / (float)g.G;
 
   auto stage = [&](int s, auto masked_c) __attribute__((always_inline)) {
@@ -293,8 +300,8 @@ __global__ __launch_bounds__(Q_NT) void dq128_kernel(
         });
       }
       // the proxy term of the tiles assigned to this head: Y^T = kp qp^T,
-      // Q = exp2(Y s_p log2e - lsep2), C^T += kp^T Q^T
-      if (((s * 2 + kt) % g.G) == hl) {
+      // qw Q = exp2(Y s_p log2e - lsepq), C^T += kp^T (qw Q)^T (none where qw = 0)
+      if (((s * 2 + kt) % g.G) == hl && qw != 0.f) {
         f32x16 Y = zero16();
         static_for<QDP / 16>([&](auto ksc) __attribute__((always_inline)) {
           constexpr int ks = decltype(ksc)::value;
@@ -304,7 +311,7 @@ __global__ __launch_bounds__(Q_NT) void dq128_kernel(
         bf16x8 bq[2];
         static_for<16>([&](auto ic) __attribute__((always_inline)) {
           constexpr int i = decltype(ic)::value;
-          float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], psl2, -lsep2));
+          float qv = __builtin_amdgcn_exp2f(fmaf(Y[i], psl2, -lsepq));
           if constexpr (MASKED) qv = keep_if<(uint32_t)(((i >> 2) << 3) + (i & 3))>(qv, mx, mw);
           bq[i >> 3][i & 7] = (bf16)qv;
         });

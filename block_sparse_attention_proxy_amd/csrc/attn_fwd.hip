@@ -97,7 +97,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(
   const int kb0 = g.kb0[b];
   const int diag = (I * g.Bq) >> 7;
   const int qbase = I * g.Bq + chunk * 32 * QT;
-  const int64_t rowi = (int64_t)grp * g.nqb + QB;
+  const int64_t rowi = (int64_t)proxy_head(g, grp) * g.nqb + QB;   // the group's block list
   const int cnt = q2k_cnt[rowi];
   const int32_t* sel = q2k_idx + rowi * g.stride;
 
@@ -503,8 +503,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(
 }
 
 // Proxy log-sum-exp over each query's selected keys: one wave per 32 queries
-// of a (group, query block); kp tiles are read as A fragments straight from
-// global memory (the waves of a workgroup walk the same blocks).
+// of a (proxy head, query block), launched over the proxy heads' geometry
+// (Hkv = Hp); kp tiles are read as A fragments straight from global memory
+// (the waves of a workgroup walk the same blocks).
 template <typename T, int DP>
 __global__ __launch_bounds__(256, 4) void proxy_lse_kernel(const T* __restrict__ qp,
                                                         const T* __restrict__ kp,
@@ -532,7 +533,7 @@ __global__ __launch_bounds__(256, 4) void proxy_lse_kernel(const T* __restrict__
   const int qrow = qpos < L ? qpos : L - 1;
   frag_t<T> QPf[DP / 16];
   {
-    const T* sp = qp + ((int64_t)(t0 + qrow) * g.Hkv + grp) * DP + hi * 8;
+    const T* sp = qp + ((int64_t)(t0 + qrow) * g.Hp + grp) * DP + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < DP / 16; ++ks) QPf[ks] = ld8(sp + ks * 16);
   }
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(256, 4) void proxy_lse_kernel(const T* __restrict__
       if (kpos > q0 + 31) break;
       int key = kpos + col;
       key = key < L ? key : L - 1;               // rows past the end are masked below
-      const T* sk = kp + ((int64_t)(t0 + key) * g.Hkv + grp) * DP + hi * 8;
+      const T* sk = kp + ((int64_t)(t0 + key) * g.Hp + grp) * DP + hi * 8;
       f32x16 Y = zero16();
 #pragma unroll
       for (int ks = 0; ks < DP / 16; ++ks) mma(Y, ld8(sk + ks * 16), QPf[ks]);
@@ -615,7 +616,7 @@ __global__ __launch_bounds__(256, 3) void proxy_lse128_kernel(const T* __restric
   const int qrow = qpos < L ? qpos : L - 1;
   frag_t<T> QPf[DP / 16];
   {
-    const T* sp = qp + ((int64_t)(t0 + qrow) * g.Hkv + grp) * DP + hi * 8;
+    const T* sp = qp + ((int64_t)(t0 + qrow) * g.Hp + grp) * DP + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < DP / 16; ++ks) QPf[ks] = ld8(sp + ks * 16);
   }
@@ -629,7 +630,7 @@ __global__ __launch_bounds__(256, 3) void proxy_lse128_kernel(const T* __restric
   // offsets; rows past the document end (diagonal block only, masked below)
   // clamped to its last row, since a copy past the bound leaves its LDS row
   // unwritten
-  const uint32_t rs = (uint32_t)g.Hkv * DP * (uint32_t)sizeof(T);
+  const uint32_t rs = (uint32_t)g.Hp * DP * (uint32_t)sizeof(T);
   uint32_t vo[C::COPIES];
   int rr[C::COPIES];
 #pragma unroll
@@ -641,7 +642,7 @@ __global__ __launch_bounds__(256, 3) void proxy_lse128_kernel(const T* __restric
   auto issue = [&](int si) __attribute__((always_inline)) {
     const int J = sel[si < cnt ? si : cnt - 1] - kb0;    // past the end: the last block again
     const uint32_t base = lds0 + (uint32_t)((si % C::NBUF) * C::SLOT);
-    const i32x4 sd = make_srd(kp + ((int64_t)(t0 + J * 128) * g.Hkv + grp) * DP, 128u * rs);
+    const i32x4 sd = make_srd(kp + ((int64_t)(t0 + J * 128) * g.Hp + grp) * DP, 128u * rs);
     const int last = L - 1 - J * 128;
     uint32_t o[C::COPIES];
 #pragma unroll
@@ -705,7 +706,7 @@ __global__ __launch_bounds__(256, 3) void proxy_lse128_kernel(const T* __restric
 }
 
 template <typename T, int D, int DP>
-static hipError_t fwd_dispatch(const Geo& g, const void* q, const void* k, const void* v,
+static hipError_t fwd_dispatch(const Geo& g, const Geo& gp, const void* q, const void* k, const void* v,
                                const void* qp, const void* kp, const int32_t* q2k_idx,
                                const int32_t* q2k_cnt, void* o, float* lse, float* lse_p,
                                hipStream_t s) {
@@ -728,29 +729,30 @@ static hipError_t fwd_dispatch(const Geo& g, const void* q, const void* k, const
                      (const T*)v, q2k_idx, q2k_cnt, (T*)o, lse, g); }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t nrow = (int64_t)g.Hkv * g.nqb;
-  if (g.Bq == 128) {
+  // the proxy log-sum-exp, once per proxy head
+  const int64_t nrow = (int64_t)gp.Hkv * gp.nqb;
+  if (gp.Bq == 128) {
     constexpr int lse_lds = LseCfg<T, DP>::LDS_BYTES;
     { ProfScope _ps("proxy_lse", s);
     hipLaunchKernelGGL((proxy_lse128_kernel<T, DP>), dim3((unsigned)nrow), dim3(256), lse_lds,
-                       s, (const T*)qp, (const T*)kp, q2k_idx, q2k_cnt, lse_p, g); }
+                       s, (const T*)qp, (const T*)kp, q2k_idx, q2k_cnt, lse_p, gp); }
     return hipGetLastError();
   }
-  const int per_wg = 4 / (g.Bq / 32);
+  const int per_wg = 4 / (gp.Bq / 32);
   { ProfScope _ps("proxy_lse", s);
   hipLaunchKernelGGL((proxy_lse_kernel<T, DP>), dim3((unsigned)((nrow + per_wg - 1) / per_wg)), dim3(256),
-                     0, s, (const T*)qp, (const T*)kp, q2k_idx, q2k_cnt, lse_p, g); }
+                     0, s, (const T*)qp, (const T*)kp, q2k_idx, q2k_cnt, lse_p, gp); }
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const Geo& g, int is_bf16, const void* q, const void* k, const void* v,
+hipError_t launch_fwd(const Geo& g, const Geo& gp, int is_bf16, const void* q, const void* k, const void* v,
                       const void* qp, const void* kp, const int32_t* q2k_idx,
                       const int32_t* q2k_cnt, void* o, float* lse, float* lse_p, hipStream_t s) {
   if (is_bf16) {
-    if (g.D == 128) return fwd_dispatch<bf16, 128, 64>(g, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, s);
-    return fwd_dispatch<bf16, 64, 32>(g, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, s);
+    if (g.D == 128) return fwd_dispatch<bf16, 128, 64>(g, gp, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, s);
+    return fwd_dispatch<bf16, 64, 32>(g, gp, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, s);
   }
-  return fwd_dispatch<float, 64, 32>(g, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, s);
+  return fwd_dispatch<float, 64, 32>(g, gp, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, s);
 }
 
 }  // namespace msa

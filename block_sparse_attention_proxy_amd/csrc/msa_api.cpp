@@ -41,11 +41,12 @@ struct Plan {
   msa_layout lay{};
   int64_t off_qb0, off_kb0, off_s0, off_order, off_unit0, off_slab0, off_qdoc, off_kdoc, off_counts, off_totals;
   int64_t off_delta, off_lse2, off_lsep2, off_cpart;
-  // one proxy head shared by every KV group: the per-group copies the
-  // forward and backward run on (used only when shared)
+  // one proxy head shared by every KV group: the kernels read the one head
+  // for every group, and the backward writes per-group proxy gradients here
+  // before they are averaged (used only when shared)
   bool shared = false;
   int32_t Hp = 0;                    // proxy heads: the group count of scoring and selection
-  int64_t off_qpb, off_kpb, off_q2kb, off_cntb, off_ptrb, off_k2qb, off_lsepb, off_dqpb, off_dkpb;
+  int64_t off_dqpb, off_dkpb;
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -152,15 +153,9 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
   if (G > 4) off = align_up(off + 4 * (int64_t)c.heads_kv * (G / 4) * vl->total_tokens * c.proxy_dim);
   P->shared = Hp == 1 && c.heads_kv > 1;
   P->Hp = (int32_t)Hp;
+  g.Hp = (int32_t)Hp;
   if (P->shared) {
-    const int64_t T = vl->total_tokens, Hkv = c.heads_kv, esz = c.dtype == MSA_BF16 ? 2 : 4;
-    P->off_qpb = off;  off = align_up(off + esz * T * Hkv * c.proxy_dim);
-    P->off_kpb = off;  off = align_up(off + esz * T * Hkv * c.proxy_dim);
-    P->off_q2kb = off; off = align_up(off + 4 * Hkv * nqb * g.stride);
-    P->off_cntb = off; off = align_up(off + 4 * Hkv * nqb);
-    P->off_ptrb = off; off = align_up(off + 4 * Hkv * (nkb + 1));
-    P->off_k2qb = off; off = align_up(off + 4 * Hkv * g.cap);
-    P->off_lsepb = off; off = align_up(off + 4 * Hkv * T);
+    const int64_t T = vl->total_tokens, Hkv = c.heads_kv;
     P->off_dqpb = off; off = align_up(off + 4 * T * Hkv * c.proxy_dim);
     P->off_dkpb = off; off = align_up(off + 4 * T * Hkv * c.proxy_dim);
   }
@@ -276,48 +271,17 @@ void prof_end(hipStream_t s) {
 
 namespace {
 
-// Views of the shared-proxy copies in a bound workspace.
-struct Shared {
-  void *qp, *kp;
-  int32_t *q2k, *cnt, *ptr, *k2q;
-  float *lsep, *dqp, *dkp;
+// Per-group proxy gradients of a shared head in a bound workspace.
+struct SharedGrads {
+  float *dqp, *dkp;
 };
 
-Shared shared_views(const Plan& P, void* ws) {
+SharedGrads shared_grads(const Plan& P, void* ws) {
   char* base = static_cast<char*>(ws);
-  Shared b;
-  b.qp = base + P.off_qpb;
-  b.kp = base + P.off_kpb;
-  b.q2k = reinterpret_cast<int32_t*>(base + P.off_q2kb);
-  b.cnt = reinterpret_cast<int32_t*>(base + P.off_cntb);
-  b.ptr = reinterpret_cast<int32_t*>(base + P.off_ptrb);
-  b.k2q = reinterpret_cast<int32_t*>(base + P.off_k2qb);
-  b.lsep = reinterpret_cast<float*>(base + P.off_lsepb);
+  SharedGrads b;
   b.dqp = reinterpret_cast<float*>(base + P.off_dqpb);
   b.dkp = reinterpret_cast<float*>(base + P.off_dkpb);
   return b;
-}
-
-// qp, kp [T, 1, dp] -> [T, Hkv, dp]
-hipError_t bcast_inputs(const Plan& P, const msa_config* cfg, const void* qp, const void* kp,
-                        const Shared& b, hipStream_t st) {
-  const int64_t row = (int64_t)P.g.DP * (cfg->dtype == MSA_BF16 ? 2 : 4);
-  hipError_t e = msa::launch_bcast(qp, b.qp, P.g.T, P.g.Hkv, row, st);
-  if (e != hipSuccess) return e;
-  return msa::launch_bcast(kp, b.kp, P.g.T, P.g.Hkv, row, st);
-}
-
-// the shared head's block lists [1, ...] -> [Hkv, ...] (the inverted index
-// only when given)
-hipError_t bcast_lists(const Plan& P, const int32_t* q2k_idx, const int32_t* q2k_cnt,
-                       const int32_t* k2q_ptr, const int32_t* k2q_idx, const Shared& b,
-                       hipStream_t st) {
-  const int Hkv = P.g.Hkv;
-  hipError_t e = msa::launch_bcast(q2k_idx, b.q2k, 1, Hkv, 4 * (int64_t)P.g.nqb * P.g.stride, st);
-  if (e == hipSuccess) e = msa::launch_bcast(q2k_cnt, b.cnt, 1, Hkv, 4 * (int64_t)P.g.nqb, st);
-  if (e == hipSuccess && k2q_ptr) e = msa::launch_bcast(k2q_ptr, b.ptr, 1, Hkv, 4 * ((int64_t)P.g.nkb + 1), st);
-  if (e == hipSuccess && k2q_idx) e = msa::launch_bcast(k2q_idx, b.k2q, 1, Hkv, 4 * P.g.cap, st);
-  return e;
 }
 
 }  // namespace
@@ -493,19 +457,10 @@ msa_status msa_fwd(const msa_config* cfg, const msa_varlen* vl, const void* q, c
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = msa::launch_meta(P.g, st);
   if (e != hipSuccess) return hip_fail(e, "metadata");
-  if (P.shared) {
-    // the shared head's inputs and lists copied to every group; its lse_p is group 0's
-    Shared b = shared_views(P, workspace);
-    if ((e = bcast_inputs(P, cfg, qp, kp, b, st)) != hipSuccess) return hip_fail(e, "shared proxy copies");
-    if ((e = bcast_lists(P, q2k_idx, q2k_cnt, nullptr, nullptr, b, st)) != hipSuccess)
-      return hip_fail(e, "shared proxy copies");
-    e = msa::launch_fwd(P.g, cfg->dtype == MSA_BF16, q, k, v, b.qp, b.kp, b.q2k, b.cnt, o, lse, b.lsep, st);
-    if (e != hipSuccess) return hip_fail(e, "fwd");
-    e = msa::launch_bcast(b.lsep, lse_p, 1, 1, 4 * (int64_t)P.g.T, st);
-    if (e != hipSuccess) return hip_fail(e, "shared proxy copies");
-    return MSA_OK;
-  }
-  e = msa::launch_fwd(P.g, cfg->dtype == MSA_BF16, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, st);
+  // every group reads the proxy head's block lists; the proxy log-sum-exp is
+  // taken once per proxy head
+  e = msa::launch_fwd(P.g, proxy_geo(P), cfg->dtype == MSA_BF16, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse,
+                      lse_p, st);
   if (e != hipSuccess) return hip_fail(e, "fwd");
   return MSA_OK;
 }
@@ -532,16 +487,12 @@ msa_status msa_bwd(const msa_config* cfg, const msa_varlen* vl, const void* q, c
   hipError_t e = msa::launch_meta(P.g, st);
   if (e != hipSuccess) return hip_fail(e, "metadata");
   if (P.shared) {
-    // per-group backward on the copies, then the proxy gradients averaged over the groups
-    Shared b = shared_views(P, workspace);
+    // every group reads the shared head; its proxy gradients, one per group
+    // (the proxy-softmax term in group 0 only), are averaged over the groups
+    SharedGrads b = shared_grads(P, workspace);
     const int64_t T = P.g.T, Hkv = P.g.Hkv, dp = P.g.DP;
-    if ((e = bcast_inputs(P, cfg, qp, kp, b, st)) != hipSuccess) return hip_fail(e, "shared proxy copies");
-    if ((e = bcast_lists(P, q2k_idx, q2k_cnt, k2q_ptr, k2q_idx, b, st)) != hipSuccess)
-      return hip_fail(e, "shared proxy copies");
-    if ((e = msa::launch_bcast(lse_p, b.lsep, 1, (int)Hkv, 4 * T, st)) != hipSuccess)
-      return hip_fail(e, "shared proxy copies");
-    e = msa::launch_bwd(P.g, cfg->dtype == MSA_BF16, q, k, v, b.qp, b.kp, o, lse, b.lsep, dout, b.q2k,
-                        b.cnt, b.ptr, b.k2q, dq, dk, dv, b.dqp, b.dkp, w, st);
+    e = msa::launch_bwd(P.g, cfg->dtype == MSA_BF16, q, k, v, qp, kp, o, lse, lse_p, dout, q2k_idx,
+                        q2k_cnt, k2q_ptr, k2q_idx, dq, dk, dv, b.dqp, b.dkp, w, st);
     if (e != hipSuccess) return hip_fail(e, "bwd");
     if ((e = msa::launch_group_mean(b.dqp, dqp, T, (int)Hkv, dp, st)) != hipSuccess)
       return hip_fail(e, "shared proxy gradients");

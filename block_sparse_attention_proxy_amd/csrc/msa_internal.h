@@ -44,6 +44,8 @@ struct Geo {
   int32_t n_units;                   // proxy-scoring units (pairs of 128-row tiles)
   int32_t nslab;                     // column slabs (K2Q_SLAB blocks) of the inverted index, per group
   int32_t k2q_chunks;                // 256-row chunks per slab (the most any slab needs)
+  int32_t Hp;                        // proxy heads of qp, kp, lse_p and the block lists: Hkv, or 1
+                                     // for one head shared by every KV group
   float scale, pscale, lam;          // softmax scale, proxy scale, proxy loss weight
   float scale_log2, pscale_log2;     // scale * log2(e), pscale * log2(e)
   const int32_t* cu;                 // device cu_seqlens [B + 1]
@@ -57,6 +59,16 @@ struct Geo {
   int32_t* kdoc;                     // [nkb] document of each global KV block
   int32_t* slab0;                    // [B + 1] first column slab of each document
 };
+
+// The proxy head a KV group reads (its own, or the one shared head), and the
+// weight of the proxy-softmax term Q in that group's proxy gradient.  With a
+// shared head the per-group gradients lam (Q - T_g) are averaged over the
+// groups afterwards, so Q is taken once, in group 0, with weight Hkv, and the
+// other groups contribute only their -T_g.
+__host__ __device__ __forceinline__ int proxy_head(const Geo& g, int grp) { return g.Hp == 1 ? 0 : grp; }
+__host__ __device__ __forceinline__ float proxy_qweight(const Geo& g, int grp) {
+  return g.Hp == g.Hkv ? 1.f : (grp == 0 ? (float)g.Hkv : 0.f);
+}
 
 // Workspace regions (byte offsets are computed by the host layout routine).
 struct Work {
@@ -80,17 +92,15 @@ constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 hipError_t noalloc_scratch(void** ptr);
 
 hipError_t launch_meta(const Geo& g, hipStream_t s);
-// shared proxy head: row broadcast (dst[r][c] = src[r], rows of row_bytes, a
-// multiple of 4) and the in-order average over copies of fp32 rows
-hipError_t launch_bcast(const void* src, void* dst, int64_t rows, int copies, int64_t row_bytes,
-                        hipStream_t s);
+// shared proxy head: the in-order average over copies of fp32 rows
 hipError_t launch_group_mean(const float* src, float* dst, int64_t rows, int copies, int64_t words,
                              hipStream_t s);
 hipError_t launch_proxy_scores(const Geo& g, int is_bf16, const void* qp, const void* kp,
                                float* scores, hipStream_t s);
 hipError_t launch_select(const Geo& g, const float* scores, int32_t* q2k_idx, int32_t* q2k_cnt,
                          int32_t* k2q_ptr, int32_t* k2q_idx, const Work& w, hipStream_t s);
-hipError_t launch_fwd(const Geo& g, int is_bf16, const void* q, const void* k, const void* v,
+// (gp: the proxy heads' geometry, Hkv = Hp, for the proxy log-sum-exp)
+hipError_t launch_fwd(const Geo& g, const Geo& gp, int is_bf16, const void* q, const void* k, const void* v,
                       const void* qp, const void* kp, const int32_t* q2k_idx,
                       const int32_t* q2k_cnt, void* o, float* lse, float* lse_p, hipStream_t s);
 hipError_t launch_bwd(const Geo& g, int is_bf16, const void* q, const void* k, const void* v,

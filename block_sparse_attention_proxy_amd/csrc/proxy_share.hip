@@ -4,12 +4,13 @@
 // "Flash-MSA: Ein Training mit einer Million Tokens", Under the hood); with
 // one proxy head its block choice serves every query head, and the proxy
 // gradient's target T is the mean of the main probabilities over all query
-// heads.  The path reuses the per-group kernels unchanged: scoring and
-// selection run once (for the one head); the forward and backward run on the
-// shared head's inputs and block lists copied to every group; the per-group
-// proxy gradients are then averaged over the groups.  That average is exact:
-// every group sees the same proxy softmax Q, the all-heads T is the mean of
-// the group means, and the proxy gradients are linear in T.
+// heads.  Scoring and selection run once, for the one head; the forward and
+// backward kernels of every KV group read the one head's inputs, block lists
+// and log-sum-exp directly.  Each group writes its own proxy gradient, in
+// which only group 0 carries the proxy-softmax term Q (with weight Hkv) and
+// every group its -T_g; the mean over the groups below is then the gradient
+// of the shared head: the all-heads T is the mean of the group means, and
+// the proxy gradients are linear in T.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -17,32 +18,6 @@
 #include "msa_profile.h"
 
 namespace msa {
-
-// dst[r][c][w] = src[r][w]: rows x copies x words (4-byte words)
-__global__ __launch_bounds__(256) void bcast_rows_kernel(const uint32_t* __restrict__ src,
-                                                         uint32_t* __restrict__ dst, int64_t rows,
-                                                         int copies, int64_t words) {
-  const int64_t n = rows * copies * words;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t w = i % words;
-    const int64_t r = i / (words * copies);
-    dst[i] = src[r * words + w];
-  }
-}
-
-// the same in 16-byte words (row bytes a multiple of 16, 16-byte aligned buffers)
-__global__ __launch_bounds__(256) void bcast_rows16_kernel(const uint4* __restrict__ src,
-                                                           uint4* __restrict__ dst, int64_t rows,
-                                                           int copies, int64_t words) {
-  const int64_t n = rows * copies * words;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t w = i % words;
-    const int64_t r = i / (words * copies);
-    dst[i] = src[r * words + w];
-  }
-}
 
 // dst[r][w] = scale * sum over c (in order) of src[r][c][w]
 __global__ __launch_bounds__(256) void group_mean_kernel(const float* __restrict__ src,
@@ -64,23 +39,6 @@ static unsigned grid_for(int64_t n) {
   return (unsigned)(b < 1 ? 1 : (b > 65536 ? 65536 : b));
 }
 
-hipError_t launch_bcast(const void* src, void* dst, int64_t rows, int copies, int64_t row_bytes,
-                        hipStream_t s) {
-  if (rows <= 0 || row_bytes <= 0) return hipSuccess;
-  const bool wide = row_bytes % 16 == 0 && ((uintptr_t)src % 16 == 0) && ((uintptr_t)dst % 16 == 0);
-  { ProfScope _ps("share_bcast", s);
-  if (wide) {
-    const int64_t words = row_bytes / 16;
-    hipLaunchKernelGGL(bcast_rows16_kernel, dim3(grid_for(rows * copies * words)), dim3(256), 0, s,
-                       (const uint4*)src, (uint4*)dst, rows, copies, words);
-  } else {
-    const int64_t words = row_bytes / 4;
-    hipLaunchKernelGGL(bcast_rows_kernel, dim3(grid_for(rows * copies * words)), dim3(256), 0, s,
-                       (const uint32_t*)src, (uint32_t*)dst, rows, copies, words);
-  } }
-  return hipGetLastError();
-}
-
 hipError_t launch_group_mean(const float* src, float* dst, int64_t rows, int copies, int64_t words,
                              hipStream_t s) {
   if (rows <= 0 || words <= 0) return hipSuccess;
@@ -92,8 +50,6 @@ hipError_t launch_group_mean(const float* src, float* dst, int64_t rows, int cop
 
 int share_kernels(KernelEntry* out, int max) {
   const KernelEntry all[] = {
-      {"share_bcast", (const void*)bcast_rows_kernel, 256, 0},
-      {"share_bcast16", (const void*)bcast_rows16_kernel, 256, 0},
       {"share_mean", (const void*)group_mean_kernel, 256, 0},
   };
   int n = (int)(sizeof(all) / sizeof(all[0]));

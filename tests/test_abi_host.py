@@ -147,7 +147,8 @@ def test_buffer_lifetimes_and_saved_bytes():
 @pytest.mark.parametrize("proxy_heads,Hp", [(0, 8), (8, 8), (1, 1)])
 def test_layout_proxy_heads(proxy_heads, Hp):
     """Hp leads every per-proxy-head tensor; the shared head adds workspace for
-    the per-group copies the forward and backward run on."""
+    exactly the per-group proxy gradients (fp32 dqp and dkp per KV group) that
+    are averaged into its own; its inputs are read in place, never copied."""
     cu = torch.tensor([0, 3000, 4100], dtype=torch.int32)
     base = msa.msa_get_layout(msa.Config(32, 8, 128, 64, 128, 8), msa.Varlen(cu))
     lay = msa.msa_get_layout(msa.Config(32, 8, 128, 64, 128, 8, proxy_heads=proxy_heads), msa.Varlen(cu))
@@ -155,9 +156,9 @@ def test_layout_proxy_heads(proxy_heads, Hp):
     assert {k: v for k, v in lay.items() if k not in ("workspace_bytes", "proxy_heads")} == \
            {k: v for k, v in base.items() if k not in ("workspace_bytes", "proxy_heads")}
     T = 4100
-    copies = 2 * 2 * T * 8 * 64 + 4 * 8 * T + 2 * 4 * T * 8 * 64    # qp, kp; lse_p; dqp, dkp
+    grads = 2 * 4 * T * 8 * 64                                       # dqp, dkp per group
     if Hp == 1:
-        assert lay["workspace_bytes"] >= base["workspace_bytes"] + copies
+        assert base["workspace_bytes"] + grads <= lay["workspace_bytes"] <= base["workspace_bytes"] + grads + 512
     else:
         assert lay["workspace_bytes"] == base["workspace_bytes"]
 
