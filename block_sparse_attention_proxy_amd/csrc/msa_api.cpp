@@ -40,7 +40,7 @@ struct Plan {
   msa::Geo g{};
   msa_layout lay{};
   int64_t off_qb0, off_kb0, off_s0, off_order, off_unit0, off_slab0, off_qdoc, off_kdoc, off_counts, off_totals;
-  int64_t off_delta, off_lse2, off_lsep2, off_cpart;
+  int64_t off_delta, off_lse2, off_lsep2, off_cpart, off_queue;
   // one proxy head shared by every KV group: the kernels read the one head
   // for every group, and the backward writes per-group proxy gradients here
   // before they are averaged (used only when shared)
@@ -151,6 +151,7 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
   P->off_lsep2 = off;  off = align_up(off + 4 * (int64_t)c.heads_kv * vl->total_tokens);
   P->off_cpart = off;
   if (G > 4) off = align_up(off + 4 * (int64_t)c.heads_kv * (G / 4) * vl->total_tokens * c.proxy_dim);
+  P->off_queue = off;  off = align_up(off + 4 * 8 * 16);
   P->shared = Hp == 1 && c.heads_kv > 1;
   P->Hp = (int32_t)Hp;
   g.Hp = (int32_t)Hp;
@@ -196,6 +197,7 @@ msa_status bind_workspace(Plan* P, void* ws, size_t ws_bytes, msa::Work* w) {
     w->lse2 = reinterpret_cast<float*>(base + P->off_lse2);
     w->lsep2 = reinterpret_cast<float*>(base + P->off_lsep2);
     w->cpart = reinterpret_cast<float*>(base + P->off_cpart);
+    w->queue = reinterpret_cast<int32_t*>(base + P->off_queue);
   }
   return MSA_OK;
 }

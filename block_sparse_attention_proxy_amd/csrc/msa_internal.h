@@ -32,6 +32,22 @@ struct LdsLimitOnce {
   }
 };
 
+// Compute units of the current device, read once per device.
+inline hipError_t device_cu_count(int* n) {
+  static constexpr int MAX_DEV = 64;
+  static std::atomic<int> cache[MAX_DEV] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < MAX_DEV;
+  if (cached && (*n = cache[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+  e = hipDeviceGetAttribute(n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (*n < 1) return hipErrorInvalidDevice;
+  if (cached) cache[dev].store(*n, std::memory_order_relaxed);
+  return hipSuccess;
+}
+
 // Geometry of one call, resolved on the host and passed to every kernel by value.
 struct Geo {
   int32_t Hq, Hkv, G, D, DP;
@@ -67,7 +83,9 @@ struct Geo {
 // other groups contribute only their -T_g.
 __host__ __device__ __forceinline__ int proxy_head(const Geo& g, int grp) { return g.Hp == 1 ? 0 : grp; }
 __host__ __device__ __forceinline__ float proxy_qweight(const Geo& g, int grp) {
-  return g.Hp == g.Hkv ? 1.f : (grp == 0 ? (float)g.Hkv : 0.f);
+  // an integer first, converted once: the float then depends on grp and is
+  // formed where it is used
+  return (float)(g.Hp == g.Hkv ? 1 : (grp == 0 ? g.Hkv : 0));
 }
 
 // Workspace regions (byte offsets are computed by the host layout routine).
@@ -78,6 +96,7 @@ struct Work {
   float* lse2;                       // [Hq * T]       main LSE in log2 units
   float* lsep2;                      // [Hkv * T]      proxy LSE in log2 units
   float* cpart;                      // [Hkv * nhg * T * DP] proxy-gradient partials (G > 4)
+  int32_t* queue;                    // [8 * 16] work-queue counters of the KV-major pass (one per 64 B)
 };
 
 // Inverted-index build: KV blocks of a document are taken in slabs of this
@@ -116,7 +135,8 @@ bool dkdv128_supported(const Geo& g);
 hipError_t launch_dkdv128(const Geo& g, const void* q, const void* k, const void* v,
                           const void* qp, const void* kp, const float* lse2, const float* lsep2,
                           const void* dout, const float* delta, const int32_t* k2q_ptr,
-                          const int32_t* k2q_idx, float* dk, float* dv, float* dkp, hipStream_t s);
+                          const int32_t* k2q_idx, float* dk, float* dv, float* dkp, int32_t* queue,
+                          hipStream_t s);
 
 // Query-major backward for bf16, d = 128, dp = 64 and 1, 2, 4 or 8 heads per
 // group (eight waves of 32 queries, two per SIMD); other shapes use the
