@@ -2,7 +2,8 @@
 oracle: top-k of 1 (only the forced blocks), documents of one token and
 shorter than a query block, a window wider than most documents, a dilated
 window whose stride skips whole documents' worth of blocks, the shared proxy
-head in fp32, and a batch whose every document but one is empty."""
+head in fp32, a batch whose every document but one is empty, and KV-major
+work-item counts that do not divide evenly over the per-XCD queues."""
 import pytest
 
 from msa_inputs import WORKLOADS
@@ -18,6 +19,11 @@ CASES = {
     "dilated-wide": (WORKLOADS["layer-32k"], dict(topk=3, local_window=3, dilation=5), (3000, 640)),
     "shared-fp32": (WORKLOADS["tiny-2k-fp32"], dict(topk=3, proxy_heads=1, local_window=1), (1500, 600)),
     "one-nonempty": (WORKLOADS["layer-32k"], dict(topk=3), (0, 0, 1900, 0)),
+    # KV-major work queue with a (group, KV block) count that is not a multiple
+    # of the eight queues (57 and 125 items: uneven queues, the later ones
+    # drained by stealing), fewer items than compute units, G = 4 and 8
+    "queue-uneven-g4": (WORKLOADS["layer-32k"], dict(heads_q=12, heads_kv=3, topk=3), (700, 1300, 129)),
+    "queue-uneven-g8": (WORKLOADS["layer-128k-gqa8"], dict(heads_q=40, heads_kv=5, topk=3), (900, 2100)),
 }
 
 
