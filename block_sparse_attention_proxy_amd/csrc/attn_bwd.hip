@@ -885,7 +885,7 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
     if (!dq128_supported(g)) return hipErrorInvalidValue;
     { ProfScope _ps("bwd_dq", s);
     e = launch_dq128(g, q, k, v, qp, kp, o, lse, lse_p, dout, w.delta, w.lse2, w.lsep2, q2k_idx,
-                     q2k_cnt, dq, dqp, s); }
+                     q2k_cnt, dq, dqp, w.queue, s); }
     if (e != hipSuccess) return e;
   } else if (nq > 0) {
     { ProfScope _ps("bwd_dq", s);
@@ -905,7 +905,7 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
   if (nk > 0 && FAST && dkdv128_supported(g)) {
     { ProfScope _ps("bwd_dkdv", s);
     e = launch_dkdv128(g, q, k, v, qp, kp, w.lse2, w.lsep2, dout, w.delta, k2q_ptr, k2q_idx, dk, dv,
-                       dkp, w.queue, s); }
+                       dkp, w.queue + 8 * 16, s); }
     if (e != hipSuccess) return e;
   } else if (nk > 0) {
     { ProfScope _ps("bwd_dkdv", s);

@@ -10,8 +10,9 @@
 // dqp = s_p dY kp, which splits over the heads of a group as
 // sum over heads of (Q on the key tiles assigned to the head - P / G) kp.
 //
-// Work decomposition: a workgroup serves one (KV group, query block) and runs
-// eight waves; wave u owns 32 queries of one head (head u mod G, query chunk
+// Work decomposition: a work item is one (KV group, query block) (or half of
+// one when it has more than eight 32-query units); the grid is persistent, one
+// workgroup per CU taking items from a queue, and a workgroup runs eight waves; wave u owns 32 queries of one head (head u mod G, query chunk
 // u / G), so a workgroup holds whole chunks for G in {1, 2, 4, 8} and sums the
 // proxy term over their heads itself.  Stages are 64-key halves of the
 // selected blocks, K, V and kp rows copied global -> LDS by DMA into a ring
@@ -35,19 +36,15 @@ constexpr int Q_NBUF = 3, Q_AHEAD = Q_NBUF - 1;        // ring slots, stages in 
 constexpr int Q_KS = QKC * QD * 2;                     // bytes of a stage's K (or V) rows: 16 KiB
 constexpr int Q_PS = QKC * QDP * 2;                    // bytes of its kp rows: 8 KiB
 constexpr int Q_STAGE = 2 * Q_KS + Q_PS;
-constexpr int Q_LDS = Q_NBUF * Q_STAGE;                // 120 KiB
+constexpr int Q_RING = Q_NBUF * Q_STAGE;               // 120 KiB
+constexpr int Q_ITEM = Q_RING;                         // the workgroup's current work item
+constexpr int Q_LDS = Q_RING + 256;
 constexpr int Q_KCOPY = QKC / (Q_NW * 4);              // K (and V) copies per wave per stage, 4 rows each
 constexpr int Q_PCOPY = QKC / (Q_NW * 8);              // kp copies per wave per stage, 8 rows each
 constexpr int Q_COPIES = 2 * Q_KCOPY + Q_PCOPY;
 constexpr int Q_RS = 33;                               // row stride (floats) of the reduction buffer
 static_assert(Q_KCOPY >= 1 && Q_PCOPY >= 1, "copy split");
-static_assert(Q_NW * QDP * Q_RS * 4 <= Q_LDS, "reduction buffer");
-
-__device__ __forceinline__ int xcd_remap_q(int i, int n) {
-  const int per = n / 8, rem = n % 8;
-  const int x = i % 8, k = i / 8;
-  return x * per + (x < rem ? x : rem) + k;
-}
+static_assert(Q_NW * QDP * Q_RS * 4 <= Q_RING, "reduction buffer");
 
 // Two transpose reads joined into one fragment: the first at a + OFF, the
 // second (8 rows further down) at b + OFF + OFF2.
@@ -66,16 +63,49 @@ __global__ __launch_bounds__(Q_NT) void dq128_kernel(
     const float* __restrict__ lse, const float* __restrict__ lse_p, const bf16* __restrict__ dout,
     float* __restrict__ delta, float* __restrict__ lse2_out, float* __restrict__ lsep2_out,
     const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_cnt,
-    float* __restrict__ dq, float* __restrict__ dqp, Geo g) {
+    float* __restrict__ dq, float* __restrict__ dqp, int32_t* __restrict__ queue, Geo g) {
   typedef Tile<bf16, QD> TK;
   typedef Tile<bf16, QDP> TP;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31, hi = lane >> 5;
   const int NU = g.G * (g.Bq / 32);
   const int nwg = (NU + Q_NW - 1) / Q_NW;
-  const int bid = xcd_remap_q(blockIdx.x, gridDim.x);
+  const int nitems = g.Hkv * g.nqb * nwg;
+  const uint32_t item_lds = lds_offset(smem_raw) + Q_ITEM;
+  int qi = 0;                                      // queues this workgroup has drained
+  // Work items (a workgroup's share of one (group, query block)) come from
+  // eight queues, one per XCD over a contiguous range of items; a workgroup
+  // takes the next item of its own XCD's queue and, once that is empty, of
+  // the others in turn (XCDs differ in speed by a few percent, and a fixed
+  // split leaves the faster ones idle at the end).  Thread 0 takes it, a
+  // barrier hands it to every wave.
+  auto next_item = [&]() __attribute__((always_inline)) {
+    if (tid == 0) {
+      int it = -1;
+      const int per = nitems / 8, rem = nitems % 8;
+      const int home = blockIdx.x & 7;
+      while (qi < 8) {
+        const int x = (home + qi) & 7;
+        const int size = per + (x < rem ? 1 : 0);
+        if (size > 0) {
+          const int c = atomicAdd(queue + x * 16, 1);
+          if (c < size) { it = x * per + (x < rem ? x : rem) + c; break; }
+        }
+        ++qi;
+      }
+      *reinterpret_cast<__attribute__((address_space(3))) int*>((uintptr_t)item_lds) = it;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(
+        *reinterpret_cast<__attribute__((address_space(3))) const int*>((uintptr_t)item_lds));
+  };
+  for (int bid; (bid = next_item()) >= 0;) {
+  // lane values from an opaque copy of the lane index, so that they are
+  // formed per item rather than kept live across items
+  int lane = tid & 63;
+  asm volatile("" : "+v"(lane));
+  const int col = lane & 31, hi = lane >> 5;
   const int64_t item = bid / nwg;
   const int wgi = bid % nwg;
   const int grp = (int)(item / g.nqb);
@@ -376,6 +406,13 @@ __global__ __launch_bounds__(Q_NT) void dq128_kernel(
     const int pos = I * g.Bq + c * 32 + qq;
     if (pos < L) dqp[((int64_t)(t0 + pos) * g.Hkv + grp) * QDP + dpi] = acc * out_scale;
   }
+  }
+}
+
+// Clears the eight queue counters (a kernel rather than a memset, so that
+// the launch sequence can be captured in a graph and replayed).
+__global__ void dq_queue_reset_kernel(int32_t* queue) {
+  if (threadIdx.x < 8) queue[threadIdx.x * 16] = 0;
 }
 
 }  // namespace
@@ -386,16 +423,22 @@ hipError_t launch_dq128(const Geo& g, const void* q, const void* k, const void* 
                         const void* kp, const void* o, const float* lse, const float* lse_p,
                         const void* dout, float* delta, float* lse2, float* lsep2,
                         const int32_t* q2k_idx, const int32_t* q2k_cnt, float* dq, float* dqp,
-                        hipStream_t s) {
+                        int32_t* queue, hipStream_t s) {
   static LdsLimitOnce lds_limit;
   hipError_t e = lds_limit.ensure({{(const void*)dq128_kernel, Q_LDS}});
   if (e != hipSuccess) return e;
   const int NU = g.G * (g.Bq / 32);
   const int64_t n = (int64_t)g.Hkv * g.nqb * ((NU + Q_NW - 1) / Q_NW);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(dq128_kernel, dim3((unsigned)n), dim3(Q_NT), Q_LDS, s, (const bf16*)q,
+  if (n > INT32_MAX / 2) return hipErrorInvalidValue;
+  int ncu = 0;
+  if ((e = device_cu_count(&ncu)) != hipSuccess) return e;
+  const unsigned grid = (unsigned)(n < ncu ? n : ncu);      // one workgroup per CU (LDS-bound)
+  hipLaunchKernelGGL(dq_queue_reset_kernel, dim3(1), dim3(64), 0, s, queue);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(dq128_kernel, dim3(grid), dim3(Q_NT), Q_LDS, s, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, (const bf16*)qp, (const bf16*)kp, (const bf16*)o,
-                     lse, lse_p, (const bf16*)dout, delta, lse2, lsep2, q2k_idx, q2k_cnt, dq, dqp, g);
+                     lse, lse_p, (const bf16*)dout, delta, lse2, lsep2, q2k_idx, q2k_cnt, dq, dqp, queue, g);
   return hipGetLastError();
 }
 

@@ -151,7 +151,7 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
   P->off_lsep2 = off;  off = align_up(off + 4 * (int64_t)c.heads_kv * vl->total_tokens);
   P->off_cpart = off;
   if (G > 4) off = align_up(off + 4 * (int64_t)c.heads_kv * (G / 4) * vl->total_tokens * c.proxy_dim);
-  P->off_queue = off;  off = align_up(off + 4 * 8 * 16);
+  P->off_queue = off;  off = align_up(off + 4 * 2 * 8 * 16);
   P->shared = Hp == 1 && c.heads_kv > 1;
   P->Hp = (int32_t)Hp;
   g.Hp = (int32_t)Hp;

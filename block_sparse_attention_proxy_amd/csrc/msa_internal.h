@@ -96,7 +96,8 @@ struct Work {
   float* lse2;                       // [Hq * T]       main LSE in log2 units
   float* lsep2;                      // [Hkv * T]      proxy LSE in log2 units
   float* cpart;                      // [Hkv * nhg * T * DP] proxy-gradient partials (G > 4)
-  int32_t* queue;                    // [8 * 16] work-queue counters of the KV-major pass (one per 64 B)
+  int32_t* queue;                    // [2][8 * 16] work-queue counters of the query-major and the
+                                     // KV-major pass (one per 64 B)
 };
 
 // Inverted-index build: KV blocks of a document are taken in slabs of this
@@ -146,7 +147,7 @@ hipError_t launch_dq128(const Geo& g, const void* q, const void* k, const void* 
                         const void* kp, const void* o, const float* lse, const float* lse_p,
                         const void* dout, float* delta, float* lse2, float* lsep2,
                         const int32_t* q2k_idx, const int32_t* q2k_cnt, float* dq, float* dqp,
-                        hipStream_t s);
+                        int32_t* queue, hipStream_t s);
 
 // Kernel registry for the resource report: each translation unit lists the
 // kernels it instantiates, with the block size and dynamic LDS of its launch.
