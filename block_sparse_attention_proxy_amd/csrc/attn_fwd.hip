@@ -68,7 +68,7 @@ template <typename T, int D, int DP, int QT, int NW>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ q2k_idx, const int32_t* __restrict__ q2k_cnt,
-    T* __restrict__ o, float* __restrict__ lse, Geo g) {
+    T* __restrict__ o, float* __restrict__ lse, int32_t* __restrict__ queue, Geo g) {
   typedef FwdCfg<T, D, DP, QT, NW> C;
   typedef typename C::TK TK;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -76,11 +76,21 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(
   constexpr int NT = C::NT;
   static_assert(C::NK >= 1, "tile split");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31, hi = lane >> 5;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NU = g.G * (g.Bq / (32 * QT));
   const int nwg = (NU + NW - 1) / NW;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  // bf16, d = 128: a persistent grid over a work queue (below); other shapes:
+  // one workgroup per item
+  constexpr bool PERSIST = sizeof(T) == 2 && D == 128;
+
+  // One work item: a workgroup's share of one (KV group, query block).
+  auto body = [&](const int bid) __attribute__((always_inline)) {
+  // lane values from an opaque copy of the lane index in the persistent
+  // kernel, so that they are formed per item rather than kept live across
+  // items
+  int lane = tid & 63;
+  if constexpr (PERSIST) asm volatile("" : "+v"(lane));
+  const int col = lane & 31, hi = lane >> 5;
   const int64_t item = bid / nwg;
   const int wgi = bid % nwg;
   const int grp = (int)(item / g.nqb);
@@ -500,6 +510,50 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(
       if (hi == 0) lse[(int64_t)h * g.T + t] = (mref[qt] + log2f(lt)) * LN2;
     }
   }
+  };
+
+  if constexpr (PERSIST) {
+    // Items come from eight queues, one per XCD over a contiguous range of
+    // items; a workgroup takes the next item of its own XCD's queue and, once
+    // that is empty, of the others in turn (XCDs differ in speed by a few
+    // percent, and a fixed split leaves the faster ones idle at the end).
+    // Thread 0 takes it, a barrier hands it to every wave.  Every item ends
+    // with a barrier after its last LDS read, so the next item's copies
+    // cannot overwrite operands still in use.
+    const uint32_t item_lds = lds_offset(smem_raw) + (uint32_t)C::LDS_BYTES;
+    const int nitems = g.Hkv * g.nqb * nwg;
+    int qi = 0;                                      // queues this workgroup has drained
+    for (;;) {
+      if (tid == 0) {
+        int it = -1;
+        const int per = nitems / 8, rem = nitems % 8;
+        const int home = blockIdx.x & 7;
+        while (qi < 8) {
+          const int x = (home + qi) & 7;
+          const int size = per + (x < rem ? 1 : 0);
+          if (size > 0) {
+            const int c = atomicAdd(queue + x * 16, 1);
+            if (c < size) { it = x * per + (x < rem ? x : rem) + c; break; }
+          }
+          ++qi;
+        }
+        *reinterpret_cast<__attribute__((address_space(3))) int*>((uintptr_t)item_lds) = it;
+      }
+      __syncthreads();
+      const int bid = __builtin_amdgcn_readfirstlane(
+          *reinterpret_cast<__attribute__((address_space(3))) const int*>((uintptr_t)item_lds));
+      if (bid < 0) break;
+      body(bid);
+    }
+  } else {
+    body(xcd_remap(blockIdx.x, gridDim.x));
+  }
+}
+
+// Clears the eight queue counters of the forward (a kernel rather than a
+// memset, so that the launch sequence can be captured in a graph and replayed).
+__global__ void fwd_queue_reset_kernel(int32_t* queue) {
+  if (threadIdx.x < 8) queue[threadIdx.x * 16] = 0;
 }
 
 // Proxy log-sum-exp over each query's selected keys: one wave per 32 queries
@@ -709,25 +763,37 @@ template <typename T, int D, int DP>
 static hipError_t fwd_dispatch(const Geo& g, const Geo& gp, const void* q, const void* k, const void* v,
                                const void* qp, const void* kp, const int32_t* q2k_idx,
                                const int32_t* q2k_cnt, void* o, float* lse, float* lse_p,
-                               hipStream_t s) {
+                               int32_t* queue, hipStream_t s) {
   // bf16, d = 128: eight waves of 32 queries (two waves per SIMD, each within
   // 256 registers); otherwise four waves of 64 queries
   constexpr bool W8 = sizeof(T) == 2 && D == 128;
   constexpr int QT = W8 ? 1 : 2, NW = W8 ? 8 : 4;
   typedef FwdCfg<T, D, DP, QT, NW> C;
   auto fn = fwd_kernel<T, D, DP, QT, NW>;
+  // the persistent kernel keeps its work item in 256 bytes past the ring
+  constexpr int lds_bytes = C::LDS_BYTES + (W8 ? 256 : 0);
   static LdsLimitOnce lds_limit;
   {
-    const hipError_t e = lds_limit.ensure({{(const void*)fn, C::LDS_BYTES}});
+    const hipError_t e = lds_limit.ensure({{(const void*)fn, lds_bytes}});
     if (e != hipSuccess) return e;
   }
   const int NU = g.G * (g.Bq / (32 * QT));
   const int64_t nblk = (int64_t)g.Hkv * g.nqb * ((NU + NW - 1) / NW);
   if (nblk == 0) return hipSuccess;
+  if (nblk > INT32_MAX / 2) return hipErrorInvalidValue;
+  unsigned grid = (unsigned)nblk;
+  hipError_t e;
+  if constexpr (W8) {
+    int ncu = 0;
+    if ((e = device_cu_count(&ncu)) != hipSuccess) return e;
+    grid = (unsigned)(nblk < ncu ? nblk : ncu);            // one workgroup per CU (LDS-bound)
+    hipLaunchKernelGGL(fwd_queue_reset_kernel, dim3(1), dim3(64), 0, s, queue);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   { ProfScope _ps("fwd", s);
-  hipLaunchKernelGGL(fn, dim3((unsigned)nblk), dim3(C::NT), C::LDS_BYTES, s, (const T*)q, (const T*)k,
-                     (const T*)v, q2k_idx, q2k_cnt, (T*)o, lse, g); }
-  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(C::NT), lds_bytes, s, (const T*)q, (const T*)k,
+                     (const T*)v, q2k_idx, q2k_cnt, (T*)o, lse, queue, g); }
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the proxy log-sum-exp, once per proxy head
   const int64_t nrow = (int64_t)gp.Hkv * gp.nqb;
@@ -747,12 +813,14 @@ static hipError_t fwd_dispatch(const Geo& g, const Geo& gp, const void* q, const
 
 hipError_t launch_fwd(const Geo& g, const Geo& gp, int is_bf16, const void* q, const void* k, const void* v,
                       const void* qp, const void* kp, const int32_t* q2k_idx,
-                      const int32_t* q2k_cnt, void* o, float* lse, float* lse_p, hipStream_t s) {
+                      const int32_t* q2k_cnt, void* o, float* lse, float* lse_p, int32_t* queue,
+                      hipStream_t s) {
   if (is_bf16) {
-    if (g.D == 128) return fwd_dispatch<bf16, 128, 64>(g, gp, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, s);
-    return fwd_dispatch<bf16, 64, 32>(g, gp, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, s);
+    if (g.D == 128)
+      return fwd_dispatch<bf16, 128, 64>(g, gp, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, queue, s);
+    return fwd_dispatch<bf16, 64, 32>(g, gp, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, queue, s);
   }
-  return fwd_dispatch<float, 64, 32>(g, gp, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, s);
+  return fwd_dispatch<float, 64, 32>(g, gp, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse, lse_p, queue, s);
 }
 
 }  // namespace msa
@@ -760,7 +828,7 @@ hipError_t launch_fwd(const Geo& g, const Geo& gp, int is_bf16, const void* q, c
 namespace msa {
 int fwd_kernels(KernelEntry* out, int max) {
   const KernelEntry all[] = {
-      {"fwd<bf16,d128,dp64>", (const void*)fwd_kernel<bf16, 128, 64, 1, 8>, 512, FwdCfg<bf16, 128, 64, 1, 8>::LDS_BYTES},
+      {"fwd<bf16,d128,dp64>", (const void*)fwd_kernel<bf16, 128, 64, 1, 8>, 512, FwdCfg<bf16, 128, 64, 1, 8>::LDS_BYTES + 256},
       {"fwd<bf16,d64,dp32>", (const void*)fwd_kernel<bf16, 64, 32, 2, 4>, 256, FwdCfg<bf16, 64, 32, 2, 4>::LDS_BYTES},
       {"fwd<f32,d64,dp32>", (const void*)fwd_kernel<float, 64, 32, 2, 4>, 256, FwdCfg<float, 64, 32, 2, 4>::LDS_BYTES},
       {"proxy_lse<bf16,dp64>", (const void*)proxy_lse_kernel<bf16, 64>, 256, 0},

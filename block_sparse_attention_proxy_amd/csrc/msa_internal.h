@@ -96,8 +96,8 @@ struct Work {
   float* lse2;                       // [Hq * T]       main LSE in log2 units
   float* lsep2;                      // [Hkv * T]      proxy LSE in log2 units
   float* cpart;                      // [Hkv * nhg * T * DP] proxy-gradient partials (G > 4)
-  int32_t* queue;                    // [2][8 * 16] work-queue counters of the query-major and the
-                                     // KV-major pass (one per 64 B)
+  int32_t* queue;                    // [3][8 * 16] work-queue counters of the query-major pass,
+                                     // the KV-major pass and the forward (one per 64 B)
 };
 
 // Inverted-index build: KV blocks of a document are taken in slabs of this
@@ -122,7 +122,8 @@ hipError_t launch_select(const Geo& g, const float* scores, int32_t* q2k_idx, in
 // (gp: the proxy heads' geometry, Hkv = Hp, for the proxy log-sum-exp)
 hipError_t launch_fwd(const Geo& g, const Geo& gp, int is_bf16, const void* q, const void* k, const void* v,
                       const void* qp, const void* kp, const int32_t* q2k_idx,
-                      const int32_t* q2k_cnt, void* o, float* lse, float* lse_p, hipStream_t s);
+                      const int32_t* q2k_cnt, void* o, float* lse, float* lse_p, int32_t* queue,
+                      hipStream_t s);
 hipError_t launch_bwd(const Geo& g, int is_bf16, const void* q, const void* k, const void* v,
                       const void* qp, const void* kp, const void* o, const float* lse,
                       const float* lse_p, const void* dout, const int32_t* q2k_idx,
