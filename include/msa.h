@@ -44,8 +44,14 @@
  *   - All device pointers are caller-owned device memory, 16-byte aligned.
  *     The library allocates no device memory.  Its only state is a
  *     thread-local error message, a per-device record that the kernels' LDS
- *     limits were raised, and (only after msa_profile_enable) a thread-local
- *     pool of timing events.  Work is enqueued asynchronously on
+ *     limits were raised and of the device's compute-unit count (the
+ *     persistent kernels launch one workgroup per compute unit), and (only
+ *     after msa_profile_enable) a thread-local pool of timing events.
+ *   - The workspace (msa_layout.workspace_bytes) holds a call's per-document
+ *     tables, per-query intermediates of the backward and the work-queue
+ *     counters of its persistent kernels, which each call clears on `stream`
+ *     before use.  Calls that share one workspace must not overlap: issue
+ *     them on one stream or order them.  Work is enqueued asynchronously on
  *     `stream` (a hipStream_t; NULL = default stream); the caller keeps every
  *     buffer alive until that work completes.  Outputs are overwritten.
  *   - Errors: every argument is checked on the host before anything is
