@@ -25,7 +25,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
-SOURCES = ["select.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_kv.hip", "attn_bwd_q.hip", "proxy_share.hip", "msa_api.cpp"]
+SOURCES = ["select.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_kv.hip", "attn_bwd_q.hip", "proxy_share.hip", "work_queue.hip", "msa_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -905,7 +905,7 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
   if (nk > 0 && FAST && dkdv128_supported(g)) {
     { ProfScope _ps("bwd_dkdv", s);
     e = launch_dkdv128(g, q, k, v, qp, kp, w.lse2, w.lsep2, dout, w.delta, k2q_ptr, k2q_idx, dk, dv,
-                       dkp, w.queue + 8 * 16, s); }
+                       dkp, w.queue + kQueueWords, s); }
     if (e != hipSuccess) return e;
   } else if (nk > 0) {
     { ProfScope _ps("bwd_dkdv", s);

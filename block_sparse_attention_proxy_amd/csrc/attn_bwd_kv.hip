@@ -134,21 +134,9 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
   // others in turn.  Thread 0 takes it; a barrier hands it to every wave
   // (each role runs its own loop, with the same barriers per item).
   auto next_item = [&]() __attribute__((always_inline)) {
-    if (tid == 0) {
-      int item = -1;
-      const int per = nk / 8, rem = nk % 8;
-      const int home = blockIdx.x & 7;
-      while (qi < 8) {
-        const int x = (home + qi) & 7;
-        const int size = per + (x < rem ? 1 : 0);
-        if (size > 0) {
-          const int c = atomicAdd(queue + x * 16, 1);
-          if (c < size) { item = x * per + (x < rem ? x : rem) + c; break; }
-        }
-        ++qi;
-      }
-      *reinterpret_cast<__attribute__((address_space(3))) int*>((uintptr_t)item_lds) = item;
-    }
+    if (tid == 0)
+      *reinterpret_cast<__attribute__((address_space(3))) int*>((uintptr_t)item_lds) =
+          queue_take(queue, nk, blockIdx.x % kQueues, qi);
     __syncthreads();
     return __builtin_amdgcn_readfirstlane(
         *reinterpret_cast<__attribute__((address_space(3))) const int*>((uintptr_t)item_lds));
@@ -608,12 +596,6 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
   }
 }
 
-// Clears the eight queue counters (a kernel rather than a memset, so that
-// the launch sequence can be captured in a graph and replayed).
-__global__ void queue_reset_kernel(int32_t* queue) {
-  if (threadIdx.x < 8) queue[threadIdx.x * 16] = 0;
-}
-
 }  // namespace
 
 bool dkdv128_supported(const Geo& g) { return g.G == 4 || g.G == 8; }
@@ -633,8 +615,7 @@ hipError_t launch_dkdv128(const Geo& g, const void* q, const void* k, const void
   int ncu = 0;
   if ((e = device_cu_count(&ncu)) != hipSuccess) return e;
   const unsigned grid = (unsigned)(nk < ncu ? nk : ncu);     // one workgroup per CU (LDS-bound)
-  hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, s, queue);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_queue_reset(queue, s)) != hipSuccess) return e;
 #define MSA_LAUNCH_KV(GG)                                                                            \
   hipLaunchKernelGGL((dkdv_ws_kernel<GG>), dim3(grid), dim3(512), WS_LDS, s,                         \
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)qp, (const bf16*)kp,  \

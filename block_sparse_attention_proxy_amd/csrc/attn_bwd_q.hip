@@ -81,21 +81,9 @@ __global__ __launch_bounds__(Q_NT) void dq128_kernel(
   // split leaves the faster ones idle at the end).  Thread 0 takes it, a
   // barrier hands it to every wave.
   auto next_item = [&]() __attribute__((always_inline)) {
-    if (tid == 0) {
-      int it = -1;
-      const int per = nitems / 8, rem = nitems % 8;
-      const int home = blockIdx.x & 7;
-      while (qi < 8) {
-        const int x = (home + qi) & 7;
-        const int size = per + (x < rem ? 1 : 0);
-        if (size > 0) {
-          const int c = atomicAdd(queue + x * 16, 1);
-          if (c < size) { it = x * per + (x < rem ? x : rem) + c; break; }
-        }
-        ++qi;
-      }
-      *reinterpret_cast<__attribute__((address_space(3))) int*>((uintptr_t)item_lds) = it;
-    }
+    if (tid == 0)
+      *reinterpret_cast<__attribute__((address_space(3))) int*>((uintptr_t)item_lds) =
+          queue_take(queue, nitems, blockIdx.x % kQueues, qi);
     __syncthreads();
     return __builtin_amdgcn_readfirstlane(
         *reinterpret_cast<__attribute__((address_space(3))) const int*>((uintptr_t)item_lds));
@@ -409,11 +397,6 @@ __global__ __launch_bounds__(Q_NT) void dq128_kernel(
   }
 }
 
-// Clears the eight queue counters (a kernel rather than a memset, so that
-// the launch sequence can be captured in a graph and replayed).
-__global__ void dq_queue_reset_kernel(int32_t* queue) {
-  if (threadIdx.x < 8) queue[threadIdx.x * 16] = 0;
-}
 
 }  // namespace
 
@@ -434,8 +417,7 @@ hipError_t launch_dq128(const Geo& g, const void* q, const void* k, const void* 
   int ncu = 0;
   if ((e = device_cu_count(&ncu)) != hipSuccess) return e;
   const unsigned grid = (unsigned)(n < ncu ? n : ncu);      // one workgroup per CU (LDS-bound)
-  hipLaunchKernelGGL(dq_queue_reset_kernel, dim3(1), dim3(64), 0, s, queue);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_queue_reset(queue, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(dq128_kernel, dim3(grid), dim3(Q_NT), Q_LDS, s, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, (const bf16*)qp, (const bf16*)kp, (const bf16*)o,
                      lse, lse_p, (const bf16*)dout, delta, lse2, lsep2, q2k_idx, q2k_cnt, dq, dqp, queue, g);

@@ -524,21 +524,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(
     const int nitems = g.Hkv * g.nqb * nwg;
     int qi = 0;                                      // queues this workgroup has drained
     for (;;) {
-      if (tid == 0) {
-        int it = -1;
-        const int per = nitems / 8, rem = nitems % 8;
-        const int home = blockIdx.x & 7;
-        while (qi < 8) {
-          const int x = (home + qi) & 7;
-          const int size = per + (x < rem ? 1 : 0);
-          if (size > 0) {
-            const int c = atomicAdd(queue + x * 16, 1);
-            if (c < size) { it = x * per + (x < rem ? x : rem) + c; break; }
-          }
-          ++qi;
-        }
-        *reinterpret_cast<__attribute__((address_space(3))) int*>((uintptr_t)item_lds) = it;
-      }
+      if (tid == 0)
+        *reinterpret_cast<__attribute__((address_space(3))) int*>((uintptr_t)item_lds) =
+            queue_take(queue, nitems, blockIdx.x % kQueues, qi);
       __syncthreads();
       const int bid = __builtin_amdgcn_readfirstlane(
           *reinterpret_cast<__attribute__((address_space(3))) const int*>((uintptr_t)item_lds));
@@ -550,11 +538,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(
   }
 }
 
-// Clears the eight queue counters of the forward (a kernel rather than a
-// memset, so that the launch sequence can be captured in a graph and replayed).
-__global__ void fwd_queue_reset_kernel(int32_t* queue) {
-  if (threadIdx.x < 8) queue[threadIdx.x * 16] = 0;
-}
 
 // Proxy log-sum-exp over each query's selected keys: one wave per 32 queries
 // of a (proxy head, query block), launched over the proxy heads' geometry
@@ -787,8 +770,7 @@ static hipError_t fwd_dispatch(const Geo& g, const Geo& gp, const void* q, const
     int ncu = 0;
     if ((e = device_cu_count(&ncu)) != hipSuccess) return e;
     grid = (unsigned)(nblk < ncu ? nblk : ncu);            // one workgroup per CU (LDS-bound)
-    hipLaunchKernelGGL(fwd_queue_reset_kernel, dim3(1), dim3(64), 0, s, queue);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_queue_reset(queue, s)) != hipSuccess) return e;
   }
   { ProfScope _ps("fwd", s);
   hipLaunchKernelGGL(fn, dim3(grid), dim3(C::NT), lds_bytes, s, (const T*)q, (const T*)k,

@@ -151,7 +151,7 @@ msa_status plan(const msa_config* cfg, const msa_varlen* vl, Plan* P) {
   P->off_lsep2 = off;  off = align_up(off + 4 * (int64_t)c.heads_kv * vl->total_tokens);
   P->off_cpart = off;
   if (G > 4) off = align_up(off + 4 * (int64_t)c.heads_kv * (G / 4) * vl->total_tokens * c.proxy_dim);
-  P->off_queue = off;  off = align_up(off + 4 * 3 * 8 * 16);
+  P->off_queue = off;  off = align_up(off + 4 * msa::kQueueSets * msa::kQueueWords);
   P->shared = Hp == 1 && c.heads_kv > 1;
   P->Hp = (int32_t)Hp;
   g.Hp = (int32_t)Hp;
@@ -462,7 +462,7 @@ msa_status msa_fwd(const msa_config* cfg, const msa_varlen* vl, const void* q, c
   // every group reads the proxy head's block lists; the proxy log-sum-exp is
   // taken once per proxy head
   // the forward's work-queue counters: the third set in the workspace
-  int32_t* queue = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + P.off_queue) + 2 * 8 * 16;
+  int32_t* queue = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + P.off_queue) + 2 * msa::kQueueWords;
   e = msa::launch_fwd(P.g, proxy_geo(P), cfg->dtype == MSA_BF16, q, k, v, qp, kp, q2k_idx, q2k_cnt, o, lse,
                       lse_p, queue, st);
   if (e != hipSuccess) return hip_fail(e, "fwd");

@@ -88,6 +88,32 @@ __host__ __device__ __forceinline__ float proxy_qweight(const Geo& g, int grp) {
   return (float)(g.Hp == g.Hkv ? 1 : (grp == 0 ? g.Hkv : 0));
 }
 
+// Work queues of the persistent kernels: one set of counters per kernel,
+// kQueues of them (one per XCD) kQueueStride words (64 bytes) apart; the
+// workspace holds kQueueSets sets.
+constexpr int kQueues = 8, kQueueStride = 16, kQueueWords = kQueues * kQueueStride;
+constexpr int kQueueSets = 3;                       // query-major, KV-major, forward
+// Work queues of the persistent kernels: kQueues counters, one per XCD,
+// kQueueStride words (64 bytes) apart; queue x serves a contiguous range of
+// the n items (the first n % kQueues queues one item more).  The calling
+// thread takes the next item of queue `home` (its workgroup's XCD) and, once
+// that is empty, of the others in turn; `drained` counts the queues it has
+// found empty and is kept by the caller between calls.  Returns -1 once every
+// queue is empty, so a loop over queue_take ends on every workgroup.
+__device__ __forceinline__ int queue_take(int32_t* queue, int n, int home, int& drained) {
+  const int per = n / kQueues, rem = n % kQueues;
+  while (drained < kQueues) {
+    const int x = (home + drained) % kQueues;
+    const int size = per + (x < rem ? 1 : 0);
+    if (size > 0) {
+      const int c = atomicAdd(queue + x * kQueueStride, 1);
+      if (c < size) return x * per + (x < rem ? x : rem) + c;
+    }
+    ++drained;
+  }
+  return -1;
+}
+
 // Workspace regions (byte offsets are computed by the host layout routine).
 struct Work {
   int32_t* counts;                   // [Hkv * nslab * k2q_chunks * 64] selections per (slab, chunk, block)
@@ -96,8 +122,8 @@ struct Work {
   float* lse2;                       // [Hq * T]       main LSE in log2 units
   float* lsep2;                      // [Hkv * T]      proxy LSE in log2 units
   float* cpart;                      // [Hkv * nhg * T * DP] proxy-gradient partials (G > 4)
-  int32_t* queue;                    // [3][8 * 16] work-queue counters of the query-major pass,
-                                     // the KV-major pass and the forward (one per 64 B)
+  int32_t* queue;                    // [kQueueSets][kQueueWords] work-queue counters of the
+                                     // query-major pass, the KV-major pass and the forward
 };
 
 // Inverted-index build: KV blocks of a document are taken in slabs of this
@@ -112,6 +138,8 @@ constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 hipError_t noalloc_scratch(void** ptr);
 
 hipError_t launch_meta(const Geo& g, hipStream_t s);
+// clears one set of work-queue counters (kQueues of them, 64 bytes apart)
+hipError_t launch_queue_reset(int32_t* queue, hipStream_t s);
 // shared proxy head: the in-order average over copies of fp32 rows
 hipError_t launch_group_mean(const float* src, float* dst, int64_t rows, int copies, int64_t words,
                              hipStream_t s);
