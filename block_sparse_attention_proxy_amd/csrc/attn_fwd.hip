@@ -8,13 +8,16 @@
 // u <= i inside the blocks selected for i's query block; the proxy softmax is
 // taken over the same set and only its log-sum-exp is kept.
 //
-// Work split: a workgroup (4 waves) serves one (KV group, query block) and
-// stages each selected KV block through LDS in two 64-key halves (K and V
-// rows), double-buffered with a register prefetch of the next half; V^T
-// fragments come from the row-major V tile through LDS transpose reads.
-// A wave owns QT x 32 queries of one head and computes S^T = K Q^T on bf16
-// MFMA so that each lane holds one query column; the probabilities then feed
-// O^T += V^T P^T without leaving registers.  The proxy log-sum-exp over the
+// Work split: a work item is one (KV group, query block), or a half of one
+// when it holds more than the workgroup's waves' worth of 32-query units.  For
+// bf16 and d = 128 the grid is persistent (one workgroup of eight waves per
+// CU, taking items from per-XCD work queues) and each selected KV block is
+// staged through an LDS ring in two 64-key halves (K and V rows) by DMA; other
+// shapes run one workgroup of four waves per item, double-buffered with a
+// register prefetch.  V^T fragments come from the row-major V tile through
+// LDS transpose reads.  A wave owns QT x 32 queries of one head and computes
+// S^T = K Q^T on bf16 MFMA so that each lane holds one query column; the
+// probabilities then feed O^T += V^T P^T without leaving registers.  The proxy log-sum-exp over the
 // same keys is a separate light kernel (one proxy head per group, dp-deep
 // contractions), which keeps the main kernel's registers for attention.
 #include "msa_device.h"
