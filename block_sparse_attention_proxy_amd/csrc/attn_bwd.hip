@@ -859,16 +859,15 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
   typedef DqCfg<T, D, DP> CQ;
   typedef KvCfg<T, D, DP> CK;
   // bf16, d = 128, dp = 64: the query-major pass is dq128 for every group
-  // size and the KV-major pass the two-role kernel for 4 and 8 heads per
+  // size and the KV-major pass the two-role kernel for 2, 4 and 8 heads per
   // group, so the generic kernels are built for the other shapes (and, here,
-  // the KV-major pass of 1 and 2 heads per group) only
+  // the KV-major pass of one head per group) only
   constexpr bool FAST = std::is_same<T, bf16>::value && D == 128 && DP == 64;
   static LdsLimitOnce lds_limit;
   {
     hipError_t e;
     if constexpr (FAST) {
-      e = lds_limit.ensure({{(const void*)dkdv_kernel<T, D, DP, 1>, CK::LDS_BYTES},
-                            {(const void*)dkdv_kernel<T, D, DP, 2>, CK::LDS_BYTES}});
+      e = lds_limit.ensure({{(const void*)dkdv_kernel<T, D, DP, 1>, CK::LDS_BYTES}});
     } else {
       e = lds_limit.ensure({{(const void*)dq_kernel<T, D, DP>, CQ::LDS_BYTES},
                             {(const void*)dkdv_kernel<T, D, DP, 1>, CK::LDS_BYTES},
@@ -915,8 +914,7 @@ static hipError_t bwd_dispatch(const Geo& g, const void* q, const void* k, const
                        w.lsep2, (const T*)dout, w.delta, k2q_ptr, k2q_idx, dk, dv, dkp, g)
     if constexpr (FAST) {
       switch (g.G) {
-        case 1: MSA_LAUNCH_DKDV(1); break;
-        case 2: MSA_LAUNCH_DKDV(2); break;
+        case 1: MSA_LAUNCH_DKDV(1); break;       // G = 2, 4, 8: the two-role kernel
         default: return hipErrorInvalidValue;
       }
     } else {
@@ -957,7 +955,6 @@ namespace msa {
 int bwd_kernels(KernelEntry* out, int max) {
   const KernelEntry all[] = {
       {"bwd_dkdv<bf16,d128,dp64,g1>", (const void*)dkdv_kernel<bf16, 128, 64, 1>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
-      {"bwd_dkdv<bf16,d128,dp64,g2>", (const void*)dkdv_kernel<bf16, 128, 64, 2>, 256, KvCfg<bf16, 128, 64>::LDS_BYTES},
       {"bwd_dq<bf16,d64,dp32>", (const void*)dq_kernel<bf16, 64, 32>, 256, DqCfg<bf16, 64, 32>::LDS_BYTES},
       {"bwd_dkdv<bf16,d64,dp32,g1>", (const void*)dkdv_kernel<bf16, 64, 32, 1>, 256, KvCfg<bf16, 64, 32>::LDS_BYTES},
       {"bwd_dkdv<bf16,d64,dp32,g2>", (const void*)dkdv_kernel<bf16, 64, 32, 2>, 256, KvCfg<bf16, 64, 32>::LDS_BYTES},

@@ -83,8 +83,8 @@ __device__ __forceinline__ bf16x8 tr_pair2(uint32_t a, uint32_t b) {
 constexpr int WS_NB = 6;                               // ring of stages
 constexpr int WS_SLOT = 2 * TILE_B;                    // Q tile, then dO tile
 constexpr int WS_FL = WS_NB * WS_SLOT;                 // float vectors, FL_SLOT per slot
-constexpr int WS_QP = WS_FL + WS_NB * FL_SLOT;         // qp tiles of two chunks
-constexpr int WS_XB = WS_QP + 2 * QP_TILE;             // P / dS fragments [parity][kg][4][64 x 16 B]
+constexpr int WS_QP = WS_FL + WS_NB * FL_SLOT;         // qp tiles of up to three chunks
+constexpr int WS_XB = WS_QP + 3 * QP_TILE;             // P / dS fragments [parity][kg][4][64 x 16 B]
 constexpr int WS_XB_KG = 4 * 1024;
 constexpr int WS_DY = WS_XB + 2 * 4 * WS_XB_KG;        // dY fragments [kg][2][64 x 16 B]
 constexpr int WS_DUMMY = WS_DY + 4 * 2 * 1024;         // target of the placeholder copy, 256 B per wave
@@ -93,6 +93,19 @@ constexpr int WS_LDS = WS_ITEM + 256;
 static_assert(WS_LDS <= 160 * 1024, "LDS budget");
 constexpr int WS_COPIES = 6;                           // per accumulation wave per stage (uniform)
 constexpr int WS_LATER = WS_COPIES * (WS_NB - 3);      // copies of stages s+1 .. s+NB-3
+
+// The qp rows of a chunk are copied with the copies of the chunk's last stage
+// (its last head), issued four stages ahead of it, and read at that stage by
+// both roles (by the accumulation wave one stage later).  With G heads a chunk
+// spans G stages.  A ring of N slots is safe when the copy of chunk c + N,
+// issued four stages before that chunk's last stage, comes at least two
+// stages after chunk c's last stage (the iteration after its last read): G N
+// >= 6, so two slots for G >= 4 and three for G = 2.
+template <int G>
+__device__ __forceinline__ uint32_t next_qp(uint32_t o) {
+  constexpr uint32_t N = G == 2 ? 3u : 2u;               // qp slots in the ring
+  return o == (N - 1) * (uint32_t)QP_TILE ? 0u : o + (uint32_t)QP_TILE;
+}
 
 __device__ __forceinline__ void lds_st16(uint32_t addr, const bf16x8& v) {
   typedef __attribute__((address_space(3))) bf16x8 lds_v8;
@@ -343,7 +356,7 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
           }
           Tacc = zero16();
           c_hl = 0;
-          c_qo ^= QP_TILE;
+          c_qo = next_qp<G>(c_qo);
           if (++c_c == nch) {
             c_c = 0;
             ++c_li;
@@ -462,7 +475,7 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
         } else {
           if (i_hl == G - 1) {
             bdma16(make_srd(i_pa, i_np), voP, ldP + i_qo);
-            i_qo ^= QP_TILE;
+            i_qo = next_qp<G>(i_qo);
             i_hl = 0;
             if (++i_c == nch) {
               i_c = 0;
@@ -542,7 +555,7 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
         if (hl == G - 1) {
           // dkp += dY^T qp over the chunk that ended at stage s - 1
           const uint32_t pb = bPc + a_qo;
-          a_qo ^= QP_TILE;
+          a_qo = next_qp<G>(a_qo);
           const bf16x8 ay0 = lds_ld8<0>(dy_lane), ay1 = lds_ld8<1024>(dy_lane);
           static_for<2>([&](auto kkc) __attribute__((always_inline)) {
             constexpr int kk = decltype(kkc)::value;
@@ -598,7 +611,7 @@ __global__ __launch_bounds__(512) void dkdv_ws_kernel(
 
 }  // namespace
 
-bool dkdv128_supported(const Geo& g) { return g.G == 4 || g.G == 8; }
+bool dkdv128_supported(const Geo& g) { return g.G == 2 || g.G == 4 || g.G == 8; }
 
 hipError_t launch_dkdv128(const Geo& g, const void* q, const void* k, const void* v,
                           const void* qp, const void* kp, const float* lse2, const float* lsep2,
@@ -606,7 +619,8 @@ hipError_t launch_dkdv128(const Geo& g, const void* q, const void* k, const void
                           const int32_t* k2q_idx, float* dk, float* dv, float* dkp, int32_t* queue,
                           hipStream_t s) {
   static LdsLimitOnce lds_limit;
-  hipError_t e = lds_limit.ensure({{(const void*)dkdv_ws_kernel<4>, WS_LDS},
+  hipError_t e = lds_limit.ensure({{(const void*)dkdv_ws_kernel<2>, WS_LDS},
+                                   {(const void*)dkdv_ws_kernel<4>, WS_LDS},
                                    {(const void*)dkdv_ws_kernel<8>, WS_LDS}});
   if (e != hipSuccess) return e;
   const int64_t nk = (int64_t)g.Hkv * g.nkb;
@@ -621,6 +635,7 @@ hipError_t launch_dkdv128(const Geo& g, const void* q, const void* k, const void
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)qp, (const bf16*)kp,  \
                      lse2, lsep2, (const bf16*)dout, delta, k2q_ptr, k2q_idx, dk, dv, dkp, queue, g)
   switch (g.G) {
+    case 2: MSA_LAUNCH_KV(2); break;
     case 4: MSA_LAUNCH_KV(4); break;
     case 8: MSA_LAUNCH_KV(8); break;
     default: return hipErrorInvalidValue;
@@ -631,6 +646,7 @@ hipError_t launch_dkdv128(const Geo& g, const void* q, const void* k, const void
 
 int bwd_kv_kernels(KernelEntry* out, int max) {
   const KernelEntry all[] = {
+      {"bwd_dkdv_ws<g2>", (const void*)dkdv_ws_kernel<2>, 512, WS_LDS},
       {"bwd_dkdv_ws<g4>", (const void*)dkdv_ws_kernel<4>, 512, WS_LDS},
       {"bwd_dkdv_ws<g8>", (const void*)dkdv_ws_kernel<8>, 512, WS_LDS},
   };

@@ -159,7 +159,7 @@ hipError_t launch_bwd(const Geo& g, int is_bf16, const void* q, const void* k, c
                       float* dq, float* dk, float* dv, float* dqp, float* dkp, const Work& w,
                       hipStream_t s);
 
-// KV-major backward for bf16, d = 128, dp = 64 and 4 or 8 heads per group
+// KV-major backward for bf16, d = 128, dp = 64 and 2, 4 or 8 heads per group
 // (the software-pipelined kernel); other shapes use the generic kernel.
 bool dkdv128_supported(const Geo& g);
 hipError_t launch_dkdv128(const Geo& g, const void* q, const void* k, const void* v,

@@ -2,8 +2,9 @@
 oracle: top-k of 1 (only the forced blocks), documents of one token and
 shorter than a query block, a window wider than most documents, a dilated
 window whose stride skips whole documents' worth of blocks, the shared proxy
-head in fp32, a batch whose every document but one is empty, and KV-major
-work-item counts that do not divide evenly over the per-XCD queues."""
+head in fp32, a batch whose every document but one is empty, KV-major
+work-item counts that do not divide evenly over the per-XCD queues, and two
+heads per group with long inverted lists."""
 import pytest
 
 from msa_inputs import WORKLOADS
@@ -24,6 +25,10 @@ CASES = {
     # drained by stealing), fewer items than compute units, G = 4 and 8
     "queue-uneven-g4": (WORKLOADS["layer-32k"], dict(heads_q=12, heads_kv=3, topk=3), (700, 1300, 129)),
     "queue-uneven-g8": (WORKLOADS["layer-128k-gqa8"], dict(heads_q=40, heads_kv=5, topk=3), (900, 2100)),
+    "queue-uneven-g2": (WORKLOADS["layer-32k"], dict(heads_q=6, heads_kv=3, topk=3), (700, 1300, 129)),
+    # G = 2 in the two-role KV-major kernel: a chunk's qp rows cycle through
+    # three ring slots; long lists (up to 47 entries) wrap the ring many times
+    "g2-long-lists": (WORKLOADS["layer-512k-window2"], dict(heads_q=16, topk=8), (6000,)),
 }
 
 
