@@ -515,22 +515,30 @@ def _doc_of_kb(docs: List[Doc], KB: int) -> Doc:
 def sampled_query_side(q, k, v, qp, kp, dO, cu_seqlens, q2k_idx, q2k_cnt, cfg: Config,
                        samples: List[Tuple[int, int]], O_for_D=None):
     """For sampled (g, global query block) pairs: O, LSE, LSE_p, dQ and dqp of
-    that block's rows, computed from the definition."""
-    assert cfg.proxy_heads != 1, "sampled evaluation covers one proxy head per group"
+    that block's rows, computed from the definition.  dqp is the gradient of
+    proxy head p = cfg.proxy_of(g) (returned as "p"); with a shared proxy head
+    (R1s) it takes T over every group's heads, as the layer backward does."""
     docs = doc_grid(cu_seqlens, cfg)
     out = []
     for g, QB in samples:
         doc = _doc_of_qb(docs, QB)
         I = QB - doc.qb0
-        fw = qblock_forward(q, k, v, qp, kp, doc, g, I, _sel_of(q2k_idx, q2k_cnt, g, QB), cfg)
+        p = cfg.proxy_of(g)
+        sel = _sel_of(q2k_idx, q2k_cnt, p, QB)
+        fw = qblock_forward(q, k, v, qp, kp, doc, g, I, sel, cfg)
         od = None
         if O_for_D is not None:
             od = [O_for_D[fw["rows"], h, :].astype(np.float64)
                   for h in range(g * cfg.G, (g + 1) * cfg.G)]
         bw = qblock_backward(fw, q, k, v, qp, kp, dO, g, cfg, od)
-        out.append(dict(g=g, QB=QB, rows=fw["rows"], O=np.stack(fw["O"], 1),
+        dqp = bw["dqp"]
+        if cfg.proxy_heads == 1:
+            fws = [fw if gg == g else qblock_forward(q, k, v, qp, kp, doc, gg, I, sel, cfg)
+                   for gg in cfg.groups_of(p)]
+            dqp = proxy_backward(fws, qp, kp, p, cfg)["dqp"]
+        out.append(dict(g=g, p=p, QB=QB, rows=fw["rows"], O=np.stack(fw["O"], 1),
                         LSE=np.stack(fw["LSE"], 0), LSE_p=fw["LSE_p"],
-                        dQ=np.stack(bw["dQ"], 1), dqp=bw["dqp"]))
+                        dQ=np.stack(bw["dQ"], 1), dqp=dqp))
     return out
 
 
@@ -538,21 +546,23 @@ def sampled_key_side(q, k, v, qp, kp, dO, cu_seqlens, q2k_idx, q2k_cnt, cfg: Con
                      samples: List[Tuple[int, int]], O_for_D=None,
                      qblocks: Optional[Tuple[int, int]] = None):
     """For sampled (g, global KV block) pairs: dK, dV and dkp of that block's
-    keys, summed over every query block whose selection holds it.  With
+    keys, summed over every query block whose selection holds it.  dK and dV
+    are group g's; dkp is proxy head p = cfg.proxy_of(g)'s (returned as "p"),
+    with T over every group's heads when the proxy head is shared (R1s).  With
     ``qblocks = (lo, hi)`` only the document's query blocks lo <= I < hi
     contribute (the full sums are the sums of such parts)."""
-    assert cfg.proxy_heads != 1, "sampled evaluation covers one proxy head per group"
     docs = doc_grid(cu_seqlens, cfg)
     out = []
     for g, KB in samples:
         doc = _doc_of_kb(docs, KB)
+        p = cfg.proxy_of(g)
         kr = _krows(doc, KB - doc.kb0, cfg)
         dK = np.zeros((len(kr), cfg.head_dim))
         dV = np.zeros((len(kr), cfg.head_dim))
         dKp = np.zeros((len(kr), cfg.proxy_dim))
         lo, hi = (0, doc.nq) if qblocks is None else (max(0, qblocks[0]), min(doc.nq, qblocks[1]))
         for I in range(lo, hi):
-            sel = _sel_of(q2k_idx, q2k_cnt, g, doc.qb0 + I)
+            sel = _sel_of(q2k_idx, q2k_cnt, p, doc.qb0 + I)
             if KB not in sel:
                 continue
             fw = qblock_forward(q, k, v, qp, kp, doc, g, I, sel, cfg)
@@ -564,8 +574,13 @@ def sampled_key_side(q, k, v, qp, kp, dO, cu_seqlens, q2k_idx, q2k_cnt, cfg: Con
             pos = np.searchsorted(fw["keys"], kr)
             dK += bw["dK"][pos]
             dV += bw["dV"][pos]
-            dKp += bw["dkp"][pos]
-        out.append(dict(g=g, KB=KB, keys=kr, dK=dK, dV=dV, dkp=dKp))
+            if cfg.proxy_heads == 1:
+                fws = [fw if gg == g else qblock_forward(q, k, v, qp, kp, doc, gg, I, sel, cfg)
+                       for gg in cfg.groups_of(p)]
+                dKp += proxy_backward(fws, qp, kp, p, cfg)["dkp"][pos]
+            else:
+                dKp += bw["dkp"][pos]
+        out.append(dict(g=g, p=p, KB=KB, keys=kr, dK=dK, dV=dV, dkp=dKp))
     return out
 
 

@@ -16,6 +16,8 @@ one by one, with the inputs gathered row by row from the seeded device tensors:
 * the KV blocks with the longest inverted list and with the list at the 99th
   percentile: the same element-wise check, the oracle's sum taken in ranges of
   query blocks (one progress line per range);
+* the 1M-token packing again with one proxy head shared by every group: the
+  same sampled checks on that head's lists, scores and gradients;
 * whole-layer identities that hold at any size: per group, the sum over keys
   of dV equals the sum over queries and heads of dO (softmax rows sum to one),
   and the sums over keys of dK and dkp vanish (each row of dS and of dY sums to
@@ -98,15 +100,18 @@ def _query_samples(docs, ocfg, rng, n_random=3):
 
 
 def _key_samples(docs, ocfg, k2q_ptr, rng, n_random=2):
-    lens = np.diff(k2q_ptr, axis=1)                       # [Hkv, NKB]
+    """(group, KV block) samples; a group's inverted lists are its proxy
+    head's (head 0 for every group when the head is shared)."""
+    lens = np.diff(k2q_ptr, axis=1)                       # [Hp, NKB]
     out = []
     longest = max(docs, key=lambda d: d.length)
     g = int(rng.integers(ocfg.heads_kv))
     out.append((g, longest.kb0 + longest.nk - 1))          # last (possibly partial) block
     short = np.argwhere((lens >= 1) & (lens <= MAX_LIST))
     for j in rng.permutation(len(short))[:n_random]:
-        out.append((int(short[j][0]), int(short[j][1])))
-    return [(g, KB) for g, KB in out if 1 <= lens[g, KB] <= 4 * MAX_LIST]
+        p, KB = int(short[j][0]), int(short[j][1])
+        out.append((int(rng.integers(ocfg.heads_kv)) if ocfg.proxy_heads == 1 else p, KB))
+    return [(g, KB) for g, KB in out if 1 <= lens[ocfg.proxy_of(g), KB] <= 4 * MAX_LIST]
 
 
 def _close(name, got, ref, atol=ATOL, cos_min=COS_MIN):
@@ -117,7 +122,13 @@ def _close(name, got, ref, atol=ATOL, cos_min=COS_MIN):
 
 
 def test_fullsize_sampled_parity(full_run):
-    name, w, ocfg, x, cu, buf = full_run
+    _check_sampled(*full_run)
+
+
+def _check_sampled(name, w, ocfg, x, cu, buf):
+    """Selection, query side and key side on sampled blocks (see the module
+    docstring); with a shared proxy head the block lists, scores and proxy
+    gradients are those of head 0."""
     docs = om.doc_grid(cu, ocfg)
     rng = np.random.default_rng(20261202)
     L = {n: DeviceRows(x[n]) for n in ("q", "k", "v", "qp", "kp", "dO")}
@@ -130,18 +141,19 @@ def test_fullsize_sampled_parity(full_run):
     qs = _query_samples(docs, ocfg, rng)
     for d, g, I in qs:
         QB = d.qb0 + I
-        got = [int(v) - d.kb0 for v in q2k_idx[g, QB, :q2k_cnt[g, QB]]]
+        p = ocfg.proxy_of(g)
+        got = [int(v) - d.kb0 for v in q2k_idx[p, QB, :q2k_cnt[p, QB]]]
         nc = om.candidate_count(I, ocfg)
-        log(f"[{name}] selection g={g} doc@{d.start} len={d.length} I={I} candidates={nc}")
+        log(f"[{name}] selection p={p} doc@{d.start} len={d.length} I={I} candidates={nc}")
         if nc == 0:
             assert got == om.select_row(np.zeros(0), I, ocfg)
             continue
-        s_gpu = buf.scores[g, d.s0 + I * d.nk: d.s0 + I * d.nk + nc].double().cpu().numpy()
-        s_or = om.proxy_row_scores(L["qp"], L["kp"], d, g, I, ocfg)
+        s_gpu = buf.scores[p, d.s0 + I * d.nk: d.s0 + I * d.nk + nc].double().cpu().numpy()
+        s_or = om.proxy_row_scores(L["qp"], L["kp"], d, p, I, ocfg)
         rows = np.arange(d.start + I * ocfg.q_block, min(d.start + (I + 1) * ocfg.q_block, d.start + d.length))
         keys = np.arange(d.start, d.start + nc * ocfg.kv_block)
-        qn = np.linalg.norm(L["qp"][rows, g, :].astype(np.float64), axis=1).max()
-        kn = np.linalg.norm(L["kp"][keys, g, :].astype(np.float64), axis=1).max()
+        qn = np.linalg.norm(L["qp"][rows, p, :].astype(np.float64), axis=1).max()
+        kn = np.linalg.norm(L["kp"][keys, p, :].astype(np.float64), axis=1).max()
         tau = ocfg.proxy_dim * 2.0 ** -23 * qn * kn
         err = np.abs(s_gpu - s_or).max()
         log(f"  scores max |gpu - fp64| {err:.3e} (bound {tau:.3e})")
@@ -164,9 +176,9 @@ def test_fullsize_sampled_parity(full_run):
         rt = torch.as_tensor(rows, device="cuda")
         o = buf.o.index_select(0, rt)[:, heads, :].float().cpu().numpy()
         dq = buf.dq.index_select(0, rt)[:, heads, :].cpu().numpy()
-        dqp = buf.dqp.index_select(0, rt)[:, g, :].cpu().numpy()
+        dqp = buf.dqp.index_select(0, rt)[:, r["p"], :].cpu().numpy()
         lse = buf.lse[heads][:, rt].cpu().numpy()
-        lsep = buf.lse_p[g, rt].cpu().numpy()
+        lsep = buf.lse_p[r["p"], rt].cpu().numpy()
         for k_, got in (("O", o), ("dQ", dq), ("dqp", dqp), ("LSE", lse), ("LSE_p", lsep)):
             acc[k_][0].append(np.ravel(got))
             acc[k_][1].append(np.ravel(r[k_]))
@@ -177,7 +189,7 @@ def test_fullsize_sampled_parity(full_run):
 
     # ---- key side
     ks = _key_samples(docs, ocfg, k2q_ptr, rng)
-    lens = [int(k2q_ptr[g, KB + 1] - k2q_ptr[g, KB]) for g, KB in ks]
+    lens = [int(k2q_ptr[ocfg.proxy_of(g), KB + 1] - k2q_ptr[ocfg.proxy_of(g), KB]) for g, KB in ks]
     log(f"[{name}] oracle key side on {len(ks)} blocks, list lengths {lens}")
     assert ks, "no KV block sampled"
     ref = om.sampled_key_side(L["q"], L["k"], L["v"], L["qp"], L["kp"], L["dO"], cu, q2k_idx, q2k_cnt,
@@ -185,8 +197,8 @@ def test_fullsize_sampled_parity(full_run):
     acc = {k_: ([], []) for k_ in ("dK", "dV", "dkp")}
     for r in ref:
         kt = torch.as_tensor(r["keys"], device="cuda")
-        for k_, t in (("dK", buf.dk), ("dV", buf.dv), ("dkp", buf.dkp)):
-            acc[k_][0].append(np.ravel(t.index_select(0, kt)[:, r["g"], :].cpu().numpy()))
+        for k_, t, hd in (("dK", buf.dk, r["g"]), ("dV", buf.dv, r["g"]), ("dkp", buf.dkp, r["p"])):
+            acc[k_][0].append(np.ravel(t.index_select(0, kt)[:, hd, :].cpu().numpy()))
             acc[k_][1].append(np.ravel(r[k_]))
     for k_ in ("dK", "dV", "dkp"):
         _close(k_, np.concatenate(acc[k_][0]), np.concatenate(acc[k_][1]))
@@ -302,3 +314,26 @@ def test_fullsize_hot_lists(full_run):
         kt = torch.as_tensor(acc["keys"] + doc.start, device=buf.dk.device)
         for k_, t in (("dK", buf.dk), ("dV", buf.dv), ("dkp", buf.dkp)):
             _close(k_, t.index_select(0, kt)[:, g, :].cpu().numpy(), acc[k_])
+
+
+def test_fullsize_shared_proxy_head():
+    """The 1M-token packing with one proxy head shared by every KV group (the
+    block-pattern variant R1s), at full size: the same sampled selection,
+    query-side and key-side checks, with the shared head's lists, scores and
+    gradients (T over every group's heads)."""
+    name = "varlen-1m-packed"
+    w, cfg, ocfg = cfgs(WORKLOADS[name], proxy_heads=1)
+    seqlens = seqlens_of(w, SEED)
+    log(f"[{name} shared head] T={sum(seqlens)} docs={len(seqlens)}: inputs")
+    x = make_case_torch(w, SEED, device="cuda", seqlens=seqlens)
+    cu = x["cu_seqlens"].cpu().numpy()
+    vl = msa.Varlen(x["cu_seqlens"], cu)
+    buf = msa.Buffers(cfg, vl, device="cuda", need_bwd=True)
+    assert tuple(buf.dqp.shape) == (sum(seqlens), 1, w.proxy_dim)
+    log(f"[{name} shared head] forward + backward through the C ABI")
+    msa.run_forward(cfg, vl, x["q"], x["k"], x["v"], x["qp"], x["kp"], buf)
+    msa.run_backward(cfg, vl, x["q"], x["k"], x["v"], x["qp"], x["kp"], x["dO"], buf)
+    torch.cuda.synchronize()
+    _check_sampled(name + " shared head", w, ocfg, x, cu, buf)
+    del buf, x
+    torch.cuda.empty_cache()

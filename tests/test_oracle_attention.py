@@ -298,6 +298,32 @@ def test_sampled_matches_full():
             np.testing.assert_allclose(sum(p[i][key] for p in parts), r[key], atol=1e-12)
 
 
+def test_sampled_matches_full_shared_head():
+    """The sampled evaluators with one shared proxy head (R1s): dqp and dkp of
+    the shared head (T over every group's heads) equal the layer backward's."""
+    rng = np.random.default_rng(31)
+    cfg = _cfg(topk=3, q_block=64, local_window=1, proxy_heads=1)
+    seqlens = (700, 260)
+    T = sum(seqlens)
+    X = _inputs(rng, T, cfg)
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    full = om.run_all(*X, cu, cfg)
+    assert full["dqp"].shape[1] == 1 and full["dkp"].shape[1] == 1
+    qs = om.sampled_query_side(*X, cu, full["q2k_idx"], full["q2k_cnt"], cfg, [(0, 3), (1, 11), (1, 15)])
+    for r in qs:
+        hs = slice(r["g"] * cfg.G, (r["g"] + 1) * cfg.G)
+        assert r["p"] == 0
+        np.testing.assert_allclose(r["O"], full["O"][r["rows"]][:, hs], atol=1e-13)
+        np.testing.assert_allclose(r["LSE_p"], full["LSEp"][0, r["rows"]], atol=1e-13)
+        np.testing.assert_allclose(r["dQ"], full["dq"][r["rows"]][:, hs], atol=1e-13)
+        np.testing.assert_allclose(r["dqp"], full["dqp"][r["rows"], 0], atol=1e-13)
+    ks = om.sampled_key_side(*X, cu, full["q2k_idx"], full["q2k_cnt"], cfg, [(0, 0), (1, 4), (0, 7)])
+    for r in ks:
+        np.testing.assert_allclose(r["dK"], full["dk"][r["keys"], r["g"]], atol=1e-12)
+        np.testing.assert_allclose(r["dV"], full["dv"][r["keys"], r["g"]], atol=1e-12)
+        np.testing.assert_allclose(r["dkp"], full["dkp"][r["keys"], 0], atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # the shared proxy head (one proxy head for all KV groups)
 # ---------------------------------------------------------------------------
