@@ -16,8 +16,9 @@ one by one, with the inputs gathered row by row from the seeded device tensors:
 * the KV blocks with the longest inverted list and with the list at the 99th
   percentile: the same element-wise check, the oracle's sum taken in ranges of
   query blocks (one progress line per range);
-* the 1M-token packing again with one proxy head shared by every group: the
-  same sampled checks on that head's lists, scores and gradients;
+* the 1M-token packing again with one proxy head shared by every group, and
+  with a dilated forced window: the same sampled checks (with the shared
+  head's lists, scores and gradients);
 * whole-layer identities that hold at any size: per group, the sum over keys
   of dV equals the sum over queries and heads of dO (softmax rows sum to one),
   and the sums over keys of dK and dkp vanish (each row of dS and of dY sums to
@@ -316,24 +317,27 @@ def test_fullsize_hot_lists(full_run):
             _close(k_, t.index_select(0, kt)[:, g, :].cpu().numpy(), acc[k_])
 
 
-def test_fullsize_shared_proxy_head():
-    """The 1M-token packing with one proxy head shared by every KV group (the
-    block-pattern variant R1s), at full size: the same sampled selection,
-    query-side and key-side checks, with the shared head's lists, scores and
+@pytest.mark.parametrize("tag,over", [("shared head", dict(proxy_heads=1)),
+                                      ("window 2 dilation 4", dict(local_window=2, dilation=4))])
+def test_fullsize_block_pattern_variants(tag, over):
+    """The 1M-token packing with a block-pattern variant at full size: one
+    proxy head shared by every KV group (R1s), or a forced window of 2 blocks
+    with dilation 4 (R3d).  The same sampled selection, query-side and
+    key-side checks; with the shared head they use its lists, scores and
     gradients (T over every group's heads)."""
     name = "varlen-1m-packed"
-    w, cfg, ocfg = cfgs(WORKLOADS[name], proxy_heads=1)
+    w, cfg, ocfg = cfgs(WORKLOADS[name], **over)
     seqlens = seqlens_of(w, SEED)
-    log(f"[{name} shared head] T={sum(seqlens)} docs={len(seqlens)}: inputs")
+    log(f"[{name} {tag}] T={sum(seqlens)} docs={len(seqlens)}: inputs")
     x = make_case_torch(w, SEED, device="cuda", seqlens=seqlens)
     cu = x["cu_seqlens"].cpu().numpy()
     vl = msa.Varlen(x["cu_seqlens"], cu)
     buf = msa.Buffers(cfg, vl, device="cuda", need_bwd=True)
-    assert tuple(buf.dqp.shape) == (sum(seqlens), 1, w.proxy_dim)
-    log(f"[{name} shared head] forward + backward through the C ABI")
+    assert tuple(buf.dqp.shape) == (sum(seqlens), ocfg.Hp, w.proxy_dim)
+    log(f"[{name} {tag}] forward + backward through the C ABI")
     msa.run_forward(cfg, vl, x["q"], x["k"], x["v"], x["qp"], x["kp"], buf)
     msa.run_backward(cfg, vl, x["q"], x["k"], x["v"], x["qp"], x["kp"], x["dO"], buf)
     torch.cuda.synchronize()
-    _check_sampled(name + " shared head", w, ocfg, x, cu, buf)
+    _check_sampled(f"{name} {tag}", w, ocfg, x, cu, buf)
     del buf, x
     torch.cuda.empty_cache()
