@@ -27,6 +27,7 @@ one by one, with the inputs gathered row by row from the seeded device tensors:
 import math
 import os
 import time
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -206,7 +207,13 @@ def _check_sampled(name, w, ocfg, x, cu, buf):
 
 
 def test_fullsize_sum_identities(full_run):
-    name, w, ocfg, x, cu, buf = full_run
+    _check_identities(*full_run)
+
+
+def _check_identities(name, w, ocfg, x, cu, buf):
+    """Whole-layer identities (one proxy head per group): per group, sum over
+    keys of dV = sum over queries and heads of dO, sums over keys of dK and
+    dkp vanish, within bf16-rounding bounds."""
     G, Hkv, d, dp = ocfg.G, ocfg.heads_kv, ocfg.head_dim, ocfg.proxy_dim
     T = int(cu[-1])
     f64 = torch.float64
@@ -339,5 +346,34 @@ def test_fullsize_block_pattern_variants(tag, over):
     msa.run_backward(cfg, vl, x["q"], x["k"], x["v"], x["qp"], x["kp"], x["dO"], buf)
     torch.cuda.synchronize()
     _check_sampled(f"{name} {tag}", w, ocfg, x, cu, buf)
+    del buf, x
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_single_1m_document():
+    """The largest single document measured: 1,048,576 tokens in one sequence
+    (the 1M-token geometry, k = 64, unpacked).  Candidate rows reach 8191
+    blocks (the selection's re-read path), the proxy scores cover an 8192 x
+    8192 block grid per group, and inverted lists are at their longest.  The
+    same sampled selection, query-side and key-side checks, and the
+    whole-layer identities."""
+    w0 = WORKLOADS["varlen-1m-packed"]
+    w = replace(w0, name="single-1m", seqlens=(1 << 20,), doc_mode="fixed", total_tokens=0)
+    w, cfg, ocfg = cfgs(w)
+    seqlens = seqlens_of(w, SEED)
+    assert seqlens == [1 << 20]
+    log(f"[single-1m] T={sum(seqlens)}: inputs")
+    x = make_case_torch(w, SEED, device="cuda", seqlens=seqlens)
+    cu = x["cu_seqlens"].cpu().numpy()
+    vl = msa.Varlen(x["cu_seqlens"], cu)
+    buf = msa.Buffers(cfg, vl, device="cuda", need_bwd=True)
+    log("[single-1m] forward + backward through the C ABI")
+    msa.run_forward(cfg, vl, x["q"], x["k"], x["v"], x["qp"], x["kp"], buf)
+    msa.run_backward(cfg, vl, x["q"], x["k"], x["v"], x["qp"], x["kp"], x["dO"], buf)
+    torch.cuda.synchronize()
+    lens = np.diff(buf.k2q_ptr.cpu().numpy(), axis=1)
+    log(f"[single-1m] inverted lists: longest {lens.max()}, mean {lens.mean():.1f}")
+    _check_sampled("single-1m", w, ocfg, x, cu, buf)
+    _check_identities("single-1m", w, ocfg, x, cu, buf)
     del buf, x
     torch.cuda.empty_cache()
