@@ -27,13 +27,6 @@
 
 namespace msa {
 
-__device__ __forceinline__ int xcd_remap_b(int i, int n) {
-  const int per = n / 8, rem = n % 8;
-  const int x = i % 8, k = i / 8;
-  return x * per + (x < rem ? x : rem) + k;
-}
-
-
 // ---------------------------------------------------------------------------
 // dQ kernel: a workgroup serves (group, query block, 4 units); a wave owns 32
 // queries of one head.  Stages are 64-key halves of the selected blocks with
@@ -77,7 +70,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
   const int col = lane & 31, hi = lane >> 5;
   const int NU = g.G * (g.Bq / 32);
   const int nwg = (NU + 3) >> 2;
-  const int bid = xcd_remap_b(blockIdx.x, gridDim.x);
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t item = bid / nwg;
   const int wgi = bid % nwg;
   const int grp = (int)(item / g.nqb);
@@ -462,7 +455,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hi = lane >> 5;
-  const int bid = xcd_remap_b(blockIdx.x, gridDim.x);
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int grp = bid / g.nkb;
   const int KB = bid % g.nkb;
   const int b = g.kdoc[KB];

@@ -28,14 +28,6 @@
 
 namespace msa {
 
-__device__ __forceinline__ int xcd_remap(int i, int n) {
-  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
-  // contiguous range of logical ids so neighbours share that XCD's L2.
-  const int per = n / 8, rem = n % 8;
-  const int x = i % 8, k = i / 8;
-  return x * per + (x < rem ? x : rem) + k;
-}
-
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d);
 template <>

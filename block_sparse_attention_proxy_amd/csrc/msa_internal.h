@@ -88,10 +88,18 @@ __host__ __device__ __forceinline__ float proxy_qweight(const Geo& g, int grp) {
   return (float)(g.Hp == g.Hkv ? 1 : (grp == 0 ? g.Hkv : 0));
 }
 
+// The contiguous range of n items that XCD x (or its queue) serves: n / 8
+// items, one more for the first n % 8 XCDs; xcd_first(x, n) is its start.
+constexpr int kXcds = 8;
+__host__ __device__ __forceinline__ int xcd_first(int x, int n) {
+  const int per = n / kXcds, rem = n % kXcds;
+  return x * per + (x < rem ? x : rem);
+}
+
 // Work queues of the persistent kernels: one set of counters per kernel,
 // kQueues of them (one per XCD) kQueueStride words (64 bytes) apart; the
 // workspace holds kQueueSets sets.
-constexpr int kQueues = 8, kQueueStride = 16, kQueueWords = kQueues * kQueueStride;
+constexpr int kQueues = kXcds, kQueueStride = 16, kQueueWords = kQueues * kQueueStride;
 constexpr int kQueueSets = 3;                       // query-major, KV-major, forward
 // Work queues of the persistent kernels: kQueues counters, one per XCD,
 // kQueueStride words (64 bytes) apart; queue x serves a contiguous range of
@@ -101,18 +109,22 @@ constexpr int kQueueSets = 3;                       // query-major, KV-major, fo
 // found empty and is kept by the caller between calls.  Returns -1 once every
 // queue is empty, so a loop over queue_take ends on every workgroup.
 __device__ __forceinline__ int queue_take(int32_t* queue, int n, int home, int& drained) {
-  const int per = n / kQueues, rem = n % kQueues;
   while (drained < kQueues) {
     const int x = (home + drained) % kQueues;
-    const int size = per + (x < rem ? 1 : 0);
+    const int first = xcd_first(x, n), size = xcd_first(x + 1, n) - first;
     if (size > 0) {
       const int c = atomicAdd(queue + x * kQueueStride, 1);
-      if (c < size) return x * per + (x < rem ? x : rem) + c;
+      if (c < size) return first + c;
     }
     ++drained;
   }
   return -1;
 }
+
+// Logical id of workgroup i of an n-workgroup grid launched one per item:
+// workgroups are dealt round-robin to the XCDs, so XCD i mod kQueues gets the
+// contiguous range of ids that queue would serve (neighbours share its L2).
+__device__ __forceinline__ int xcd_remap(int i, int n) { return xcd_first(i % kQueues, n) + i / kQueues; }
 
 // Workspace regions (byte offsets are computed by the host layout routine).
 struct Work {
